@@ -1,0 +1,232 @@
+"""Plain CPU oracle for the ZeRO-sharded mixed-precision Adam step.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It
+shares no code with the HIP library and imports nothing from it; the two meet
+only in the seeded input generators of ``synth``.
+
+The arithmetic lives in ``oracle.c`` (scalar C, one IEEE binary32 operation
+at a time) and is reached through ctypes; this module adds argument
+marshalling and the host-side loss-scale policy.
+
+Sources (page title, section):
+  * "Training models too big for one GPU: ZeRO & FSDP" -- "Adam, and why it's
+    expensive" (update equations), "How a computer stores real numbers"
+    (format table), "Mixed-precision training" (FP32 master copy, loss
+    scaling, skip on overflow), "The memory bill: 16 bytes per parameter",
+    "Data parallelism and the all-reduce" (chunk i to GPU i), "ZeRO stages 1,
+    2 and 3" (per-GPU formulas).
+  * "Stop Replicating What You Can Shard: ZeRO and FSDP" -- "The three stages
+    of ZeRO".
+  * "ZeRO memory math" (tm_zero_math) -- "Stage 1 - P_os" (N equal shards).
+  * "ZeRO Stage 3 Math" -- "Stage 3: divide everything by N".
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+except the FP64 sum of squares (``overflow_check(...)[1]``), whose only pin is
+an exactly rounded sum (``math.fsum``) of the same squares; the pages never
+define a gradient norm.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+DTYPES = {"f16": 0, "bf16": 1}
+
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no HIP, no FMA)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [
+        ("psi", ctypes.c_uint64),
+        ("shard", ctypes.c_uint64),
+        ("offset", ctypes.c_uint64),
+        ("count", ctypes.c_uint64),
+        ("pad", ctypes.c_uint64),
+        ("padded_total", ctypes.c_uint64),
+        ("n", ctypes.c_uint32),
+        ("rank", ctypes.c_uint32),
+        ("bytes_dp", ctypes.c_uint64),
+        ("bytes_z1", ctypes.c_uint64),
+        ("bytes_z2", ctypes.c_uint64),
+        ("bytes_z3", ctypes.c_uint64),
+    ]
+
+
+class _Scalars(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_float) for k in ("bc1", "bc2", "omb1", "omb2", "decay")]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        u64, u32, i32, f32, f64 = (ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
+                                   ctypes.c_float, ctypes.c_double)
+        vp = ctypes.c_void_p
+        lib.oracle_layout.argtypes = [u64, u32, u32, ctypes.POINTER(_Layout)]
+        lib.oracle_layout.restype = i32
+        lib.oracle_decode16.argtypes = [ctypes.c_uint16, i32]
+        lib.oracle_decode16.restype = f64
+        lib.oracle_encode16.argtypes = [f64, i32]
+        lib.oracle_encode16.restype = ctypes.c_uint16
+        lib.oracle_decode16_array.argtypes = [vp, vp, u64, i32]
+        lib.oracle_encode16_array.argtypes = [vp, vp, u64, i32]
+        lib.oracle_overflow_check.argtypes = [vp, i32, u64, f32, vp, vp]
+        lib.oracle_step_scalars.argtypes = [f32, f32, f32, f32, u64, ctypes.POINTER(_Scalars)]
+        lib.oracle_adam_step.argtypes = [vp, vp, vp, vp, vp, i32, u64, f32, f32, f32, f32, f32,
+                                         u64, f32]
+        lib.oracle_adam_step_f64.argtypes = [vp, vp, vp, vp, i32, u64, f64, f64, f64, f64, f64,
+                                             u64, f64]
+        for name in ("oracle_decode16_array", "oracle_encode16_array", "oracle_overflow_check",
+                     "oracle_step_scalars", "oracle_adam_step", "oracle_adam_step_f64"):
+            getattr(lib, name).restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray, dtype) -> int:
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    if not a.flags.c_contiguous:
+        raise ValueError("oracle arrays must be C-contiguous")
+    return a.ctypes.data
+
+
+@dataclass(frozen=True)
+class Layout:
+    psi: int
+    shard: int
+    offset: int
+    count: int
+    pad: int
+    padded_total: int
+    n: int
+    rank: int
+    bytes_dp: int
+    bytes_z1: int
+    bytes_z2: int
+    bytes_z3: int
+
+
+def layout(psi: int, n: int, rank: int) -> Layout:
+    """Shard layout of rank ``rank`` among ``n`` over a flat buffer of ``psi`` params."""
+    out = _Layout()
+    rc = _load().oracle_layout(psi, n, rank, ctypes.byref(out))
+    if rc != 0:
+        raise ValueError(f"invalid layout arguments psi={psi} n={n} rank={rank}")
+    return Layout(*(getattr(out, f) for f, _ in _Layout._fields_))
+
+
+def decode16(bits: np.ndarray, dtype: str) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float32)
+    _load().oracle_decode16_array(_ptr(bits, np.uint16), _ptr(out, np.float32), bits.size,
+                                  DTYPES[dtype])
+    return out
+
+
+def encode16(x: np.ndarray, dtype: str) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_encode16_array(_ptr(x, np.float32), _ptr(out, np.uint16), x.size,
+                                  DTYPES[dtype])
+    return out
+
+
+def overflow_check(g16: np.ndarray, dtype: str, loss_scale: float) -> tuple[int, float]:
+    """Return (found_inf, sum of squares of the unscaled gradients)."""
+    flag = np.zeros(1, np.int32)
+    s = np.zeros(1, np.float64)
+    _load().oracle_overflow_check(_ptr(g16, np.uint16), DTYPES[dtype], g16.size, loss_scale,
+                                  flag.ctypes.data, s.ctypes.data)
+    return int(flag[0]), float(s[0])
+
+
+@dataclass(frozen=True)
+class Scalars:
+    bc1: float
+    bc2: float
+    omb1: float
+    omb2: float
+    decay: float
+
+
+def step_scalars(lr, beta1, beta2, weight_decay, step) -> Scalars:
+    out = _Scalars()
+    _load().oracle_step_scalars(lr, beta1, beta2, weight_decay, step, ctypes.byref(out))
+    return Scalars(out.bc1, out.bc2, out.omb1, out.omb2, out.decay)
+
+
+def adam_step(w16, g16, master, m, v, dtype, *, lr, beta1, beta2, eps, weight_decay, step,
+              loss_scale) -> None:
+    """One Adam step over a shard, in place on numpy arrays of equal length."""
+    count = g16.size
+    for a in (w16, master, m, v):
+        if a.size != count:
+            raise ValueError("all shard arrays must have the same length")
+    _load().oracle_adam_step(_ptr(w16, np.uint16), _ptr(g16, np.uint16), _ptr(master, np.float32),
+                             _ptr(m, np.float32), _ptr(v, np.float32), DTYPES[dtype], count,
+                             lr, beta1, beta2, eps, weight_decay, step, loss_scale)
+
+
+def adam_step_f64(master, m, v, g16, dtype, *, lr, beta1, beta2, eps, weight_decay, step,
+                  loss_scale) -> None:
+    """FP64 evaluation of the same update (error bound only), in place on float64 arrays."""
+    _load().oracle_adam_step_f64(_ptr(master, np.float64), _ptr(m, np.float64),
+                                 _ptr(v, np.float64), _ptr(g16, np.uint16), DTYPES[dtype],
+                                 g16.size, float(np.float32(lr)), float(np.float32(beta1)),
+                                 float(np.float32(beta2)), float(np.float32(eps)),
+                                 float(np.float32(weight_decay)), step,
+                                 float(np.float32(loss_scale)))
+
+
+@dataclass
+class ScalerState:
+    """Dynamic loss scale and applied-step counter held on the host."""
+    loss_scale: float
+    step: int = 0
+    clean_steps: int = 0
+    growth_interval: int = 2000
+
+
+def policy(state: ScalerState, found_inf: int) -> bool:
+    """Skip-or-apply decision after the overflow check ("Mixed-precision training").
+
+    On overflow the step is skipped, the loss scale halves and the step counter
+    stays.  Otherwise the counter advances (the update about to run is number
+    ``state.step``) and, after ``growth_interval`` clean steps in a row, the
+    scale doubles.  Returns True when the update must be applied.
+    """
+    if found_inf:
+        state.loss_scale = state.loss_scale / 2.0
+        state.clean_steps = 0
+        return False
+    state.step += 1
+    state.clean_steps += 1
+    if state.clean_steps >= state.growth_interval:
+        state.loss_scale = state.loss_scale * 2.0
+        state.clean_steps = 0
+    return True
