@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the ZeRO-sharded mixed-precision Adam step on one MI355X.
+
+A step is one pass of the whole hot path over the shard:
+  layout (host) -> unscale + overflow check (GPU, 2 B/param) -> 4-byte flag
+  read back -> skip-or-apply decision and loss scale (host) -> Adam step (GPU,
+  28 B/param, writes the 16-bit working copy).
+Inputs are synthetic, seeded and resident in HBM before the timed region.
+
+Default workload: 1e10 parameters, N = 1 (the 160 GB unsharded case), FP16
+gradients ~N(0,1e-3) carrying a loss scale of 65536, FP32 master ~N(0,0.02),
+m = v = 0 at the start, AdamW lr 1e-4, wd 0.1.
+
+Prints one JSON line: params/s over the timed steps, the step kernel's HBM
+roofline (algorithmic 28 B/param over its HIP-event-timed average duration,
+against the 8 TB/s peak), the HBM traffic measured by rocprofv3 counters when
+the profiled kernel source matches, and the CPU oracle timed on a bounded
+sample of the same inputs.
+
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload 4]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "shard Adam params/sec + achieved HBM GB/s (28 B/param) vs peak, 1×MI355X"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+STEP_BYTES_PER_PARAM = 28       # read g 2 + master/m/v 12; write master/m/v 12 + w16 2
+CHECK_BYTES_PER_PARAM = 2
+KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_shard_amd", "csrc", "shard_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adam_step_flat10B_hbm_traffic.md")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per step-kernel launch from the committed rocprofv3 counter summary.
+
+    Returns None unless the summary was taken on this workload with the kernel
+    source that is built now."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    if kv.get("workload") != workload_name:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_workload(cfg: int, dev):
+    import torch
+
+    import synth
+    import zero_sharded_mixed_shard_amd as zs
+
+    w = synth.WORKLOADS[cfg]
+    rank = w.ranks[-1]
+    lay = zs.zero_shard_layout(w.psi, w.n, rank)
+    cnt = lay.count
+    # shard-local buffers that keep the rank's alignment phase in the flat buffer
+    phase = lay.offset % 8
+    td = w.torch_dtype
+
+    def alloc(dtype):
+        return torch.empty(phase + cnt, dtype=dtype, device=dev)[phase:]
+
+    t0 = time.time()
+    bufs = dict(g16=alloc(td), w16=alloc(td), master=alloc(torch.float32),
+                m=alloc(torch.float32), v=alloc(torch.float32))
+    synth.fill_normal_(bufs["g16"], w.grad_std, synth.seed_of(cfg, 1))
+    synth.fill_normal_(bufs["master"], w.master_std, synth.seed_of(cfg, 2))
+    if w.warm_steps:
+        synth.fill_warm_moments_(bufs["m"], bufs["v"], w.grad_std, synth.seed_of(cfg, 3),
+                                 w.beta1, w.beta2, w.warm_steps)
+    else:
+        bufs["m"].zero_()
+        bufs["v"].zero_()
+    bufs["w16"].zero_()
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: rank {rank}/{w.n}, {cnt} params, inputs ready in "
+        f"{time.time() - t0:.1f}s")
+    return w, rank, lay, bufs
+
+
+def cpu_baseline(bufs, w, budget_s: float, sample: int):
+    """The oracle as it stands, on the host's cores, over a slice of the same inputs."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    n = min(sample, bufs["g16"].numel())
+    g = synth.to_numpy_u16(bufs["g16"][:n])
+    master = bufs["master"][:n].cpu().numpy().copy()
+    m = bufs["m"][:n].cpu().numpy().copy()
+    v = bufs["v"][:n].cpu().numpy().copy()
+    w16 = np.zeros(n, np.uint16)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    threads = oracle.host_threads()
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        used = oracle.adam_step_mt(w16, g, master, m, v, w.dtype, threads=threads,
+                                   step=steps + 1, loss_scale=w.loss_scale, **hp)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    rate = n * steps / el
+    return {"value": rate, "unit": "params/s", "cores": used, "kind": "oracle",
+            "sample": f"first {n} params of the same shard inputs, {steps} Adam steps "
+                      f"({el:.1f} s wall) on {used} host threads"}
+
+
+def copy_bandwidth(dev, gib: int = 4):
+    """Same-run plain device copy (torch copy_): GB/s of read + write bytes."""
+    import torch
+
+    n = gib * (1 << 30) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="workload id (4 = 1e10 params, N=1; the reported configuration)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the CPU oracle baseline")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 24,
+                    help="parameters in the CPU baseline's sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy", action="store_true", help="skip the device-copy measurement")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the step runs on one rank's shard and no multi-GPU "
+              f"run is provided (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import zero_sharded_mixed_shard_amd as zs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w, rank, lay, b = make_workload(args.workload, dev)
+    psi, n, cnt = w.psi, w.n, lay.count
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    scaler = zs.Scaler(w.loss_scale)
+    if w.warm_steps:
+        scaler.step = w.warm_steps
+    stream = torch.cuda.current_stream(dev)
+    ev = []
+
+    def one_step(timed: bool):
+        layout = zs.zero_shard_layout(psi, n, rank)                          # shard range
+        S = scaler.loss_scale
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        if timed:
+            e[0].record(stream)
+        zs.zero_overflow_check(b["g16"], psi, n, rank, S, flag, stream=stream)   # unscale + check
+        if timed:
+            e[1].record(stream)
+        found = int(flag.item())                                            # 4 bytes to host
+        if zs.zero_scaler_update(scaler, found):                            # skip or apply
+            if timed:
+                e[2].record(stream)
+            zs.zero_adam_step(b["w16"], b["g16"], b["master"], b["m"], b["v"], psi, n, rank,
+                              step=scaler.step, loss_scale=S, found_inf=flag, stream=stream,
+                              **hp)
+            if timed:
+                e[3].record(stream)
+                ev.append(e)
+        return layout
+
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    step_ms = [x[2].elapsed_time(x[3]) for x in ev]
+    check_ms = [x[0].elapsed_time(x[1]) for x in ev]
+    if not step_ms:
+        raise RuntimeError("every timed step overflowed; nothing was measured")
+    avg_step_ms = sum(step_ms) / len(step_ms)
+    avg_check_ms = sum(check_ms) / len(check_ms)
+    achieved = STEP_BYTES_PER_PARAM * cnt / (avg_step_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+
+    copy_gbps = None if args.no_copy else copy_bandwidth(dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        cpu = cpu_baseline(b, w, args.cpu_seconds, args.cpu_sample)
+
+    out = {
+        "metric": METRIC,
+        "value": cnt * args.steps / elapsed,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "psi": psi, "zero_ranks": n, "rank": rank,
+                   "shard_params": cnt, "grad_weight_dtype": w.dtype,
+                   "optimizer": "AdamW" if w.weight_decay else "Adam",
+                   "loss_scale": w.loss_scale, "bytes_per_param": STEP_BYTES_PER_PARAM},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": traffic},
+        "kernels": {"adam_step_ms": avg_step_ms, "adam_step_ms_min": min(step_ms),
+                    "overflow_check_ms": avg_check_ms,
+                    "overflow_check_GBps": CHECK_BYTES_PER_PARAM * cnt / (avg_check_ms * 1e-3)
+                    / 1e9,
+                    "device_copy_GBps": copy_gbps},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * zero_shard.h -- C ABI of the ZeRO-partitioned mixed-precision Adam step
+ * that one data-parallel rank runs on its 1/N shard of a flat parameter
+ * buffer, on an MI355X (gfx950).
+ *
+ * Model state per parameter is 2 + 2 + 12 bytes: 16-bit working weights
+ * (w16), 16-bit gradients (g16), and FP32 master weights, first moment and
+ * second moment (master, m, v) -- "Training models too big for one GPU:
+ * ZeRO & FSDP", "The memory bill: 16 bytes per parameter".  Rank r owns
+ * chunk r of the flat buffer, all chunks the same size, and updates only
+ * that chunk ("Training models too big for one GPU", "ZeRO stages 1, 2 and
+ * 3"; "ZeRO memory math" (tm_zero_math), "Stage 1 - P_os").
+ *
+ * Conventions shared by every entry point
+ *   - Return 0 on success, a negative ZERO_E* code on error; no C++
+ *     exception ever crosses this boundary.  zero_strerror() explains a code.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     keeps a pointer past the call.
+ *   - Device pointers are SHARD VIEWS: element 0 is the first element of
+ *     rank r's range, i.e. either base + r*S into a full flat buffer (the
+ *     replicated arrays of ZeRO-1/2) or a shard-local allocation (ZeRO-3).
+ *     Exactly elements [0, count) of each view are read or written, where
+ *     count is the layout's count for (psi, n, rank).  The padding of a short
+ *     last shard and anything past count are never touched.
+ *   - Any element-aligned pointer is accepted (4 bytes for FP32 arrays, 2
+ *     for 16-bit ones).  The fast 16-byte vector path runs when one head of
+ *     h < 4 elements brings all five views to 16-byte (FP32) and 8-byte
+ *     (16-bit) alignment, which holds whenever all views sit at the same
+ *     element offset into 16-byte-aligned buffers.  Otherwise a slower
+ *     element-wise kernel gives the same results.
+ *   - All device work is enqueued on `stream` (a hipStream_t; 0 = the null
+ *     stream) of the current HIP device, and the call returns without
+ *     synchronising.  Calls are thread-safe: the library has no mutable
+ *     state shared between calls other than a per-device cache of the
+ *     compute-unit count.
+ */
+#ifndef ZERO_SHARD_H_
+#define ZERO_SHARD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Format of the 16-bit gradients and working weights (one for both). */
+typedef enum { ZERO_F16 = 0, ZERO_BF16 = 1 } zero_dtype;
+
+#define ZERO_OK 0
+#define ZERO_EINVAL (-1) /* an argument is out of its documented domain */
+#define ZERO_EDTYPE (-2) /* dt is not a zero_dtype value */
+#define ZERO_EHIP (-3)   /* the HIP runtime reported an error (see zero_strerror) */
+
+/* Largest flat buffer accepted: keeps every byte count below 2^64. */
+#define ZERO_MAX_PSI (1ull << 56)
+
+/* Doubles the caller provides in `d_partials` when asking for a sum of squares. */
+#define ZERO_SUMSQ_PARTIALS 4096
+
+/* Shard layout of one rank (all counts in elements unless named bytes_*). */
+typedef struct {
+    uint64_t psi;          /* parameters in the flat buffer */
+    uint64_t shard;        /* S = ceil(psi / n): every chunk's size, padding included */
+    uint64_t offset;       /* rank * S: flat index of the chunk's first element */
+    uint64_t count;        /* real elements in the chunk: clamp(psi - offset, 0, S) */
+    uint64_t pad;          /* S - count: padding at the tail of the flat buffer */
+    uint64_t padded_total; /* n * S */
+    uint32_t n;            /* data-parallel ranks */
+    uint32_t rank;
+    /* Model-state bytes held by one rank ("ZeRO stages 1, 2 and 3" on the
+     * first page; "The three stages of ZeRO" on "Stop Replicating What You
+     * Can Shard"; "Stage 3: divide everything by N" on "ZeRO Stage 3 Math").
+     * Sharded terms hold S elements; replicated terms hold the padded flat
+     * buffer of n*S elements.  They equal 16psi, 4psi + 12psi/n,
+     * 2psi + 14psi/n and 16psi/n exactly when n divides psi. */
+    uint64_t bytes_dp;     /* plain data parallel: 16 * psi */
+    uint64_t bytes_z1;     /* optimizer states sharded: 4 * n*S + 12 * S */
+    uint64_t bytes_z2;     /* gradients sharded too:    2 * n*S + 14 * S */
+    uint64_t bytes_z3;     /* weights sharded too:      16 * S */
+} zero_layout;
+
+/*
+ * zero_shard_layout -- where rank `rank` of `n` sits in a flat buffer of
+ * `psi` parameters, and what each ZeRO stage costs it in bytes.
+ * Chunk i of an equally chunked buffer belongs to rank i ("Training models
+ * too big for one GPU", "Data parallelism and the all-reduce"; "ZeRO memory
+ * math", "Stage 1 - P_os").  When n does not divide psi the chunk size is
+ * ceil(psi/n) and the padding sits at the tail; trailing ranks may own
+ * fewer, or zero, real elements.
+ *   Host only: no device access, no allocation.
+ *   Errors: ZERO_EINVAL if out is NULL, psi == 0, psi > ZERO_MAX_PSI,
+ *   n == 0 or rank >= n (out is then left untouched).
+ */
+int zero_shard_layout(uint64_t psi, uint32_t n, uint32_t rank, zero_layout *out);
+
+/*
+ * zero_overflow_check -- unscale this rank's gradients by the loss scale and
+ * report whether any is +-inf or NaN, so that the step can be skipped
+ * ("Training models too big for one GPU", "Mixed-precision training": the
+ * gradients are divided by S before the update; frameworks pick S
+ * dynamically and skip a step on overflow).
+ *   g16          device, shard view of `count` 16-bit gradients of format dt.
+ *   loss_scale   S > 0 and finite; each gradient is tested as float(g)/S.
+ *   d_found_inf  device int32, written with 0 or 1 (1 iff some unscaled
+ *                gradient in [0, count) is not finite).  Required.
+ *   d_sumsq      device float or NULL.  If given, receives the sum over the
+ *                shard of the unscaled gradients' squares, accumulated in
+ *                FP64 in a fixed order (so repeatable bit for bit) and
+ *                rounded to FP32: the local term of a gradient norm.
+ *   d_partials   device buffer of ZERO_SUMSQ_PARTIALS doubles, scratch for
+ *                d_sumsq; required iff d_sumsq is given, otherwise ignored.
+ *   An empty rank (count == 0) still writes 0 to d_found_inf (and d_sumsq).
+ *   Errors: ZERO_EDTYPE for a bad dt; ZERO_EINVAL for bad layout arguments,
+ *   a NULL d_found_inf, a NULL g16 with count > 0, a NULL d_partials with a
+ *   d_sumsq, a misaligned pointer, or S not positive and finite;
+ *   ZERO_EHIP if a launch fails.
+ */
+int zero_overflow_check(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank,
+                        float loss_scale, int32_t *d_found_inf, float *d_sumsq,
+                        double *d_partials, void *stream);
+
+/*
+ * zero_adam_step -- one Adam (weight_decay == 0) or AdamW step over this
+ * rank's shard, elementwise, each operation one FP32 rounding to nearest
+ * even, no contraction:
+ *     g  = float(g16) / loss_scale
+ *     p  = master * (1 - lr*weight_decay)            decoupled weight decay
+ *     m  = beta1*m + (1 - beta1)*g
+ *     v  = beta2*v + (1 - beta2)*(g*g)
+ *     m^ = m / (1 - beta1^step),   v^ = v / (1 - beta2^step)
+ *     p  = p - (lr * m^) / (sqrt(v^) + eps)         eps outside the root
+ *     master = p;  w16 = p rounded to nearest-even in format dt
+ * ("Training models too big for one GPU", "Adam, and why it's expensive":
+ * the moment, bias-correction and update equations; "Mixed-precision
+ * training": the FP32 master copy is updated and rounded to 16 bits for the
+ * next forward pass.)  1 - beta^step is formed on the host in FP64 and
+ * rounded once to FP32; 1 - beta, and 1 - lr*weight_decay, are FP32
+ * operations.  Reads 2 + 4 + 4 + 4 and writes 4 + 4 + 4 + 2 bytes per
+ * element: 28 bytes.
+ *   w16, g16     device, shard views of 16-bit working weights (written) and
+ *                gradients (read), both of format dt.
+ *   master, m, v device, shard views of FP32 state, read and written.
+ *   step         t >= 1: the number of updates applied so far, this one
+ *                included (a skipped step does not count).
+ *   d_found_inf  device int32 or NULL.  If given and non-zero when the
+ *                kernel runs, nothing is written: the step is skipped on the
+ *                device without a host round trip.
+ *   An empty rank (count == 0) returns ZERO_OK without touching the device.
+ *   Errors: ZERO_EDTYPE for a bad dt; ZERO_EINVAL for bad layout arguments,
+ *   step == 0, loss_scale not positive and finite, beta1 or beta2 outside
+ *   [0, 1), eps negative or not finite, lr or weight_decay not finite, a
+ *   NULL or misaligned array pointer with count > 0; ZERO_EHIP if the launch
+ *   fails.  On error nothing has been enqueued.
+ */
+int zero_adam_step(void *w16, const void *g16, float *master, float *m, float *v, zero_dtype dt,
+                   uint64_t psi, uint32_t n, uint32_t rank, float lr, float beta1, float beta2,
+                   float eps, float weight_decay, uint64_t step, float loss_scale,
+                   const int32_t *d_found_inf, void *stream);
+
+/* Dynamic loss scale and applied-update counter of one training run; the
+ * caller owns it (host memory) and passes it to every decision. */
+typedef struct {
+    float loss_scale;         /* S in force for the next check and step: > 0, finite */
+    uint32_t growth_interval; /* clean steps in a row before S doubles; 0 = never */
+    uint64_t step;            /* updates applied so far (t of the last applied update) */
+    uint64_t clean_steps;     /* clean steps since the last overflow or doubling */
+} zero_scaler;
+
+/*
+ * zero_scaler_update -- the skip-or-apply decision between the overflow
+ * check and the step ("Training models too big for one GPU",
+ * "Mixed-precision training": S is picked dynamically and a step with an
+ * overflow is skipped).
+ *   found_inf != 0: *apply = 0; S halves; step and the update are skipped;
+ *                   clean_steps = 0.
+ *   found_inf == 0: *apply = 1; step += 1 (the update about to run is number
+ *                   `step`); clean_steps += 1, and when it reaches a non-zero
+ *                   growth_interval S doubles (unless 2S would overflow) and
+ *                   clean_steps = 0.
+ * The update, when applied, must unscale with the S in force BEFORE this
+ * call: the gradients were produced with it.  In data parallelism found_inf
+ * is the OR of every rank's flag.
+ *   Host only.  Errors: ZERO_EINVAL if s or apply is NULL or s->loss_scale is
+ *   not positive and finite (s is then left untouched).
+ */
+int zero_scaler_update(zero_scaler *s, int32_t found_inf, int32_t *apply);
+
+/*
+ * zero_strerror -- text for a return code.  For ZERO_EHIP it names the HIP
+ * error of the most recent failing call made by this thread.  The pointer
+ * stays valid until this thread's next call into the library.
+ */
+const char *zero_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H_ */

@@ -30,7 +30,6 @@ from __future__ import annotations
 
 import ctypes
 import os
-import subprocess
 from dataclasses import dataclass
 
 import numpy as np
@@ -41,15 +40,13 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 DTYPES = {"f16": 0, "bf16": 1}
 
-GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (no HIP, no FMA)."""
+    """Compile oracle.c into liboracle.so with gcc (no HIP, no FMA); see build_oracle.py."""
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"], check=True)
-        os.replace(tmp, _LIB)
+        from . import build_oracle
+        build_oracle.build()
     return _LIB
 
 
@@ -218,15 +215,97 @@ def policy(state: ScalerState, found_inf: int) -> bool:
     On overflow the step is skipped, the loss scale halves and the step counter
     stays.  Otherwise the counter advances (the update about to run is number
     ``state.step``) and, after ``growth_interval`` clean steps in a row, the
-    scale doubles.  Returns True when the update must be applied.
+    scale doubles.  Returns True when the update must be applied.  An applied
+    update unscales with the loss scale in force BEFORE this call (the one the
+    gradients carry); ``state.loss_scale`` afterwards is the next step's.
     """
+    S = np.float32(state.loss_scale)  # the scale is an FP32 number
     if found_inf:
-        state.loss_scale = state.loss_scale / 2.0
+        state.loss_scale = float(S / np.float32(2))
         state.clean_steps = 0
         return False
     state.step += 1
     state.clean_steps += 1
-    if state.clean_steps >= state.growth_interval:
-        state.loss_scale = state.loss_scale * 2.0
+    if state.growth_interval and state.clean_steps >= state.growth_interval:
+        with np.errstate(over="ignore"):
+            grown = S * np.float32(2)
+        if np.isfinite(grown):  # the scale stays a finite number
+            state.loss_scale = float(grown)
         state.clean_steps = 0
     return True
+
+
+# ---------------------------------------------------------------------------
+# Parity bar: ordinal distance between bit patterns (test infrastructure).
+# ---------------------------------------------------------------------------
+
+def _ordinal(bits: np.ndarray, width: int) -> np.ndarray:
+    """Map sign-magnitude float bit patterns onto a line where +0 and -0 meet."""
+    b = bits.astype(np.int64)
+    sign = np.int64(1) << (width - 1)
+    mag = b & (sign - 1)
+    return np.where(b & sign, -mag, mag)
+
+
+def ulp_distance32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """|ordinal(a) - ordinal(b)| for float32 arrays (NaN pairs count 0, NaN vs number huge)."""
+    a = np.ascontiguousarray(a, np.float32)
+    b = np.ascontiguousarray(b, np.float32)
+    d = np.abs(_ordinal(a.view(np.uint32), 32) - _ordinal(b.view(np.uint32), 32))
+    na, nb = np.isnan(a), np.isnan(b)
+    d = np.where(na & nb, 0, d)
+    return np.where(na ^ nb, np.int64(1) << 40, d)
+
+
+def ulp_distance16(a: np.ndarray, b: np.ndarray, dtype: str) -> np.ndarray:
+    """Same for 16-bit patterns of format dtype."""
+    a = np.ascontiguousarray(a, np.uint16)
+    b = np.ascontiguousarray(b, np.uint16)
+    d = np.abs(_ordinal(a, 16) - _ordinal(b, 16))
+    emask = 0x7C00 if dtype == "f16" else 0x7F80
+    mmask = 0x03FF if dtype == "f16" else 0x007F
+    na = ((a & emask) == emask) & ((a & mmask) != 0)
+    nb = ((b & emask) == emask) & ((b & mmask) != 0)
+    d = np.where(na & nb, 0, d)
+    return np.where(na ^ nb, np.int64(1) << 40, d)
+
+
+# ---------------------------------------------------------------------------
+# Host-thread drivers.  The step is elementwise, so contiguous sub-ranges are
+# independent; ctypes releases the GIL while the C loop runs.
+# ---------------------------------------------------------------------------
+
+def host_threads() -> int:
+    """Threads to use on this host: its CPU share, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _ranges(count: int, threads: int):
+    threads = max(1, min(threads, count // 4096 or 1))
+    step = (count + threads - 1) // threads
+    return [(s, min(count, s + step)) for s in range(0, count, step)]
+
+
+def adam_step_mt(w16, g16, master, m, v, dtype, *, threads=None, **hp) -> int:
+    """adam_step over sub-ranges on `threads` host threads; returns the threads used."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    rs = _ranges(g16.size, threads or host_threads())
+    with ThreadPoolExecutor(len(rs)) as ex:
+        list(ex.map(lambda r: adam_step(w16[r[0]:r[1]], g16[r[0]:r[1]], master[r[0]:r[1]],
+                                        m[r[0]:r[1]], v[r[0]:r[1]], dtype, **hp), rs))
+    return len(rs)
+
+
+def overflow_flag_mt(g16, dtype, loss_scale, threads=None) -> int:
+    """The overflow flag of overflow_check, over sub-ranges on host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    rs = _ranges(g16.size, threads or host_threads())
+    with ThreadPoolExecutor(len(rs)) as ex:
+        flags = list(ex.map(lambda r: overflow_check(g16[r[0]:r[1]], dtype, loss_scale)[0], rs))
+    return int(any(flags))

@@ -1,0 +1,202 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* libzero_shard.so loads and exports every function include/zero_shard.h declares;
+* the zero_layout struct has the same size and field offsets in C and in the binding;
+* zero_shard_layout agrees with the oracle (and so with the brute force pinning it);
+* argument errors come back as codes before anything touches a device;
+* an empty rank's step returns OK without touching the device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import zero_sharded_mixed_shard_amd as zs
+from zero_sharded_mixed_shard_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero_shard.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("zero_shard_layout", "zero_overflow_check", "zero_adam_step",
+                     "zero_strerror"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", zs.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(zs.lib, name)
+
+
+def test_layout_struct_matches_header():
+    src = r"""
+    #include <stddef.h>
+    #include <stdio.h>
+    #include "zero_shard.h"
+    int main(void) {
+      printf("%zu", sizeof(zero_layout));
+    #define F(f) printf(" %zu", offsetof(zero_layout, f));
+      F(psi) F(shard) F(offset) F(count) F(pad) F(padded_total) F(n) F(rank)
+      F(bytes_dp) F(bytes_z1) F(bytes_z2) F(bytes_z3)
+      printf(" %d %d %d %d %d", ZERO_OK, ZERO_EINVAL, ZERO_EDTYPE, ZERO_EHIP, ZERO_SUMSQ_PARTIALS);
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), c, "-o", exe],
+                       check=True)
+        vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                               check=True).stdout.split()]
+    size, offs, codes = vals[0], vals[1:13], vals[13:]
+    S = _binding._Layout
+    assert size == ctypes.sizeof(S)
+    assert offs == [getattr(S, f).offset for f, _ in S._fields_]
+    assert codes == [0, -1, -2, -3, _binding.SUMSQ_PARTIALS]
+
+
+@pytest.mark.parametrize("psi,n", [(1, 1), (10, 8), (1_000_000, 8), (124_439_808, 8),
+                                   (7_500_000_000, 8), (10_000_000_000, 1),
+                                   (8_810_000_003, 64), (2**56, 3), (255, 32)])
+def test_layout_matches_oracle(psi, n):
+    for r in range(n):
+        a = zs.zero_shard_layout(psi, n, r)
+        b = oracle.layout(psi, n, r)
+        assert a.__dict__ == b.__dict__
+
+
+def test_layout_matches_oracle_small_exhaustive():
+    for psi in range(1, 130):
+        for n in range(1, 20):
+            for r in range(n):
+                assert zs.zero_shard_layout(psi, n, r).__dict__ == oracle.layout(psi, n, r).__dict__
+
+
+@pytest.mark.parametrize("args", [(0, 8, 0), (10, 0, 0), (10, 8, 8), (2**56 + 1, 8, 0)])
+def test_layout_errors(args):
+    with pytest.raises(zs.ZeroError) as e:
+        zs.zero_shard_layout(*args)
+    assert e.value.code == -1
+    assert zs.lib.zero_shard_layout(10, 8, 0, None) == -1
+
+
+# Raw C calls with fake pointers: every one must be rejected (or be an empty
+# rank) before any HIP call, so no device is needed.
+FAKE = 0x10000  # never dereferenced
+GOOD = dict(lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, step=1, S=1.0)
+
+
+def adam(dt=0, psi=100, n=4, rank=0, ptrs=(FAKE,) * 5, flag=None, **kw):
+    a = dict(GOOD, **kw)
+    return zs.lib.zero_adam_step(*ptrs, dt, psi, n, rank, a["lr"], a["b1"], a["b2"], a["eps"],
+                                 a["wd"], a["step"], a["S"], flag, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), -2), (dict(dt=-1), -2),
+    (dict(psi=0), -1), (dict(n=0), -1), (dict(rank=4), -1), (dict(psi=2**56 + 1), -1),
+    (dict(step=0), -1), (dict(S=0.0), -1), (dict(S=-1.0), -1), (dict(S=float("inf")), -1),
+    (dict(S=float("nan")), -1), (dict(b1=1.0), -1), (dict(b1=-0.1), -1), (dict(b2=1.0), -1),
+    (dict(b2=float("nan")), -1), (dict(eps=-1e-8), -1), (dict(eps=float("inf")), -1),
+    (dict(lr=float("nan")), -1), (dict(wd=float("inf")), -1),
+    (dict(ptrs=(None, FAKE, FAKE, FAKE, FAKE)), -1), (dict(ptrs=(FAKE, FAKE, None, FAKE, FAKE)), -1),
+    (dict(ptrs=(FAKE, FAKE, FAKE, FAKE, None)), -1),
+    (dict(ptrs=(FAKE + 1, FAKE, FAKE, FAKE, FAKE)), -1),      # w16 not 2-B aligned
+    (dict(ptrs=(FAKE, FAKE, FAKE + 2, FAKE, FAKE)), -1),      # master not 4-B aligned
+    (dict(flag=FAKE + 2), -1),
+])
+def test_adam_step_argument_errors(kw, code):
+    assert adam(**kw) == code
+
+
+def test_adam_step_empty_rank_is_a_no_op():
+    # psi = 10 over 8 ranks: rank 7 owns nothing; null pointers are fine then
+    assert adam(psi=10, n=8, rank=7, ptrs=(None,) * 5) == 0
+    # but the scalars are still checked
+    assert adam(psi=10, n=8, rank=7, ptrs=(None,) * 5, step=0) == -1
+
+
+def check(dt=0, psi=100, n=4, rank=0, g=FAKE, S=1.0, flag=FAKE, sumsq=None, parts=None):
+    return zs.lib.zero_overflow_check(g, dt, psi, n, rank, S, flag, sumsq, parts, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), -2), (dict(psi=0), -1), (dict(rank=9), -1), (dict(S=0.0), -1),
+    (dict(S=float("inf")), -1), (dict(flag=None), -1), (dict(flag=FAKE + 1), -1),
+    (dict(g=None), -1), (dict(g=FAKE + 1), -1), (dict(sumsq=FAKE), -1),
+    (dict(sumsq=FAKE, parts=FAKE + 4), -1),
+])
+def test_overflow_check_argument_errors(kw, code):
+    assert check(**kw) == code
+
+
+def test_strerror():
+    assert zs.zero_strerror(0) == "ok"
+    assert "invalid" in zs.zero_strerror(-1)
+    assert "dtype" in zs.zero_strerror(-2)
+    assert "HIP" in zs.zero_strerror(-3)
+    assert "unknown" in zs.zero_strerror(-99)
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    import torch
+    cpu = torch.zeros(10, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        zs.zero_adam_step(cpu, cpu, torch.zeros(10), torch.zeros(10), torch.zeros(10), 10, 1, 0,
+                          lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1,
+                          loss_scale=1.0)
+
+
+def test_scaler_matches_oracle_policy_and_pages_trace():
+    # the C5 schedule: overflow on every even step, S from 65536
+    import numpy as np
+    st = zs.Scaler(65536.0)
+    ref = oracle.ScalerState(65536.0)
+    applied = []
+    for step in range(1, 11):
+        found = int(step % 2 == 0)
+        a = zs.zero_scaler_update(st, found)
+        assert a == oracle.policy(ref, found)
+        assert (st.step, st.loss_scale, st.clean_steps) == (ref.step, ref.loss_scale,
+                                                             ref.clean_steps)
+        if a:
+            applied.append(st.step)
+    assert applied == [1, 2, 3, 4, 5] and st.loss_scale == 2048.0
+    # growth after a clean run, capped before it would overflow
+    rng = np.random.default_rng(0)
+    for interval in (0, 1, 3, 7):
+        st = zs.Scaler(2.0 ** 120, growth_interval=interval)
+        ref = oracle.ScalerState(2.0 ** 120, growth_interval=interval)
+        for found in rng.integers(0, 2, 60) * (rng.random(60) < 0.3):
+            assert zs.zero_scaler_update(st, int(found)) == oracle.policy(ref, int(found))
+            assert (st.step, st.loss_scale, st.clean_steps) == (ref.step, ref.loss_scale,
+                                                                 ref.clean_steps)
+        assert np.isfinite(st.loss_scale)
+
+
+def test_scaler_errors():
+    st = zs.Scaler(0.0)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_scaler_update(st, 0)
+    st = zs.Scaler(float("inf"))
+    with pytest.raises(zs.ZeroError):
+        zs.zero_scaler_update(st, 1)
+    assert zs.lib.zero_scaler_update(None, 0, None) == -1

@@ -1,0 +1,251 @@
+"""GPU parity, element by element, on small shards (seconds of oracle time).
+
+Sizes span the kernels' head / 16-B tile / ragged tail split at every
+alignment phase, both 16-bit formats, views of mismatched phase (the
+element-wise kernel), the overflow flag at every kind of position, NaN
+sentinels around the views (never read), the sum of squares, flag-gated
+skipping, empty ranks and a non-default stream.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import zero_sharded_mixed_shard_amd as zs
+from gpu_util import (GuardedView, assert_close, f32, log, u16)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+TD = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def run_case(count, dtype, phases, steps=3, S=1.0, hp=HP, seed=1, grad_std=1e-3, psi=None,
+             n=1, rank=0):
+    psi = count if psi is None else psi
+    td = TD[dtype]
+    V = {k: GuardedView(count, td if k in ("g16", "w16") else torch.float32, phases[k], DEV)
+         for k in ("g16", "w16", "master", "m", "v")}
+    master0 = synth.fill_normal_(torch.empty(count), 0.02, seed)
+    V["master"].view.copy_(master0.to(DEV))
+    for k in ("m", "v", "w16"):
+        V[k].view.zero_()
+    host = dict(master=master0.numpy().copy(), m=np.zeros(count, np.float32),
+                v=np.zeros(count, np.float32), w16=np.zeros(count, np.uint16))
+    for t in range(1, steps + 1):
+        g = synth.fill_normal_(torch.empty(count, dtype=td), grad_std, seed * 100 + t)
+        V["g16"].view.copy_(g.to(DEV))
+        zs.zero_adam_step(V["w16"].view, V["g16"].view, V["master"].view, V["m"].view,
+                          V["v"].view, psi, n, rank, step=t, loss_scale=S, **hp)
+        oracle.adam_step(host["w16"], u16(g), host["master"], host["m"], host["v"], dtype,
+                         step=t, loss_scale=S, **hp)
+    torch.cuda.synchronize()
+    gpu = dict(master=f32(V["master"].view), m=f32(V["m"].view), v=f32(V["v"].view),
+               w16=u16(V["w16"].view))
+    stats = assert_close(gpu, host, dtype, f"count={count} phases={phases}")
+    for k, gv in V.items():
+        assert gv.guards_intact(), (k, count, phases)
+    return stats
+
+
+COUNTS = [1, 2, 3, 4, 5, 7, 8, 9, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 2047, 2048, 2049,
+          2050, 4095, 4096, 4097, 6161, 65541, 614431]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("phase", [0, 1, 2, 3])
+def test_step_sizes_at_each_phase(dtype, phase):
+    log(f"step sizes dtype={dtype} phase={phase}")
+    worst = {}
+    for count in COUNTS:
+        st = run_case(count, dtype, dict.fromkeys(("g16", "w16", "master", "m", "v"), phase))
+        for k, (mx, nz) in st.items():
+            worst[k] = max(worst.get(k, 0), mx)
+    log("  max ulp", worst)
+
+
+@pytest.mark.parametrize("phases", [
+    dict(g16=1, w16=0, master=0, m=0, v=0),
+    dict(g16=0, w16=3, master=0, m=0, v=0),
+    dict(g16=0, w16=0, master=0, m=2, v=0),
+    dict(g16=2, w16=1, master=3, m=1, v=2),
+])
+def test_step_mismatched_phases_use_the_elementwise_kernel(phases):
+    log(f"mismatched phases {phases}")
+    for count in (1, 5, 1000, 4097, 65541):
+        for dtype in ("f16", "bf16"):
+            run_case(count, dtype, phases)
+
+
+@pytest.mark.parametrize("S", [1.0, 3.0, 1024.0, 65536.0, 0.25])
+def test_step_loss_scales(S):
+    log(f"loss scale {S}")
+    run_case(9000, "f16", dict.fromkeys(("g16", "w16", "master", "m", "v"), 0), S=S)
+    run_case(9000, "bf16", dict.fromkeys(("g16", "w16", "master", "m", "v"), 1), S=S)
+
+
+def test_step_hyperparameter_corners():
+    ph = dict.fromkeys(("g16", "w16", "master", "m", "v"), 0)
+    for hp in (dict(lr=1e-3, beta1=0.0, beta2=0.0, eps=1e-8, weight_decay=0.0),
+               dict(lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1),
+               dict(lr=1e-2, beta1=0.5, beta2=0.9, eps=0.0, weight_decay=0.0),
+               dict(lr=-1e-3, beta1=0.99, beta2=0.9999, eps=1e-6, weight_decay=1.0)):
+        log(f"hp {hp}")
+        run_case(5003, "f16", ph, hp=hp, steps=4)
+
+
+def test_step_subnormal_gradients_survive():
+    # N(0, 1e-6) FP16 gradients are mostly FP16 subnormals
+    ph = dict.fromkeys(("g16", "w16", "master", "m", "v"), 0)
+    run_case(50000, "f16", ph, grad_std=1e-6)
+    run_case(50000, "bf16", ph, grad_std=1e-30)
+
+
+def test_step_ragged_rank_of_a_sharded_buffer():
+    # psi = 10,007 over 8 ranks: ranks 0..6 own 1,251, rank 7 owns 1,250
+    for r in (0, 6, 7):
+        lay = oracle.layout(10_007, 8, r)
+        run_case(lay.count, "f16", dict.fromkeys(("g16", "w16", "master", "m", "v"), 0),
+                 psi=10_007, n=8, rank=r)
+
+
+def test_step_empty_rank_touches_nothing():
+    # psi = 10 over 8 ranks: rank 7 owns nothing
+    lay = zs.zero_shard_layout(10, 8, 7)
+    assert lay.count == 0
+    views = [GuardedView(0, torch.float16, 0, DEV), GuardedView(0, torch.float16, 0, DEV)] + \
+        [GuardedView(0, torch.float32, 0, DEV) for _ in range(3)]
+    zs.zero_adam_step(*(v.view for v in views), 10, 8, 7, step=1, loss_scale=1.0, **HP)
+    torch.cuda.synchronize()
+    assert all(v.guards_intact() for v in views)
+
+
+def test_step_skipped_on_device_when_flag_is_set():
+    count = 70001
+    td = torch.float16
+    g = synth.fill_normal_(torch.empty(count, dtype=td), 1e-3, 5).to(DEV)
+    master = synth.fill_normal_(torch.empty(count), 0.02, 6).to(DEV)
+    m = torch.full((count,), 0.5, device=DEV)
+    v = torch.full((count,), 0.25, device=DEV)
+    w = torch.zeros(count, dtype=td, device=DEV)
+    before = [x.clone() for x in (w, master, m, v)]
+    flag = torch.ones(1, dtype=torch.int32, device=DEV)
+    zs.zero_adam_step(w, g, master, m, v, count, 1, 0, step=3, loss_scale=1.0, found_inf=flag,
+                      **HP)
+    torch.cuda.synchronize()
+    for a, b in zip((w, master, m, v), before):
+        assert torch.equal(a.view(torch.int16) if a.dtype == td else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == td else b.view(torch.int32))
+    flag.zero_()
+    zs.zero_adam_step(w, g, master, m, v, count, 1, 0, step=3, loss_scale=1.0, found_inf=flag,
+                      **HP)
+    torch.cuda.synchronize()
+    host = [u16(before[0]), u16(g), f32(before[1]), f32(before[2]), f32(before[3])]
+    oracle.adam_step(host[0], host[1], host[2], host[3], host[4], "f16", step=3, loss_scale=1.0,
+                     **HP)
+    assert_close(dict(w16=u16(w), master=f32(master), m=f32(m), v=f32(v)),
+                 dict(w16=host[0], master=host[2], m=host[3], v=host[4]), "f16")
+
+
+def test_step_on_a_side_stream():
+    count = 123457
+    s = torch.cuda.Stream(device=DEV)
+    g = synth.fill_normal_(torch.empty(count, dtype=torch.bfloat16), 1e-4, 7)
+    master0 = synth.fill_normal_(torch.empty(count), 0.02, 8)
+    with torch.cuda.stream(s):
+        dg, dmaster = g.to(DEV), master0.to(DEV)
+        dm = torch.zeros(count, device=DEV)
+        dv = torch.zeros(count, device=DEV)
+        dw = torch.zeros(count, dtype=torch.bfloat16, device=DEV)
+        zs.zero_adam_step(dw, dg, dmaster, dm, dv, count, 1, 0, step=1, loss_scale=1.0, **HP)
+    s.synchronize()
+    host = dict(w16=np.zeros(count, np.uint16), master=master0.numpy().copy(),
+                m=np.zeros(count, np.float32), v=np.zeros(count, np.float32))
+    oracle.adam_step(host["w16"], u16(g), host["master"], host["m"], host["v"], "bf16", step=1,
+                     loss_scale=1.0, **HP)
+    assert_close(dict(w16=u16(dw), master=f32(dmaster), m=f32(dm), v=f32(dv)), host, "bf16")
+
+
+def test_binding_rejects_short_tensors():
+    t16 = torch.zeros(10, dtype=torch.float16, device=DEV)
+    t32 = torch.zeros(10, device=DEV)
+    with pytest.raises(ValueError):
+        zs.zero_adam_step(t16, t16, t32, t32, t32, 11, 1, 0, step=1, loss_scale=1.0, **HP)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        zs.zero_overflow_check(t16, 11, 1, 0, 1.0, flag)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_adam_step(t16, t16, t32, t32, t32, 10, 1, 0, step=0, loss_scale=1.0, **HP)
+
+
+# ---- overflow check -----------------------------------------------------------
+
+BAD = {"f16": (0x7C00, 0xFC00, 0x7E00), "bf16": (0x7F80, 0xFF80, 0x7FC0)}
+
+
+def check_case(bits: np.ndarray, dtype, phase, S, sumsq=True):
+    count = bits.size
+    gv = GuardedView(count, TD[dtype], phase, DEV)  # guards hold NaN sentinels
+    gv.view.copy_(torch.from_numpy(bits.view(np.int16).copy()).view(TD[dtype]).to(DEV))
+    flag = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    s = torch.full((1,), -1.0, device=DEV) if sumsq else None
+    parts = torch.empty(zs.SUMSQ_PARTIALS, dtype=torch.float64, device=DEV) if sumsq else None
+    zs.zero_overflow_check(gv.view, count, 1, 0, S, flag, s, parts)
+    torch.cuda.synchronize()
+    ref_flag, ref_s = oracle.overflow_check(bits, dtype, S)
+    assert int(flag.item()) == ref_flag, (count, phase, S)
+    if sumsq and ref_flag == 0:
+        assert oracle.ulp_distance32(np.float32(s.item()), np.float32(ref_s)).max() <= 1, \
+            (s.item(), ref_s)
+    assert gv.guards_intact()
+    return int(flag.item()), (s.item() if sumsq else None)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_overflow_flag_positions_and_phases(dtype):
+    rng = np.random.default_rng(3)
+    for count in (1, 7, 8, 9, 17, 4096 * 8 + 3, 300001):
+        x = (rng.standard_normal(count) * 1e-3).astype(np.float32)
+        bits = oracle.encode16(x, dtype)
+        for phase in range(8):
+            assert check_case(bits, dtype, phase, 1.0)[0] == 0
+            head = (8 - phase) % 8
+            cand = {0, head, head - 1, count // 2, count - 1, count - 8}
+            for pos in sorted(p for p in cand if 0 <= p < count):
+                for bad in BAD[dtype]:
+                    b = bits.copy()
+                    b[pos] = bad
+                    assert check_case(b, dtype, phase, 1.0, sumsq=False)[0] == 1
+
+
+def test_overflow_after_unscaling_on_device():
+    bits = oracle.encode16(np.array([60000.0, 1.0, -2.0] * 1000, np.float32), "f16")
+    assert check_case(bits, "f16", 0, 1.0)[0] == 0
+    assert check_case(bits, "f16", 0, 1e-35)[0] == 1
+    bf = oracle.encode16(np.array([3e38, -1.0] * 777, np.float32), "bf16")
+    assert check_case(bf, "bf16", 3, 1.0)[0] == 0
+    assert check_case(bf, "bf16", 3, 0.5)[0] == 1
+
+
+def test_overflow_sumsq_large_grid_and_repeatable():
+    rng = np.random.default_rng(4)
+    count = 40_000_003          # enough vectors to cap the grid and loop in it
+    x = (rng.standard_normal(count) * 1e-3).astype(np.float32)
+    bits = x.astype(np.float16).view(np.uint16)
+    f1, s1 = check_case(bits, "f16", 5, 1024.0)
+    f2, s2 = check_case(bits, "f16", 5, 1024.0)
+    assert f1 == f2 == 0 and s1 == s2
+    b = bits.copy()
+    b[rng.integers(0, count, 3)] = 0x7E00
+    assert check_case(b, "f16", 5, 1024.0, sumsq=False)[0] == 1
+
+
+def test_overflow_check_of_empty_rank_clears_outputs():
+    flag = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    s = torch.full((1,), 3.0, device=DEV)
+    parts = torch.empty(zs.SUMSQ_PARTIALS, dtype=torch.float64, device=DEV)
+    empty = torch.empty(0, dtype=torch.float16, device=DEV)
+    zs.zero_overflow_check(empty, 10, 8, 6, 1.0, flag, s, parts)
+    torch.cuda.synchronize()
+    assert flag.item() == 0 and s.item() == 0.0

@@ -1,0 +1,73 @@
+"""Checks on the gfx950 assembly of our own kernels (host only: hipcc cross-compiles).
+
+The numerics contract needs correctly rounded FP32 division and square root,
+round-to-nearest-even 16-bit conversions and no packed FP32 VALU ops; the
+memory contract needs 16-byte vector loads and stores in the step, and no
+scalar-cache writes anywhere.
+"""
+import re
+
+import pytest
+
+ROOT_BUILD = None
+
+
+@pytest.fixture(scope="module")
+def asm():
+    import importlib.util
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location(
+        "_zs_build", os.path.join(root, "zero_sharded_mixed_shard_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    text = mod.device_assembly()
+    kernels = {}
+    for m in re.finditer(r"^(_Z\S+):[^\n]*\n(.*?)^\.Lfunc_end", text, re.M | re.S):
+        kernels[m.group(1)] = m.group(2)
+    assert kernels
+    return text, kernels
+
+
+def count(body, op):
+    return len(re.findall(r"\b" + re.escape(op) + r"\b", body))
+
+
+def test_no_forbidden_instructions(asm):
+    text, _ = asm
+    for op in ("v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32", "v_cvt_pkrtz_f16_f32",
+               "s_store_dword", "s_store_dwordx2", "s_store_dwordx4", "s_atomic_add",
+               "s_dcache_wb", "s_dcache_discard", "s_buffer_store_dword"):
+        assert count(text, op) == 0, op
+    assert not re.search(r"\bs_(store|atomic|buffer_store|buffer_atomic|scratch_store)\w*", text)
+    assert not re.search(r"\bs_dcache_(wb|discard)\w*", text)
+
+
+def test_step_kernels_keep_each_operation_correctly_rounded(asm):
+    _, kernels = asm
+    steps = {k: b for k, b in kernels.items() if "adam_step" in k}
+    assert len(steps) == 4  # vector and element-wise kernels, FP16 and BF16
+    for name, body in steps.items():
+        sq = count(body, "v_sqrt_f32_e32") + count(body, "v_sqrt_f32_e64")
+        assert sq >= 1, name
+        # four divisions per element (unscale, two bias corrections, update),
+        # each the full scale / reciprocal / fma / fixup sequence
+        assert count(body, "v_div_fixup_f32") == 4 * sq, name
+        assert count(body, "v_div_fmas_f32") == 4 * sq, name
+        # the square root is refined to the correctly rounded result
+        assert count(body, "v_cmp_class_f32_e32") + count(body, "v_cmp_class_f32_e64") >= sq
+        if "ILi0E" in name:      # FP16 (the SDWA form writes the upper half-word)
+            assert sum(count(body, "v_cvt_f16_f32_" + f) for f in ("e32", "e64", "sdwa")) == sq
+        else:                    # BF16: gfx950's round-to-nearest-even convert
+            assert count(body, "v_cvt_pk_bf16_f32") == sq
+
+
+def test_vector_step_uses_16_byte_accesses(asm):
+    _, kernels = asm
+    vec = [b for k, b in kernels.items() if "adam_step_vec" in k]
+    assert len(vec) == 2
+    for body in vec:
+        assert count(body, "global_load_dwordx4") >= 6     # master, m, v x U groups
+        assert count(body, "global_store_dwordx4") >= 6
+        assert count(body, "global_load_dwordx2") >= 2     # 4 gradients per lane per group
+        assert count(body, "global_store_dwordx2") >= 2    # 4 working weights

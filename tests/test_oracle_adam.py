@@ -264,8 +264,11 @@ def test_skip_policy_trace():
 
 def test_growth_after_clean_run():
     st = oracle.ScalerState(loss_scale=1024.0, growth_interval=3)
+    used = []
     for _ in range(3):
+        used.append(st.loss_scale)
         assert oracle.policy(st, 0)
+    assert used == [1024.0] * 3       # the third update still unscales by 1024
     assert st.loss_scale == 2048.0 and st.step == 3
     assert not oracle.policy(st, 1)
     assert st.loss_scale == 1024.0 and st.step == 3
@@ -279,12 +282,14 @@ def test_skipped_step_touches_nothing():
     b = [x.copy() for x in a]
     st_a, st_b = oracle.ScalerState(65536.0), oracle.ScalerState(65536.0)
     for found in (0, 1):
+        S = st_a.loss_scale
         if oracle.policy(st_a, found):
             oracle.adam_step(a[4], a[0], a[1], a[2], a[3], "f16", step=st_a.step,
-                             loss_scale=st_a.loss_scale, **HP)
+                             loss_scale=S, **HP)
+    S = st_b.loss_scale
     if oracle.policy(st_b, 0):
         oracle.adam_step(b[4], b[0], b[1], b[2], b[3], "f16", step=st_b.step,
-                         loss_scale=st_b.loss_scale, **HP)
+                         loss_scale=S, **HP)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
     assert st_a.step == st_b.step == 1

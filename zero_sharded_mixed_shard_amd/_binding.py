@@ -1,0 +1,179 @@
+"""ctypes binding of libzero_shard.so (see include/zero_shard.h for the contract)."""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero_shard.so")
+SUMSQ_PARTIALS = 4096  # ZERO_SUMSQ_PARTIALS
+
+ZERO_F16, ZERO_BF16 = 0, 1
+_DTYPES = {torch.float16: ZERO_F16, torch.bfloat16: ZERO_BF16}
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {zero_strerror(code)} (code {code})")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python zero_sharded_mixed_shard_amd/build.py` "
+        "(or __graft_entry__.build()); there is no fallback path")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [
+        ("psi", ctypes.c_uint64),
+        ("shard", ctypes.c_uint64),
+        ("offset", ctypes.c_uint64),
+        ("count", ctypes.c_uint64),
+        ("pad", ctypes.c_uint64),
+        ("padded_total", ctypes.c_uint64),
+        ("n", ctypes.c_uint32),
+        ("rank", ctypes.c_uint32),
+        ("bytes_dp", ctypes.c_uint64),
+        ("bytes_z1", ctypes.c_uint64),
+        ("bytes_z2", ctypes.c_uint64),
+        ("bytes_z3", ctypes.c_uint64),
+    ]
+
+
+_u64, _u32, _i32, _f32, _vp = (ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_float,
+                               ctypes.c_void_p)
+lib.zero_shard_layout.argtypes = [_u64, _u32, _u32, ctypes.POINTER(_Layout)]
+lib.zero_shard_layout.restype = _i32
+lib.zero_overflow_check.argtypes = [_vp, _i32, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _vp]
+lib.zero_overflow_check.restype = _i32
+lib.zero_adam_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32, _u32, _f32, _f32, _f32,
+                               _f32, _f32, _u64, _f32, _vp, _vp]
+lib.zero_adam_step.restype = _i32
+
+
+class Scaler(ctypes.Structure):
+    """zero_scaler: dynamic loss scale and applied-update counter (host memory)."""
+    _fields_ = [("loss_scale", ctypes.c_float), ("growth_interval", ctypes.c_uint32),
+                ("step", ctypes.c_uint64), ("clean_steps", ctypes.c_uint64)]
+
+    def __init__(self, loss_scale: float, growth_interval: int = 2000, step: int = 0):
+        super().__init__(loss_scale, growth_interval, step, 0)
+
+
+lib.zero_scaler_update.argtypes = [ctypes.POINTER(Scaler), ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_int32)]
+lib.zero_scaler_update.restype = _i32
+lib.zero_strerror.argtypes = [_i32]
+lib.zero_strerror.restype = ctypes.c_char_p
+
+
+def zero_strerror(code: int) -> str:
+    return lib.zero_strerror(code).decode()
+
+
+@dataclass(frozen=True)
+class Layout:
+    psi: int
+    shard: int
+    offset: int
+    count: int
+    pad: int
+    padded_total: int
+    n: int
+    rank: int
+    bytes_dp: int
+    bytes_z1: int
+    bytes_z2: int
+    bytes_z3: int
+
+
+def zero_shard_layout(psi: int, n: int, rank: int) -> Layout:
+    out = _Layout()
+    rc = lib.zero_shard_layout(psi, n, rank, ctypes.byref(out))
+    if rc != 0:
+        raise ZeroError(rc, "zero_shard_layout")
+    return Layout(*(getattr(out, f) for f, _ in _Layout._fields_))
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _view(t: torch.Tensor, name: str, dtypes, count: int, device) -> int:
+    """Pointer of a 1-D contiguous device tensor holding at least `count` elements."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {list(dtypes)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a 1-D contiguous view")
+    if t.numel() < count:
+        raise ValueError(f"{name} holds {t.numel()} elements, the shard needs {count}")
+    return t.data_ptr()
+
+
+def zero_overflow_check(g16: torch.Tensor, psi: int, n: int, rank: int, loss_scale: float,
+                        found_inf: torch.Tensor, sumsq: torch.Tensor | None = None,
+                        partials: torch.Tensor | None = None, stream=None) -> None:
+    """Unscale this rank's gradients by loss_scale; found_inf[0] := 1 iff any is inf/NaN."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g16.device
+    if dev.type != "cuda":
+        raise ValueError("g16 must be a device tensor")
+    p_g = _view(g16, "g16", _DTYPES, lay.count, dev)
+    p_f = _view(found_inf, "found_inf", (torch.int32,), 1, dev)
+    p_s = p_p = None
+    if sumsq is not None:
+        p_s = _view(sumsq, "sumsq", (torch.float32,), 1, dev)
+        if partials is None:
+            raise ValueError("sumsq needs a partials buffer of SUMSQ_PARTIALS float64")
+        p_p = _view(partials, "partials", (torch.float64,), SUMSQ_PARTIALS, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_overflow_check(p_g, _DTYPES[g16.dtype], psi, n, rank, loss_scale, p_f, p_s,
+                                     p_p, _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_overflow_check")
+
+
+def zero_adam_step(w16: torch.Tensor, g16: torch.Tensor, master: torch.Tensor, m: torch.Tensor,
+                   v: torch.Tensor, psi: int, n: int, rank: int, *, lr: float, beta1: float,
+                   beta2: float, eps: float, weight_decay: float, step: int, loss_scale: float,
+                   found_inf: torch.Tensor | None = None, stream=None) -> None:
+    """One Adam/AdamW step over rank `rank`'s shard; every array is a shard view."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g16.device
+    if dev.type != "cuda":
+        raise ValueError("g16 must be a device tensor")
+    if w16.dtype != g16.dtype:
+        raise TypeError("w16 and g16 must share one 16-bit dtype")
+    ptrs = [
+        _view(w16, "w16", _DTYPES, lay.count, dev),
+        _view(g16, "g16", _DTYPES, lay.count, dev),
+        _view(master, "master", (torch.float32,), lay.count, dev),
+        _view(m, "m", (torch.float32,), lay.count, dev),
+        _view(v, "v", (torch.float32,), lay.count, dev),
+    ]
+    p_f = None if found_inf is None else _view(found_inf, "found_inf", (torch.int32,), 1, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_adam_step(*ptrs, _DTYPES[g16.dtype], psi, n, rank, lr, beta1, beta2, eps,
+                                weight_decay, step, loss_scale, p_f, _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_adam_step")
+
+
+def zero_scaler_update(state: Scaler, found_inf: int) -> bool:
+    """Skip-or-apply decision; returns True when the update must run (see the header)."""
+    apply = ctypes.c_int32(0)
+    rc = lib.zero_scaler_update(ctypes.byref(state), int(found_inf), ctypes.byref(apply))
+    if rc != 0:
+        raise ZeroError(rc, "zero_scaler_update")
+    return bool(apply.value)

@@ -1,0 +1,130 @@
+// C-ABI entry points: argument checks, host-side scalars, kernel dispatch.
+//
+// Every check runs before anything is enqueued, so an error leaves the
+// device untouched.  No C++ exception crosses the boundary.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+#include "zero_shard.h"
+
+namespace {
+
+thread_local char g_err[256];
+
+int fail_hip(hipError_t e, const char *what) {
+    std::snprintf(g_err, sizeof g_err, "HIP error in %s: %s (%d)", what, hipGetErrorString(e),
+                  static_cast<int>(e));
+    return ZERO_EHIP;
+}
+
+// Compute units per device, queried once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus(int *cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int cached = g_cus[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *cus = cached;
+            return ZERO_OK;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute");
+    if (n <= 0) n = 1;
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return ZERO_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+bool finite(float x) { return std::isfinite(x); }
+
+}  // namespace
+
+extern "C" int zero_overflow_check(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n,
+                                   uint32_t rank, float loss_scale, int32_t *d_found_inf,
+                                   float *d_sumsq, double *d_partials, void *stream) {
+    if (dt != ZERO_F16 && dt != ZERO_BF16) return ZERO_EDTYPE;
+    zero_layout lay;
+    if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
+    if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
+    if (d_found_inf == nullptr || !aligned(d_found_inf, 4)) return ZERO_EINVAL;
+    if (d_sumsq != nullptr &&
+        (!aligned(d_sumsq, 4) || d_partials == nullptr || !aligned(d_partials, 8)))
+        return ZERO_EINVAL;
+    if (lay.count > 0 && (g16 == nullptr || !aligned(g16, 2))) return ZERO_EINVAL;
+
+    const hipError_t e = zs::launch_overflow_check(
+        static_cast<int>(dt), static_cast<const uint16_t *>(g16), lay.count, loss_scale,
+        d_found_inf, d_sumsq, d_partials, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check launch");
+}
+
+extern "C" int zero_adam_step(void *w16, const void *g16, float *master, float *m, float *v,
+                              zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank, float lr,
+                              float beta1, float beta2, float eps, float weight_decay,
+                              uint64_t step, float loss_scale, const int32_t *d_found_inf,
+                              void *stream) {
+    if (dt != ZERO_F16 && dt != ZERO_BF16) return ZERO_EDTYPE;
+    zero_layout lay;
+    if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
+    if (step == 0) return ZERO_EINVAL;
+    if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
+    if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f)) return ZERO_EINVAL;
+    if (!(eps >= 0.0f) || !finite(eps) || !finite(lr) || !finite(weight_decay)) return ZERO_EINVAL;
+    if (d_found_inf != nullptr && !aligned(d_found_inf, 4)) return ZERO_EINVAL;
+    if (lay.count == 0) return ZERO_OK;
+    if (w16 == nullptr || g16 == nullptr || master == nullptr || m == nullptr || v == nullptr)
+        return ZERO_EINVAL;
+    if (!aligned(w16, 2) || !aligned(g16, 2) || !aligned(master, 4) || !aligned(m, 4) ||
+        !aligned(v, 4))
+        return ZERO_EINVAL;
+
+    // Host scalars: bias corrections in FP64, rounded once; the rest FP32.
+    zs::AdamScalars s;
+    s.loss_scale = loss_scale;
+    s.lr = lr;
+    s.beta1 = beta1;
+    s.beta2 = beta2;
+    s.omb1 = 1.0f - beta1;
+    s.omb2 = 1.0f - beta2;
+    s.eps = eps;
+    s.bc1 = static_cast<float>(1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step)));
+    s.bc2 = static_cast<float>(1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step)));
+    const float lw = lr * weight_decay;
+    s.decay = 1.0f - lw;
+
+    int cus = 0;
+    const int rc = device_cus(&cus);
+    if (rc != ZERO_OK) return rc;
+    const hipError_t e = zs::launch_adam_step(
+        static_cast<int>(dt), static_cast<uint16_t *>(w16), static_cast<const uint16_t *>(g16),
+        master, m, v, lay.count, s, d_found_inf, cus, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step launch");
+}
+
+extern "C" const char *zero_strerror(int code) {
+    switch (code) {
+        case ZERO_OK:
+            return "ok";
+        case ZERO_EINVAL:
+            return "invalid argument";
+        case ZERO_EDTYPE:
+            return "unsupported dtype (expected ZERO_F16 or ZERO_BF16)";
+        case ZERO_EHIP:
+            return g_err[0] ? g_err : "HIP runtime error";
+        default:
+            return "unknown error code";
+    }
+}

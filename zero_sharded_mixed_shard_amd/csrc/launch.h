@@ -1,0 +1,40 @@
+// Internal interface between the C-ABI layer (api.cpp) and the gfx950
+// kernels (shard_kernels.hip).  Not installed; callers use zero_shard.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace zs {
+
+// Per-call scalars of the Adam step, all formed on the host.
+struct AdamScalars {
+    float loss_scale;  // S: gradients are divided by it
+    float lr;
+    float beta1;
+    float beta2;
+    float omb1;        // 1 - beta1 (FP32 subtraction)
+    float omb2;        // 1 - beta2 (FP32 subtraction)
+    float eps;
+    float bc1;         // 1 - beta1^t, FP64 then rounded to FP32
+    float bc2;         // 1 - beta2^t, FP64 then rounded to FP32
+    float decay;       // 1 - lr * weight_decay (two FP32 operations)
+};
+
+// Blocks per CU the streaming kernels are sized for.
+constexpr int kBlocksPerCU = 8;
+
+// Enqueue the Adam step over `count` elements of five shard views.  The
+// caller has validated every argument; count > 0.
+hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float *master, float *m,
+                            float *v, uint64_t count, const AdamScalars &s, const int32_t *flag,
+                            int num_cus, hipStream_t stream);
+
+// Enqueue the unscale + overflow check of `count` gradients (count may be 0:
+// then only the outputs are cleared).  partials holds ZERO_SUMSQ_PARTIALS
+// doubles when sumsq is non-null.
+hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
+                                 int32_t *flag, float *sumsq, double *partials,
+                                 hipStream_t stream);
+
+}  // namespace zs

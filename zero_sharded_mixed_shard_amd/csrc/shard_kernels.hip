@@ -1,0 +1,350 @@
+// gfx950 (MI355X) kernels of the ZeRO-sharded mixed-precision Adam step.
+//
+// The step is elementwise over five structure-of-arrays streams (16-bit
+// gradients, FP32 master / m / v, 16-bit working weights): 28 bytes of HBM
+// traffic and ~80 VALU operations per element, far below the FP32 ridge
+// point, so the kernels are built for bandwidth: every lane moves one 16-B
+// FP32 vector per array and one 8-B 16-bit vector per group of 4 elements,
+// a wave's accesses are contiguous 1 KiB (FP32) or 512 B (16-bit) runs, and
+// each lane keeps U groups in flight.  No LDS: nothing is reused.
+//
+// Numerics follow the update of "Training models too big for one GPU: ZeRO &
+// FSDP" ("Adam, and why it's expensive", "Mixed-precision training") with
+// one binary32 rounding per operation: contraction is off for this file,
+// FP32 division and square root stay correctly rounded (the HIP default),
+// denormals are kept, and the 16-bit conversions round to nearest even.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+#pragma clang fp contract(off)
+
+namespace zs {
+namespace {
+
+constexpr int kThreads = 256;              // 4 wave64s
+constexpr int kVec = 4;                    // elements per lane per group
+constexpr int kGroup = kThreads * kVec;    // elements per block per group
+constexpr uint32_t kSumsqPartials = 4096;  // == ZERO_SUMSQ_PARTIALS
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- 16-bit formats -------------------------------------------------------
+
+template <int DT> __device__ __forceinline__ float widen(uint32_t h);
+template <> __device__ __forceinline__ float widen<0>(uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+template <> __device__ __forceinline__ float widen<1>(uint32_t h) {
+    return __builtin_bit_cast(float, h << 16);
+}
+
+template <int DT> __device__ __forceinline__ uint32_t narrow(float f);
+template <> __device__ __forceinline__ uint32_t narrow<0>(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // RNE
+}
+template <> __device__ __forceinline__ uint32_t narrow<1>(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));    // RNE
+}
+
+__device__ __forceinline__ uint32_t not_finite(float x) {
+    return (__builtin_bit_cast(uint32_t, x) & 0x7f800000u) == 0x7f800000u;
+}
+
+// ---- one element of the step ---------------------------------------------
+
+template <int DT>
+__device__ __forceinline__ void adam_update(uint32_t gbits, float &p, float &m, float &v,
+                                            uint32_t &w, const AdamScalars &s) {
+    const float g = widen<DT>(gbits) / s.loss_scale;
+    const float pd = p * s.decay;
+    const float m_new = s.beta1 * m + s.omb1 * g;
+    const float v_new = s.beta2 * v + s.omb2 * (g * g);
+    const float m_hat = m_new / s.bc1;
+    const float v_hat = v_new / s.bc2;
+    const float denom = __builtin_sqrtf(v_hat) + s.eps;
+    const float p_new = pd - s.lr * m_hat / denom;
+    p = p_new;
+    m = m_new;
+    v = v_new;
+    w = narrow<DT>(p_new);
+}
+
+template <int DT>
+__device__ __forceinline__ void adam_one(uint16_t *__restrict__ w16,
+                                         const uint16_t *__restrict__ g16,
+                                         float *__restrict__ master, float *__restrict__ m,
+                                         float *__restrict__ v, uint64_t i,
+                                         const AdamScalars &s) {
+    float p = master[i], mm = m[i], vv = v[i];
+    uint32_t w;
+    adam_update<DT>(g16[i], p, mm, vv, w, s);
+    master[i] = p;
+    m[i] = mm;
+    v[i] = vv;
+    w16[i] = static_cast<uint16_t>(w);
+}
+
+// ---- the step: aligned vector path ----------------------------------------
+//
+// Elements [0, head) and [head + n_tiles*U*kGroup, count) are done one at a
+// time; in between, tile t covers U groups of kGroup elements and lane l of
+// group u owns elements head + t*U*kGroup + u*kGroup + 4l .. +3.  The host
+// guarantees that master/m/v + head are 16-B aligned and g16/w16 + head are
+// 8-B aligned.
+
+template <int DT, int U>
+__global__ __launch_bounds__(kThreads) void adam_step_vec(
+    uint16_t *__restrict__ w16, const uint16_t *__restrict__ g16, float *__restrict__ master,
+    float *__restrict__ m, float *__restrict__ v, uint64_t count, uint32_t head,
+    uint64_t n_tiles, AdamScalars s, const int32_t *__restrict__ flag) {
+    if (flag != nullptr && *flag != 0) return;
+    const uint32_t tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid < head) adam_one<DT>(w16, g16, master, m, v, tid, s);
+
+    constexpr uint64_t kTile = static_cast<uint64_t>(U) * kGroup;
+    for (uint64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        const uint64_t base = head + t * kTile + static_cast<uint64_t>(tid) * kVec;
+        f32x4 P[U], M[U], V[U];
+        u32x2 G[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t e = base + static_cast<uint64_t>(u) * kGroup;
+            G[u] = *reinterpret_cast<const u32x2 *>(g16 + e);
+            P[u] = *reinterpret_cast<const f32x4 *>(master + e);
+            M[u] = *reinterpret_cast<const f32x4 *>(m + e);
+            V[u] = *reinterpret_cast<const f32x4 *>(v + e);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t e = base + static_cast<uint64_t>(u) * kGroup;
+            float p[4] = {P[u].x, P[u].y, P[u].z, P[u].w};
+            float mm[4] = {M[u].x, M[u].y, M[u].z, M[u].w};
+            float vv[4] = {V[u].x, V[u].y, V[u].z, V[u].w};
+            const uint32_t gh[4] = {G[u].x & 0xffffu, G[u].x >> 16, G[u].y & 0xffffu,
+                                    G[u].y >> 16};
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) adam_update<DT>(gh[j], p[j], mm[j], vv[j], w[j], s);
+            *reinterpret_cast<f32x4 *>(master + e) = f32x4{p[0], p[1], p[2], p[3]};
+            *reinterpret_cast<f32x4 *>(m + e) = f32x4{mm[0], mm[1], mm[2], mm[3]};
+            *reinterpret_cast<f32x4 *>(v + e) = f32x4{vv[0], vv[1], vv[2], vv[3]};
+            *reinterpret_cast<u32x2 *>(w16 + e) = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+        }
+    }
+
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+    for (uint64_t i = head + n_tiles * kTile + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
+         i < count; i += stride)
+        adam_one<DT>(w16, g16, master, m, v, i, s);
+}
+
+// ---- the step: element-wise path for views of different alignment phase --
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void adam_step_elem(
+    uint16_t *__restrict__ w16, const uint16_t *__restrict__ g16, float *__restrict__ master,
+    float *__restrict__ m, float *__restrict__ v, uint64_t count, AdamScalars s,
+    const int32_t *__restrict__ flag) {
+    if (flag != nullptr && *flag != 0) return;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < count;
+         i += stride)
+        adam_one<DT>(w16, g16, master, m, v, i, s);
+}
+
+// ---- unscale + overflow check ----------------------------------------------
+
+__global__ void check_init(int32_t *__restrict__ flag, float *__restrict__ sumsq) {
+    if (threadIdx.x == 0) {
+        *flag = 0;
+        if (sumsq != nullptr) *sumsq = 0.0f;
+    }
+}
+
+// Elements [0, head) and [head + 8*n_vec, count) one at a time; in between,
+// 16-B vectors of 8 gradients, grid-stride, U vectors in flight per lane.
+// Each wave that sees a non-finite value stores 1 from one lane.  With
+// SUMSQ, block b writes its FP64 partial sum to partials[b].
+template <int DT, bool SUMSQ, int U>
+__global__ __launch_bounds__(kThreads) void overflow_check_kernel(
+    const uint16_t *__restrict__ g16, uint64_t count, uint32_t head, uint64_t n_vec,
+    float loss_scale, int32_t *__restrict__ flag, double *__restrict__ partials) {
+    const uint32_t tid = threadIdx.x;
+    uint32_t bad = 0;
+    double acc = 0.0;
+    auto visit = [&](uint32_t h) {
+        const float q = widen<DT>(h) / loss_scale;
+        bad |= not_finite(q);
+        if (SUMSQ) acc += static_cast<double>(q) * static_cast<double>(q);
+    };
+
+    if (blockIdx.x == 0 && tid < head) visit(g16[tid]);
+
+    const u32x4 *vec = reinterpret_cast<const u32x4 *>(g16 + head);
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+    uint64_t k = static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
+    for (; k + (U - 1) * stride < n_vec; k += U * stride) {
+        u32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = vec[k + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                visit(x[u][j] & 0xffffu);
+                visit(x[u][j] >> 16);
+            }
+        }
+    }
+    for (; k < n_vec; k += stride) {
+        const u32x4 x = vec[k];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            visit(x[j] & 0xffffu);
+            visit(x[j] >> 16);
+        }
+    }
+    for (uint64_t i = head + n_vec * 8 + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
+         i < count; i += stride)
+        visit(g16[i]);
+
+    if (__any(bad)) {
+        if ((tid & 63u) == 0) *flag = 1;
+    }
+
+    if (SUMSQ) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        __shared__ double wave_sum[kThreads / 64];
+        if ((tid & 63u) == 0) wave_sum[tid >> 6] = acc;
+        __syncthreads();
+        if (tid == 0) {
+            double b = 0.0;
+#pragma unroll
+            for (int w = 0; w < kThreads / 64; ++w) b += wave_sum[w];
+            partials[blockIdx.x] = b;
+        }
+    }
+}
+
+// Sum the per-block partials in a fixed order and round once to FP32.
+__global__ __launch_bounds__(kThreads) void sumsq_finalize(const double *__restrict__ partials,
+                                                           uint32_t n_parts,
+                                                           float *__restrict__ sumsq) {
+    __shared__ double red[kThreads];
+    const uint32_t tid = threadIdx.x;
+    double a = 0.0;
+    for (uint32_t i = tid; i < n_parts; i += kThreads) a += partials[i];
+    red[tid] = a;
+    __syncthreads();
+    for (uint32_t h = kThreads / 2; h > 0; h >>= 1) {
+        if (tid < h) red[tid] += red[tid + h];
+        __syncthreads();
+    }
+    if (tid == 0) *sumsq = static_cast<float>(red[0]);
+}
+
+// ---- launch helpers --------------------------------------------------------
+
+constexpr int kAdamU = 2;   // groups in flight per lane in the step
+constexpr int kCheckU = 4;  // 16-B vectors in flight per lane in the check
+
+inline uint32_t align_head(uintptr_t addr, uint32_t elem_bytes, uint32_t align) {
+    // elements to skip until addr is `align`-aligned (addr is elem-aligned)
+    const uintptr_t mis = addr % align;
+    return mis == 0 ? 0u : static_cast<uint32_t>((align - mis) / elem_bytes);
+}
+
+template <int DT>
+hipError_t adam_dispatch(uint16_t *w16, const uint16_t *g16, float *master, float *m, float *v,
+                         uint64_t count, const AdamScalars &s, const int32_t *flag, int num_cus,
+                         hipStream_t stream) {
+    const uint64_t max_blocks = static_cast<uint64_t>(num_cus) * kBlocksPerCU;
+    uint32_t head = align_head(reinterpret_cast<uintptr_t>(master), 4, 16);
+    const bool same_phase =
+        reinterpret_cast<uintptr_t>(m) % 16 == reinterpret_cast<uintptr_t>(master) % 16 &&
+        reinterpret_cast<uintptr_t>(v) % 16 == reinterpret_cast<uintptr_t>(master) % 16 &&
+        (reinterpret_cast<uintptr_t>(g16) + 2u * head) % 8 == 0 &&
+        (reinterpret_cast<uintptr_t>(w16) + 2u * head) % 8 == 0;
+    if (!same_phase) {
+        const uint64_t need = (count + kThreads - 1) / kThreads;
+        const uint32_t blocks = static_cast<uint32_t>(need < max_blocks ? need : max_blocks);
+        adam_step_elem<DT><<<blocks, kThreads, 0, stream>>>(w16, g16, master, m, v, count, s,
+                                                             flag);
+        return hipGetLastError();
+    }
+    if (head > count) head = static_cast<uint32_t>(count);
+    constexpr uint64_t kTile = static_cast<uint64_t>(kAdamU) * kGroup;
+    const uint64_t n_tiles = (count - head) / kTile;
+    const uint64_t rest = count - head - n_tiles * kTile;
+    uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
+    if (need == 0) need = 1;
+    const uint32_t blocks = static_cast<uint32_t>(need < max_blocks ? need : max_blocks);
+    adam_step_vec<DT, kAdamU><<<blocks, kThreads, 0, stream>>>(w16, g16, master, m, v, count,
+                                                               head, n_tiles, s, flag);
+    return hipGetLastError();
+}
+
+struct CheckGrid {
+    uint32_t head;    // elements done one at a time before the first 16-B vector
+    uint64_t n_vec;   // 16-B vectors of 8 gradients
+    uint32_t blocks;  // grid size == number of partial sums written
+};
+
+// The grid depends on the size and the pointer's phase only, never on the
+// device, so the partial sums and their order are the same on every device.
+inline CheckGrid check_grid(const uint16_t *g16, uint64_t count) {
+    CheckGrid c;
+    c.head = align_head(reinterpret_cast<uintptr_t>(g16), 2, 16);
+    if (c.head > count) c.head = static_cast<uint32_t>(count);
+    c.n_vec = (count - c.head) / 8;
+    const uint64_t rest = count - c.head - 8 * c.n_vec;
+    const uint64_t per_block = static_cast<uint64_t>(kThreads) * kCheckU;
+    uint64_t need = c.n_vec > 0 ? (c.n_vec + per_block - 1) / per_block
+                                : (rest + kThreads - 1) / kThreads;
+    if (need == 0) need = 1;
+    c.blocks = static_cast<uint32_t>(need < kSumsqPartials ? need : kSumsqPartials);
+    return c;
+}
+
+template <int DT, bool SUMSQ>
+hipError_t check_dispatch(const uint16_t *g16, uint64_t count, float loss_scale, int32_t *flag,
+                          double *partials, const CheckGrid &c, hipStream_t stream) {
+    overflow_check_kernel<DT, SUMSQ, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
+        g16, count, c.head, c.n_vec, loss_scale, flag, partials);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float *master, float *m,
+                            float *v, uint64_t count, const AdamScalars &s, const int32_t *flag,
+                            int num_cus, hipStream_t stream) {
+    if (dtype == 0) return adam_dispatch<0>(w16, g16, master, m, v, count, s, flag, num_cus, stream);
+    return adam_dispatch<1>(w16, g16, master, m, v, count, s, flag, num_cus, stream);
+}
+
+hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
+                                 int32_t *flag, float *sumsq, double *partials,
+                                 hipStream_t stream) {
+    check_init<<<1, 64, 0, stream>>>(flag, sumsq);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || count == 0) return err;
+    const bool want = sumsq != nullptr;
+    const CheckGrid c = check_grid(g16, count);
+    if (dtype == 0)
+        err = want ? check_dispatch<0, true>(g16, count, loss_scale, flag, partials, c, stream)
+                   : check_dispatch<0, false>(g16, count, loss_scale, flag, partials, c, stream);
+    else
+        err = want ? check_dispatch<1, true>(g16, count, loss_scale, flag, partials, c, stream)
+                   : check_dispatch<1, false>(g16, count, loss_scale, flag, partials, c, stream);
+    if (err != hipSuccess || !want) return err;
+    sumsq_finalize<<<1, kThreads, 0, stream>>>(partials, c.blocks, sumsq);
+    return hipGetLastError();
+}
+
+}  // namespace zs
