@@ -65,9 +65,12 @@ extern "C" int zero_overflow_check(const void *g16, zero_dtype dt, uint64_t psi,
         return ZERO_EINVAL;
     if (lay.count > 0 && (g16 == nullptr || !aligned(g16, 2))) return ZERO_EINVAL;
 
+    int cus = 0;
+    const int rc = device_cus(&cus);
+    if (rc != ZERO_OK) return rc;
     const hipError_t e = zs::launch_overflow_check(
         static_cast<int>(dt), static_cast<const uint16_t *>(g16), lay.count, loss_scale,
-        d_found_inf, d_sumsq, d_partials, static_cast<hipStream_t>(stream));
+        d_found_inf, d_sumsq, d_partials, cus, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check launch");
 }
 
@@ -105,12 +108,9 @@ extern "C" int zero_adam_step(void *w16, const void *g16, float *master, float *
     const float lw = lr * weight_decay;
     s.decay = 1.0f - lw;
 
-    int cus = 0;
-    const int rc = device_cus(&cus);
-    if (rc != ZERO_OK) return rc;
     const hipError_t e = zs::launch_adam_step(
         static_cast<int>(dt), static_cast<uint16_t *>(w16), static_cast<const uint16_t *>(g16),
-        master, m, v, lay.count, s, d_found_inf, cus, static_cast<hipStream_t>(stream));
+        master, m, v, lay.count, s, d_found_inf, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step launch");
 }
 

@@ -21,20 +21,22 @@ struct AdamScalars {
     float decay;       // 1 - lr * weight_decay (two FP32 operations)
 };
 
-// Blocks per CU the streaming kernels are sized for.
-constexpr int kBlocksPerCU = 8;
+// Largest grid of the streaming kernels, in 256-thread blocks: one tile per
+// block measured fastest, and 2^23 blocks keep the grid below 2^32 threads.
+// Larger shards loop over tiles.
+constexpr uint64_t kMaxBlocks = 1ull << 23;
 
 // Enqueue the Adam step over `count` elements of five shard views.  The
 // caller has validated every argument; count > 0.
 hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float *master, float *m,
                             float *v, uint64_t count, const AdamScalars &s, const int32_t *flag,
-                            int num_cus, hipStream_t stream);
+                            hipStream_t stream);
 
 // Enqueue the unscale + overflow check of `count` gradients (count may be 0:
 // then only the outputs are cleared).  partials holds ZERO_SUMSQ_PARTIALS
 // doubles when sumsq is non-null.
 hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
-                                 int32_t *flag, float *sumsq, double *partials,
+                                 int32_t *flag, float *sumsq, double *partials, int num_cus,
                                  hipStream_t stream);
 
 }  // namespace zs

@@ -6,7 +6,11 @@
 // point, so the kernels are built for bandwidth: every lane moves one 16-B
 // FP32 vector per array and one 8-B 16-bit vector per group of 4 elements,
 // a wave's accesses are contiguous 1 KiB (FP32) or 512 B (16-bit) runs, and
-// each lane keeps U groups in flight.  No LDS: nothing is reused.
+// each lane keeps U groups in flight.  No LDS: nothing is reused.  Every
+// access of the streaming kernels is non-temporal (the data is touched once),
+// and the step launches one block per tile (a grid-stride loop only past 2^23
+// tiles): both measured faster on MI355X than a resident grid looping over
+// tiles.
 //
 // Numerics follow the update of "Training models too big for one GPU: ZeRO &
 // FSDP" ("Adam, and why it's expensive", "Mixed-precision training") with
@@ -31,6 +35,17 @@ constexpr uint32_t kSumsqPartials = 4096;  // == ZERO_SUMSQ_PARTIALS
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Streaming accesses: every byte is read once and written once.
+template <typename T>
+__device__ __forceinline__ T load_nt(const T *p) {
+    return __builtin_nontemporal_load(p);
+}
+template <typename T>
+__device__ __forceinline__ void store_nt(T *p, T v) {
+    __builtin_nontemporal_store(v, p);
+}
 
 // ---- 16-bit formats -------------------------------------------------------
 
@@ -113,10 +128,10 @@ __global__ __launch_bounds__(kThreads) void adam_step_vec(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint64_t e = base + static_cast<uint64_t>(u) * kGroup;
-            G[u] = *reinterpret_cast<const u32x2 *>(g16 + e);
-            P[u] = *reinterpret_cast<const f32x4 *>(master + e);
-            M[u] = *reinterpret_cast<const f32x4 *>(m + e);
-            V[u] = *reinterpret_cast<const f32x4 *>(v + e);
+            G[u] = load_nt(reinterpret_cast<const u32x2 *>(g16 + e));
+            P[u] = load_nt(reinterpret_cast<const f32x4 *>(master + e));
+            M[u] = load_nt(reinterpret_cast<const f32x4 *>(m + e));
+            V[u] = load_nt(reinterpret_cast<const f32x4 *>(v + e));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -129,10 +144,11 @@ __global__ __launch_bounds__(kThreads) void adam_step_vec(
             uint32_t w[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) adam_update<DT>(gh[j], p[j], mm[j], vv[j], w[j], s);
-            *reinterpret_cast<f32x4 *>(master + e) = f32x4{p[0], p[1], p[2], p[3]};
-            *reinterpret_cast<f32x4 *>(m + e) = f32x4{mm[0], mm[1], mm[2], mm[3]};
-            *reinterpret_cast<f32x4 *>(v + e) = f32x4{vv[0], vv[1], vv[2], vv[3]};
-            *reinterpret_cast<u32x2 *>(w16 + e) = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+            store_nt(reinterpret_cast<f32x4 *>(master + e), f32x4{p[0], p[1], p[2], p[3]});
+            store_nt(reinterpret_cast<f32x4 *>(m + e), f32x4{mm[0], mm[1], mm[2], mm[3]});
+            store_nt(reinterpret_cast<f32x4 *>(v + e), f32x4{vv[0], vv[1], vv[2], vv[3]});
+            store_nt(reinterpret_cast<u32x2 *>(w16 + e),
+                     u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)});
         }
     }
 
@@ -165,12 +181,63 @@ __global__ void check_init(int32_t *__restrict__ flag, float *__restrict__ sumsq
     }
 }
 
-// Elements [0, head) and [head + 8*n_vec, count) one at a time; in between,
-// 16-B vectors of 8 gradients, grid-stride, U vectors in flight per lane.
-// Each wave that sees a non-finite value stores 1 from one lane.  With
-// SUMSQ, block b writes its FP64 partial sum to partials[b].
-template <int DT, bool SUMSQ, int U>
-__global__ __launch_bounds__(kThreads) void overflow_check_kernel(
+// Flag only.  Division by S > 0 correctly rounded is monotone in |g|, so
+// some float(g)/S is not finite iff some g is inf/NaN or the largest finite
+// |g| divided by S overflows.  For 16-bit patterns with the sign cleared the
+// integer order is the magnitude order, so each lane keeps the max of
+// (bits & 0x7fff) with packed 16-bit integer maxima and divides once at the
+// end: the pass is two integer operations per gradient and runs at read
+// bandwidth.  Elements [0, head) and [head + 8*n_vec, count) one at a time;
+// in between, 16-B vectors of 8 gradients, grid-stride, U in flight per lane.
+template <int DT, int U>
+__global__ __launch_bounds__(kThreads) void overflow_flag_kernel(
+    const uint16_t *__restrict__ g16, uint64_t count, uint32_t head, uint64_t n_vec,
+    float loss_scale, int32_t *__restrict__ flag) {
+    constexpr uint32_t kExpField = DT == 0 ? 0x7c00u : 0x7f80u;  // inf/NaN at or above
+    const uint32_t tid = threadIdx.x;
+    u16x2 mx2 = {0, 0};
+    uint32_t mx = 0;
+    if (blockIdx.x == 0 && tid < head) mx = g16[tid] & 0x7fffu;
+
+    const u32x4 *vec = reinterpret_cast<const u32x4 *>(g16 + head);
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+    uint64_t k = static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
+    for (; k + (U - 1) * stride < n_vec; k += U * stride) {
+        u32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = load_nt(vec + k + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, x[u][j] & 0x7fff7fffu));
+        }
+    }
+    for (; k < n_vec; k += stride) {
+        const u32x4 x = load_nt(vec + k);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, x[j] & 0x7fff7fffu));
+    }
+    for (uint64_t i = head + n_vec * 8 + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
+         i < count; i += stride) {
+        const uint32_t a = g16[i] & 0x7fffu;
+        mx = a > mx ? a : mx;
+    }
+    mx = mx > mx2.x ? mx : mx2.x;
+    mx = mx > mx2.y ? mx : mx2.y;
+    const uint32_t bad = mx >= kExpField || not_finite(widen<DT>(mx) / loss_scale);
+    if (__any(bad)) {
+        if ((tid & 63u) == 0) *flag = 1;
+    }
+}
+
+// Flag and sum of squares: each gradient is unscaled, tested and squared as
+// its definition says; lanes accumulate in FP64, waves reduce by shuffles,
+// and block b writes its partial sum to partials[b].  Same element split as
+// the flag kernel.
+template <int DT, int U>
+__global__ __launch_bounds__(kThreads) void overflow_sumsq_kernel(
     const uint16_t *__restrict__ g16, uint64_t count, uint32_t head, uint64_t n_vec,
     float loss_scale, int32_t *__restrict__ flag, double *__restrict__ partials) {
     const uint32_t tid = threadIdx.x;
@@ -179,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void overflow_check_kernel(
     auto visit = [&](uint32_t h) {
         const float q = widen<DT>(h) / loss_scale;
         bad |= not_finite(q);
-        if (SUMSQ) acc += static_cast<double>(q) * static_cast<double>(q);
+        acc += static_cast<double>(q) * static_cast<double>(q);
     };
 
     if (blockIdx.x == 0 && tid < head) visit(g16[tid]);
@@ -190,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void overflow_check_kernel(
     for (; k + (U - 1) * stride < n_vec; k += U * stride) {
         u32x4 x[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = vec[k + u * stride];
+        for (int u = 0; u < U; ++u) x[u] = load_nt(vec + k + u * stride);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -201,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void overflow_check_kernel(
         }
     }
     for (; k < n_vec; k += stride) {
-        const u32x4 x = vec[k];
+        const u32x4 x = load_nt(vec + k);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             visit(x[j] & 0xffffu);
@@ -215,19 +282,16 @@ __global__ __launch_bounds__(kThreads) void overflow_check_kernel(
     if (__any(bad)) {
         if ((tid & 63u) == 0) *flag = 1;
     }
-
-    if (SUMSQ) {
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-        __shared__ double wave_sum[kThreads / 64];
-        if ((tid & 63u) == 0) wave_sum[tid >> 6] = acc;
-        __syncthreads();
-        if (tid == 0) {
-            double b = 0.0;
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    __shared__ double wave_sum[kThreads / 64];
+    if ((tid & 63u) == 0) wave_sum[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        double b = 0.0;
 #pragma unroll
-            for (int w = 0; w < kThreads / 64; ++w) b += wave_sum[w];
-            partials[blockIdx.x] = b;
-        }
+        for (int w = 0; w < kThreads / 64; ++w) b += wave_sum[w];
+        partials[blockIdx.x] = b;
     }
 }
 
@@ -250,8 +314,9 @@ __global__ __launch_bounds__(kThreads) void sumsq_finalize(const double *__restr
 
 // ---- launch helpers --------------------------------------------------------
 
-constexpr int kAdamU = 2;   // groups in flight per lane in the step
-constexpr int kCheckU = 4;  // 16-B vectors in flight per lane in the check
+constexpr int kAdamU = 2;              // groups in flight per lane in the step
+constexpr int kCheckU = 4;             // 16-B vectors in flight per lane in the check
+constexpr int kCheckBlocksPerCU = 128; // flag-only check grid cap per CU (measured)
 
 inline uint32_t align_head(uintptr_t addr, uint32_t elem_bytes, uint32_t align) {
     // elements to skip until addr is `align`-aligned (addr is elem-aligned)
@@ -261,9 +326,9 @@ inline uint32_t align_head(uintptr_t addr, uint32_t elem_bytes, uint32_t align) 
 
 template <int DT>
 hipError_t adam_dispatch(uint16_t *w16, const uint16_t *g16, float *master, float *m, float *v,
-                         uint64_t count, const AdamScalars &s, const int32_t *flag, int num_cus,
+                         uint64_t count, const AdamScalars &s, const int32_t *flag,
                          hipStream_t stream) {
-    const uint64_t max_blocks = static_cast<uint64_t>(num_cus) * kBlocksPerCU;
+    const uint64_t max_blocks = kMaxBlocks;
     uint32_t head = align_head(reinterpret_cast<uintptr_t>(master), 4, 16);
     const bool same_phase =
         reinterpret_cast<uintptr_t>(m) % 16 == reinterpret_cast<uintptr_t>(master) % 16 &&
@@ -292,12 +357,13 @@ hipError_t adam_dispatch(uint16_t *w16, const uint16_t *g16, float *master, floa
 struct CheckGrid {
     uint32_t head;    // elements done one at a time before the first 16-B vector
     uint64_t n_vec;   // 16-B vectors of 8 gradients
-    uint32_t blocks;  // grid size == number of partial sums written
+    uint32_t blocks;  // grid size (with a sum of squares: the number of partials)
 };
 
-// The grid depends on the size and the pointer's phase only, never on the
-// device, so the partial sums and their order are the same on every device.
-inline CheckGrid check_grid(const uint16_t *g16, uint64_t count) {
+// With a sum of squares the grid depends on the size and the pointer's phase
+// only, never on the device, so the partial sums and their order are the
+// same everywhere.  The flag-only grid is sized per CU.
+inline CheckGrid check_grid(const uint16_t *g16, uint64_t count, bool sumsq, int num_cus) {
     CheckGrid c;
     c.head = align_head(reinterpret_cast<uintptr_t>(g16), 2, 16);
     if (c.head > count) c.head = static_cast<uint32_t>(count);
@@ -307,15 +373,26 @@ inline CheckGrid check_grid(const uint16_t *g16, uint64_t count) {
     uint64_t need = c.n_vec > 0 ? (c.n_vec + per_block - 1) / per_block
                                 : (rest + kThreads - 1) / kThreads;
     if (need == 0) need = 1;
-    c.blocks = static_cast<uint32_t>(need < kSumsqPartials ? need : kSumsqPartials);
+    const uint64_t cap = sumsq ? kSumsqPartials
+                               : static_cast<uint64_t>(num_cus) * kCheckBlocksPerCU;
+    c.blocks = static_cast<uint32_t>(need < cap ? need : cap);
     return c;
 }
 
-template <int DT, bool SUMSQ>
+template <int DT>
 hipError_t check_dispatch(const uint16_t *g16, uint64_t count, float loss_scale, int32_t *flag,
-                          double *partials, const CheckGrid &c, hipStream_t stream) {
-    overflow_check_kernel<DT, SUMSQ, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
+                          float *sumsq, double *partials, int num_cus, hipStream_t stream) {
+    const CheckGrid c = check_grid(g16, count, sumsq != nullptr, num_cus);
+    if (sumsq == nullptr) {
+        overflow_flag_kernel<DT, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
+            g16, count, c.head, c.n_vec, loss_scale, flag);
+        return hipGetLastError();
+    }
+    overflow_sumsq_kernel<DT, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
         g16, count, c.head, c.n_vec, loss_scale, flag, partials);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    sumsq_finalize<<<1, kThreads, 0, stream>>>(partials, c.blocks, sumsq);
     return hipGetLastError();
 }
 
@@ -323,28 +400,20 @@ hipError_t check_dispatch(const uint16_t *g16, uint64_t count, float loss_scale,
 
 hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float *master, float *m,
                             float *v, uint64_t count, const AdamScalars &s, const int32_t *flag,
-                            int num_cus, hipStream_t stream) {
-    if (dtype == 0) return adam_dispatch<0>(w16, g16, master, m, v, count, s, flag, num_cus, stream);
-    return adam_dispatch<1>(w16, g16, master, m, v, count, s, flag, num_cus, stream);
+                            hipStream_t stream) {
+    if (dtype == 0) return adam_dispatch<0>(w16, g16, master, m, v, count, s, flag, stream);
+    return adam_dispatch<1>(w16, g16, master, m, v, count, s, flag, stream);
 }
 
 hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
-                                 int32_t *flag, float *sumsq, double *partials,
+                                 int32_t *flag, float *sumsq, double *partials, int num_cus,
                                  hipStream_t stream) {
     check_init<<<1, 64, 0, stream>>>(flag, sumsq);
-    hipError_t err = hipGetLastError();
+    const hipError_t err = hipGetLastError();
     if (err != hipSuccess || count == 0) return err;
-    const bool want = sumsq != nullptr;
-    const CheckGrid c = check_grid(g16, count);
     if (dtype == 0)
-        err = want ? check_dispatch<0, true>(g16, count, loss_scale, flag, partials, c, stream)
-                   : check_dispatch<0, false>(g16, count, loss_scale, flag, partials, c, stream);
-    else
-        err = want ? check_dispatch<1, true>(g16, count, loss_scale, flag, partials, c, stream)
-                   : check_dispatch<1, false>(g16, count, loss_scale, flag, partials, c, stream);
-    if (err != hipSuccess || !want) return err;
-    sumsq_finalize<<<1, kThreads, 0, stream>>>(partials, c.blocks, sumsq);
-    return hipGetLastError();
+        return check_dispatch<0>(g16, count, loss_scale, flag, sumsq, partials, num_cus, stream);
+    return check_dispatch<1>(g16, count, loss_scale, flag, sumsq, partials, num_cus, stream);
 }
 
 }  // namespace zs
