@@ -168,6 +168,9 @@ def main():
                     help="parameters in the CPU baseline's sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy measurement")
+    ap.add_argument("--control", choices=["host", "device"], default="host",
+                    help="skip-or-apply decision on the host (4-byte read-back per step) or in "
+                         "device memory (no read-back)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -214,6 +217,30 @@ def main():
                 ev.append(e)
         return layout
 
+    if args.control == "device":
+        ctl = zs.device_ctl_new(w.loss_scale, dev, step=scaler.step)
+        t_first = scaler.step + 1
+        bias = zs.zero_bias_corrections(w.beta1, w.beta2, t_first,
+                                        args.warmup + args.steps + 1).to(dev)
+
+        def one_step(timed: bool):   # noqa: F811  (device-resident control)
+            layout = zs.zero_shard_layout(psi, n, rank)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+            if timed:
+                e[0].record(stream)
+            zs.zero_overflow_check_dev(b["g16"], psi, n, rank, ctl, stream=stream)
+            if timed:
+                e[1].record(stream)
+            zs.zero_scaler_update_dev(ctl, bias, t_first, stream=stream)
+            if timed:
+                e[2].record(stream)
+            zs.zero_adam_step_dev(b["w16"], b["g16"], b["master"], b["m"], b["v"], psi, n, rank,
+                                  ctl=ctl, stream=stream, **hp)
+            if timed:
+                e[3].record(stream)
+                ev.append(e)
+            return layout
+
     for _ in range(args.warmup):
         one_step(False)
     torch.cuda.synchronize()
@@ -223,6 +250,11 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    if args.control == "device":
+        c = zs.device_ctl_read(ctl)
+        if c.status != 0 or c.scaler.step != scaler.step + args.warmup + args.steps:
+            raise RuntimeError(f"device control skipped steps: status {c.status}, "
+                               f"t {c.scaler.step}")
     step_ms = [x[2].elapsed_time(x[3]) for x in ev]
     check_ms = [x[0].elapsed_time(x[1]) for x in ev]
     if not step_ms:
@@ -254,7 +286,8 @@ def main():
         "config": {"workload": w.name, "psi": psi, "zero_ranks": n, "rank": rank,
                    "shard_params": cnt, "grad_weight_dtype": w.dtype,
                    "optimizer": "AdamW" if w.weight_decay else "Adam",
-                   "loss_scale": w.loss_scale, "bytes_per_param": STEP_BYTES_PER_PARAM},
+                   "loss_scale": w.loss_scale, "bytes_per_param": STEP_BYTES_PER_PARAM,
+                   "control": args.control},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic},

@@ -186,6 +186,75 @@ typedef struct {
  */
 int zero_scaler_update(zero_scaler *s, int32_t found_inf, int32_t *apply);
 
+/* ---------------------------------------------------------------------------
+ * Device-resident control: the same check -> decision -> step sequence with
+ * the loss scale, the step counter and the flag kept in device memory, so a
+ * training loop can enqueue step after step without reading anything back.
+ * ------------------------------------------------------------------------- */
+
+/* Control block in device memory.  The caller allocates sizeof(zero_device_ctl)
+ * bytes (4-byte aligned) and initialises `scaler` by copying a host struct in;
+ * the other fields are outputs. */
+typedef struct {
+    zero_scaler scaler;    /* as for zero_scaler_update: S in force, counters */
+    int32_t found_inf;     /* flag of the last zero_overflow_check_dev (0/1) */
+    int32_t apply;         /* 1 if the last zero_scaler_update_dev applied the update */
+    float loss_scale_used; /* S that the applied update unscales with */
+    float bc1;             /* 1 - beta1^t of the applied update */
+    float bc2;             /* 1 - beta2^t of the applied update */
+    int32_t status;        /* 0; ZERO_ERANGE if the bias table missed t (update skipped) */
+} zero_device_ctl;
+
+#define ZERO_ERANGE (-4) /* written to zero_device_ctl.status: t outside the bias table */
+
+/*
+ * zero_bias_corrections -- host helper: bc1[k] = 1 - beta1^(t_first + k) and
+ * bc2[k] = 1 - beta2^(t_first + k) for k < len, each formed in FP64 and
+ * rounded once to FP32, exactly as zero_adam_step forms them ("Training
+ * models too big for one GPU", "Adam, and why it's expensive": bias-corrected
+ * moments).  The device path reads them from a table because the host's libm
+ * fixes their last bit.
+ *   out  host, 2*len floats: bc1[0..len) then bc2[0..len).
+ *   Errors: ZERO_EINVAL if out is NULL, len == 0, t_first == 0, or a beta
+ *   is outside [0, 1).
+ */
+int zero_bias_corrections(float beta1, float beta2, uint64_t t_first, uint32_t len, float *out);
+
+/*
+ * zero_overflow_check_dev -- zero_overflow_check with S read from
+ * d_ctl->scaler.loss_scale on the device; writes d_ctl->found_inf.  In data
+ * parallelism, OR (MAX all-reduce) every rank's found_inf before the decision.
+ *   Errors: as zero_overflow_check (d_ctl replaces loss_scale and d_found_inf;
+ *   S is not checked on the host, a non-positive S on the device reads as
+ *   overflow).
+ */
+int zero_overflow_check_dev(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n,
+                            uint32_t rank, zero_device_ctl *d_ctl, void *stream);
+
+/*
+ * zero_scaler_update_dev -- zero_scaler_update on the device (one thread):
+ * reads found_inf, updates scaler, sets apply, and for an applied update
+ * records loss_scale_used (S before the decision) and bc1, bc2 for the new
+ * step t from the table (entries for t_first .. t_first + len - 1, as
+ * zero_bias_corrections writes them).  If t falls outside the table the
+ * update is skipped, status = ZERO_ERANGE and scaler is left as it was.
+ *   d_bias  device, 2*len floats.
+ *   Errors: ZERO_EINVAL for a NULL or misaligned pointer, len == 0 or
+ *   t_first == 0; ZERO_EHIP if the launch fails.
+ */
+int zero_scaler_update_dev(zero_device_ctl *d_ctl, const float *d_bias, uint64_t t_first,
+                           uint32_t len, void *stream);
+
+/*
+ * zero_adam_step_dev -- zero_adam_step with loss_scale, 1 - beta1^t and
+ * 1 - beta2^t read from d_ctl on the device; writes nothing unless
+ * d_ctl->apply is set.  The other arguments are as for zero_adam_step.
+ */
+int zero_adam_step_dev(void *w16, const void *g16, float *master, float *m, float *v,
+                       zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank, float lr,
+                       float beta1, float beta2, float eps, float weight_decay,
+                       const zero_device_ctl *d_ctl, void *stream);
+
 /*
  * zero_strerror -- text for a return code.  For ZERO_EHIP it names the HIP
  * error of the most recent failing call made by this thread.  The pointer

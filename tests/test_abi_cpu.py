@@ -200,3 +200,70 @@ def test_scaler_errors():
     with pytest.raises(zs.ZeroError):
         zs.zero_scaler_update(st, 1)
     assert zs.lib.zero_scaler_update(None, 0, None) == -1
+
+
+def test_device_ctl_struct_matches_header():
+    src = r"""
+    #include <stddef.h>
+    #include <stdio.h>
+    #include "zero_shard.h"
+    int main(void) {
+      printf("%zu %zu", sizeof(zero_device_ctl), _Alignof(zero_device_ctl));
+    #define F(f) printf(" %zu", offsetof(zero_device_ctl, f));
+      F(scaler) F(found_inf) F(apply) F(loss_scale_used) F(bc1) F(bc2) F(status)
+      printf(" %zu %d", sizeof(zero_scaler), ZERO_ERANGE);
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), c, "-o", exe],
+                       check=True)
+        vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                               check=True).stdout.split()]
+    D = _binding.DeviceCtl
+    assert vals[0] == ctypes.sizeof(D) and vals[1] == ctypes.alignment(D)
+    assert vals[2:9] == [getattr(D, f).offset for f, _ in D._fields_]
+    assert vals[9] == ctypes.sizeof(_binding.Scaler) and vals[10] == -4
+
+
+@pytest.mark.parametrize("b1,b2,t0,n", [(0.9, 0.999, 1, 64), (0.9, 0.999, 101, 20),
+                                        (0.95, 0.9999, 10_000, 7), (0.0, 0.5, 3, 5)])
+def test_bias_table_matches_oracle_scalars(b1, b2, t0, n):
+    tab = zs.zero_bias_corrections(b1, b2, t0, n).numpy()
+    for k in range(n):
+        ref = oracle.step_scalars(1e-3, b1, b2, 0.0, t0 + k)
+        assert tab[k] == ref.bc1 and tab[n + k] == ref.bc2
+
+
+def test_bias_table_errors():
+    for args in ((0.9, 0.999, 0, 4), (1.0, 0.999, 1, 4), (0.9, -0.1, 1, 4)):
+        with pytest.raises(zs.ZeroError):
+            zs.zero_bias_corrections(*args)
+    assert zs.lib.zero_bias_corrections(0.9, 0.999, 1, 0, FAKE) == -1
+    assert zs.lib.zero_bias_corrections(0.9, 0.999, 1, 4, None) == -1
+
+
+def test_device_path_argument_errors():
+    L = zs.lib
+    # check: dtype, layout, misaligned / null control block, null gradients
+    assert L.zero_overflow_check_dev(FAKE, 3, 100, 4, 0, FAKE, None) == -2
+    assert L.zero_overflow_check_dev(FAKE, 0, 100, 4, 4, FAKE, None) == -1
+    assert L.zero_overflow_check_dev(FAKE, 0, 100, 4, 0, None, None) == -1
+    assert L.zero_overflow_check_dev(FAKE, 0, 100, 4, 0, FAKE + 4, None) == -1
+    assert L.zero_overflow_check_dev(None, 0, 100, 4, 0, FAKE, None) == -1
+    # decision: null control block or table, empty table, t_first 0
+    assert L.zero_scaler_update_dev(None, FAKE, 1, 4, None) == -1
+    assert L.zero_scaler_update_dev(FAKE, None, 1, 4, None) == -1
+    assert L.zero_scaler_update_dev(FAKE, FAKE, 1, 0, None) == -1
+    assert L.zero_scaler_update_dev(FAKE, FAKE, 0, 4, None) == -1
+    # step: as zero_adam_step, with the control block required
+    p = (FAKE,) * 5
+    assert L.zero_adam_step_dev(*p, 0, 100, 4, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, None, None) == -1
+    assert L.zero_adam_step_dev(*p, 0, 100, 4, 0, 1e-3, 1.0, 0.999, 1e-8, 0.0, FAKE, None) == -1
+    assert L.zero_adam_step_dev(*p, 2, 100, 4, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, FAKE, None) == -2
+    # empty rank: no launch
+    assert L.zero_adam_step_dev(None, None, None, None, None, 0, 10, 8, 7, 1e-3, 0.9, 0.999,
+                                1e-8, 0.0, FAKE, None) == 0
+    assert "table" in zs.zero_strerror(-4)

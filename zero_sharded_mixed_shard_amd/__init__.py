@@ -14,17 +14,32 @@ Functions carry the names of the C entry points (include/zero_shard.h):
                    weight_decay, step, loss_scale, found_inf=None)
     zero_scaler_update(state: Scaler, found_inf) -> bool   (skip-or-apply, loss scale)
     zero_strerror(code) -> str
+
+Device-resident control (no read-back between steps):
+
+    ctl = device_ctl_new(loss_scale, device)            # zero_device_ctl in device memory
+    bias = zero_bias_corrections(b1, b2, t_first, k).to(device)
+    zero_overflow_check_dev(g16, psi, n, rank, ctl)
+    zero_scaler_update_dev(ctl, bias, t_first)
+    zero_adam_step_dev(w16, g16, master, m, v, psi, n, rank, lr=..., ..., ctl=ctl)
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
     SUMSQ_PARTIALS,
+    DeviceCtl,
     Layout,
     Scaler,
     ZeroError,
     lib,
+    device_ctl_new,
+    device_ctl_read,
     zero_adam_step,
+    zero_adam_step_dev,
+    zero_bias_corrections,
     zero_overflow_check,
+    zero_overflow_check_dev,
     zero_scaler_update,
+    zero_scaler_update_dev,
     zero_shard_layout,
     zero_strerror,
 )
@@ -38,4 +53,11 @@ __all__ = [
     "Scaler",
     "zero_scaler_update",
     "zero_strerror",
+    "DeviceCtl",
+    "device_ctl_new",
+    "device_ctl_read",
+    "zero_bias_corrections",
+    "zero_overflow_check_dev",
+    "zero_scaler_update_dev",
+    "zero_adam_step_dev",
 ]

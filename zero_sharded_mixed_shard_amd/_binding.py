@@ -68,6 +68,24 @@ class Scaler(ctypes.Structure):
 lib.zero_scaler_update.argtypes = [ctypes.POINTER(Scaler), ctypes.c_int32,
                                    ctypes.POINTER(ctypes.c_int32)]
 lib.zero_scaler_update.restype = _i32
+
+
+class DeviceCtl(ctypes.Structure):
+    """zero_device_ctl: the control block the device-resident path keeps in device memory."""
+    _fields_ = [("scaler", Scaler), ("found_inf", ctypes.c_int32), ("apply", ctypes.c_int32),
+                ("loss_scale_used", ctypes.c_float), ("bc1", ctypes.c_float),
+                ("bc2", ctypes.c_float), ("status", ctypes.c_int32)]
+
+
+lib.zero_bias_corrections.argtypes = [_f32, _f32, _u64, _u32, _vp]
+lib.zero_bias_corrections.restype = _i32
+lib.zero_overflow_check_dev.argtypes = [_vp, _i32, _u64, _u32, _u32, _vp, _vp]
+lib.zero_overflow_check_dev.restype = _i32
+lib.zero_scaler_update_dev.argtypes = [_vp, _vp, _u64, _u32, _vp]
+lib.zero_scaler_update_dev.restype = _i32
+lib.zero_adam_step_dev.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32, _u32, _f32, _f32,
+                                   _f32, _f32, _f32, _vp, _vp]
+lib.zero_adam_step_dev.restype = _i32
 lib.zero_strerror.argtypes = [_i32]
 lib.zero_strerror.restype = ctypes.c_char_p
 
@@ -177,3 +195,87 @@ def zero_scaler_update(state: Scaler, found_inf: int) -> bool:
     if rc != 0:
         raise ZeroError(rc, "zero_scaler_update")
     return bool(apply.value)
+
+
+# ---- device-resident control -------------------------------------------------
+
+def device_ctl_new(loss_scale: float, device, growth_interval: int = 2000,
+                   step: int = 0) -> torch.Tensor:
+    """A zero_device_ctl in device memory (a uint8 tensor), initialised from the host."""
+    host = DeviceCtl()
+    host.scaler = Scaler(loss_scale, growth_interval, step)
+    raw = torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8)
+    return raw.to(device)
+
+
+def device_ctl_read(ctl: torch.Tensor) -> DeviceCtl:
+    """Copy a device control block back to the host (synchronises the stream)."""
+    return DeviceCtl.from_buffer_copy(bytes(ctl.cpu().numpy().tobytes()))
+
+
+def _ctl_ptr(ctl: torch.Tensor, device) -> int:
+    if ctl.dtype != torch.uint8 or ctl.numel() < ctypes.sizeof(DeviceCtl) or \
+            ctl.device != device or not ctl.is_contiguous():
+        raise ValueError(f"ctl must be a contiguous uint8 tensor of {ctypes.sizeof(DeviceCtl)} "
+                         f"bytes on {device}")
+    return ctl.data_ptr()
+
+
+def zero_bias_corrections(beta1: float, beta2: float, t_first: int, length: int) -> torch.Tensor:
+    """Host table [bc1 of t_first .. t_first+length-1, then bc2 of the same t] (float32)."""
+    out = torch.empty(2 * length, dtype=torch.float32)
+    rc = lib.zero_bias_corrections(beta1, beta2, t_first, length, out.data_ptr())
+    if rc != 0:
+        raise ZeroError(rc, "zero_bias_corrections")
+    return out
+
+
+def zero_overflow_check_dev(g16: torch.Tensor, psi: int, n: int, rank: int, ctl: torch.Tensor,
+                            stream=None) -> None:
+    """Overflow check with S read on the device; writes ctl.found_inf."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g16.device
+    p_g = _view(g16, "g16", _DTYPES, lay.count, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_overflow_check_dev(p_g, _DTYPES[g16.dtype], psi, n, rank,
+                                         _ctl_ptr(ctl, dev), _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_overflow_check_dev")
+
+
+def zero_scaler_update_dev(ctl: torch.Tensor, bias: torch.Tensor, t_first: int,
+                           stream=None) -> None:
+    """Skip-or-apply decision on the device; `bias` is a device copy of zero_bias_corrections."""
+    dev = ctl.device
+    if bias.dtype != torch.float32 or bias.device != dev or bias.dim() != 1 or \
+            bias.numel() % 2 or not bias.is_contiguous():
+        raise ValueError("bias must be a 1-D float32 device tensor of 2*length entries")
+    with torch.cuda.device(dev):
+        rc = lib.zero_scaler_update_dev(_ctl_ptr(ctl, dev), bias.data_ptr(), t_first,
+                                        bias.numel() // 2, _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_scaler_update_dev")
+
+
+def zero_adam_step_dev(w16: torch.Tensor, g16: torch.Tensor, master: torch.Tensor,
+                       m: torch.Tensor, v: torch.Tensor, psi: int, n: int, rank: int, *,
+                       lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                       ctl: torch.Tensor, stream=None) -> None:
+    """Adam step with S and the bias corrections read from the device control block."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g16.device
+    if w16.dtype != g16.dtype:
+        raise TypeError("w16 and g16 must share one 16-bit dtype")
+    ptrs = [
+        _view(w16, "w16", _DTYPES, lay.count, dev),
+        _view(g16, "g16", _DTYPES, lay.count, dev),
+        _view(master, "master", (torch.float32,), lay.count, dev),
+        _view(m, "m", (torch.float32,), lay.count, dev),
+        _view(v, "v", (torch.float32,), lay.count, dev),
+    ]
+    with torch.cuda.device(dev):
+        rc = lib.zero_adam_step_dev(*ptrs, _DTYPES[g16.dtype], psi, n, rank, lr, beta1, beta2,
+                                    eps, weight_decay, _ctl_ptr(ctl, dev),
+                                    _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_adam_step_dev")

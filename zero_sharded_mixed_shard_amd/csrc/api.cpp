@@ -50,26 +50,74 @@ bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p)
 
 bool finite(float x) { return std::isfinite(x); }
 
+bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; }
+
+// 1 - beta^t formed in FP64 and rounded once to FP32 (bias correction).
+float bias_correction(float beta, uint64_t t) {
+    return static_cast<float>(1.0 - std::pow(static_cast<double>(beta), static_cast<double>(t)));
+}
+
+// Checks shared by both forms of the check; returns the layout's count.
+int check_args(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank,
+               uint64_t *count) {
+    if (dt != ZERO_F16 && dt != ZERO_BF16) return ZERO_EDTYPE;
+    zero_layout lay;
+    if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
+    if (lay.count > 0 && (g16 == nullptr || !aligned(g16, 2))) return ZERO_EINVAL;
+    *count = lay.count;
+    return ZERO_OK;
+}
+
+// Checks shared by both forms of the step, and the scalars that depend on
+// neither the step number nor the loss scale.
+int step_args(void *w16, const void *g16, float *master, float *m, float *v, zero_dtype dt,
+              uint64_t psi, uint32_t n, uint32_t rank, float lr, float beta1, float beta2,
+              float eps, float weight_decay, uint64_t *count, zs::AdamScalars *s) {
+    if (dt != ZERO_F16 && dt != ZERO_BF16) return ZERO_EDTYPE;
+    zero_layout lay;
+    if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
+    if (!beta_ok(beta1) || !beta_ok(beta2)) return ZERO_EINVAL;
+    if (!(eps >= 0.0f) || !finite(eps) || !finite(lr) || !finite(weight_decay)) return ZERO_EINVAL;
+    *count = lay.count;
+    if (lay.count > 0) {
+        if (w16 == nullptr || g16 == nullptr || master == nullptr || m == nullptr || v == nullptr)
+            return ZERO_EINVAL;
+        if (!aligned(w16, 2) || !aligned(g16, 2) || !aligned(master, 4) || !aligned(m, 4) ||
+            !aligned(v, 4))
+            return ZERO_EINVAL;
+    }
+    s->lr = lr;
+    s->beta1 = beta1;
+    s->beta2 = beta2;
+    s->omb1 = 1.0f - beta1;
+    s->omb2 = 1.0f - beta2;
+    s->eps = eps;
+    const float lw = lr * weight_decay;
+    s->decay = 1.0f - lw;
+    s->loss_scale = 1.0f;
+    s->bc1 = 1.0f;
+    s->bc2 = 1.0f;
+    return ZERO_OK;
+}
+
 }  // namespace
 
 extern "C" int zero_overflow_check(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n,
                                    uint32_t rank, float loss_scale, int32_t *d_found_inf,
                                    float *d_sumsq, double *d_partials, void *stream) {
-    if (dt != ZERO_F16 && dt != ZERO_BF16) return ZERO_EDTYPE;
-    zero_layout lay;
-    if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
+    uint64_t count = 0;
+    int rc = check_args(g16, dt, psi, n, rank, &count);
+    if (rc != ZERO_OK) return rc;
     if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
     if (d_found_inf == nullptr || !aligned(d_found_inf, 4)) return ZERO_EINVAL;
     if (d_sumsq != nullptr &&
         (!aligned(d_sumsq, 4) || d_partials == nullptr || !aligned(d_partials, 8)))
         return ZERO_EINVAL;
-    if (lay.count > 0 && (g16 == nullptr || !aligned(g16, 2))) return ZERO_EINVAL;
-
     int cus = 0;
-    const int rc = device_cus(&cus);
+    rc = device_cus(&cus);
     if (rc != ZERO_OK) return rc;
     const hipError_t e = zs::launch_overflow_check(
-        static_cast<int>(dt), static_cast<const uint16_t *>(g16), lay.count, loss_scale,
+        static_cast<int>(dt), static_cast<const uint16_t *>(g16), count, loss_scale, nullptr,
         d_found_inf, d_sumsq, d_partials, cus, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check launch");
 }
@@ -79,39 +127,76 @@ extern "C" int zero_adam_step(void *w16, const void *g16, float *master, float *
                               float beta1, float beta2, float eps, float weight_decay,
                               uint64_t step, float loss_scale, const int32_t *d_found_inf,
                               void *stream) {
-    if (dt != ZERO_F16 && dt != ZERO_BF16) return ZERO_EDTYPE;
-    zero_layout lay;
-    if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
+    uint64_t count = 0;
+    zs::AdamScalars s;
+    const int rc = step_args(w16, g16, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
+                             weight_decay, &count, &s);
+    if (rc != ZERO_OK) return rc;
     if (step == 0) return ZERO_EINVAL;
     if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
-    if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f)) return ZERO_EINVAL;
-    if (!(eps >= 0.0f) || !finite(eps) || !finite(lr) || !finite(weight_decay)) return ZERO_EINVAL;
     if (d_found_inf != nullptr && !aligned(d_found_inf, 4)) return ZERO_EINVAL;
-    if (lay.count == 0) return ZERO_OK;
-    if (w16 == nullptr || g16 == nullptr || master == nullptr || m == nullptr || v == nullptr)
-        return ZERO_EINVAL;
-    if (!aligned(w16, 2) || !aligned(g16, 2) || !aligned(master, 4) || !aligned(m, 4) ||
-        !aligned(v, 4))
-        return ZERO_EINVAL;
-
-    // Host scalars: bias corrections in FP64, rounded once; the rest FP32.
-    zs::AdamScalars s;
+    if (count == 0) return ZERO_OK;
     s.loss_scale = loss_scale;
-    s.lr = lr;
-    s.beta1 = beta1;
-    s.beta2 = beta2;
-    s.omb1 = 1.0f - beta1;
-    s.omb2 = 1.0f - beta2;
-    s.eps = eps;
-    s.bc1 = static_cast<float>(1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step)));
-    s.bc2 = static_cast<float>(1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step)));
-    const float lw = lr * weight_decay;
-    s.decay = 1.0f - lw;
-
+    s.bc1 = bias_correction(beta1, step);
+    s.bc2 = bias_correction(beta2, step);
     const hipError_t e = zs::launch_adam_step(
         static_cast<int>(dt), static_cast<uint16_t *>(w16), static_cast<const uint16_t *>(g16),
-        master, m, v, lay.count, s, d_found_inf, static_cast<hipStream_t>(stream));
+        master, m, v, count, s, d_found_inf, nullptr, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step launch");
+}
+
+extern "C" int zero_bias_corrections(float beta1, float beta2, uint64_t t_first, uint32_t len,
+                                     float *out) {
+    if (out == nullptr || len == 0 || t_first == 0 || !beta_ok(beta1) || !beta_ok(beta2))
+        return ZERO_EINVAL;
+    for (uint32_t k = 0; k < len; ++k) {
+        out[k] = bias_correction(beta1, t_first + k);
+        out[len + k] = bias_correction(beta2, t_first + k);
+    }
+    return ZERO_OK;
+}
+
+extern "C" int zero_overflow_check_dev(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n,
+                                       uint32_t rank, zero_device_ctl *d_ctl, void *stream) {
+    uint64_t count = 0;
+    int rc = check_args(g16, dt, psi, n, rank, &count);
+    if (rc != ZERO_OK) return rc;
+    if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != ZERO_OK) return rc;
+    const hipError_t e = zs::launch_overflow_check(
+        static_cast<int>(dt), static_cast<const uint16_t *>(g16), count, 1.0f,
+        &d_ctl->scaler.loss_scale, &d_ctl->found_inf, nullptr, nullptr, cus,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check_dev launch");
+}
+
+extern "C" int zero_scaler_update_dev(zero_device_ctl *d_ctl, const float *d_bias,
+                                      uint64_t t_first, uint32_t len, void *stream) {
+    if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
+    if (d_bias == nullptr || !aligned(d_bias, 4) || len == 0 || t_first == 0) return ZERO_EINVAL;
+    const hipError_t e =
+        zs::launch_scaler_decide(d_ctl, d_bias, t_first, len, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_scaler_update_dev launch");
+}
+
+extern "C" int zero_adam_step_dev(void *w16, const void *g16, float *master, float *m, float *v,
+                                  zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank,
+                                  float lr, float beta1, float beta2, float eps,
+                                  float weight_decay, const zero_device_ctl *d_ctl,
+                                  void *stream) {
+    uint64_t count = 0;
+    zs::AdamScalars s;
+    const int rc = step_args(w16, g16, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
+                             weight_decay, &count, &s);
+    if (rc != ZERO_OK) return rc;
+    if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
+    if (count == 0) return ZERO_OK;
+    const hipError_t e = zs::launch_adam_step(
+        static_cast<int>(dt), static_cast<uint16_t *>(w16), static_cast<const uint16_t *>(g16),
+        master, m, v, count, s, nullptr, d_ctl, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step_dev launch");
 }
 
 extern "C" const char *zero_strerror(int code) {
@@ -124,6 +209,8 @@ extern "C" const char *zero_strerror(int code) {
             return "unsupported dtype (expected ZERO_F16 or ZERO_BF16)";
         case ZERO_EHIP:
             return g_err[0] ? g_err : "HIP runtime error";
+        case ZERO_ERANGE:
+            return "step outside the bias-correction table";
         default:
             return "unknown error code";
     }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "zero_shard.h"
+
 namespace zs {
 
 // Per-call scalars of the Adam step, all formed on the host.
@@ -27,16 +29,22 @@ struct AdamScalars {
 constexpr uint64_t kMaxBlocks = 1ull << 23;
 
 // Enqueue the Adam step over `count` elements of five shard views.  The
-// caller has validated every argument; count > 0.
+// caller has validated every argument; count > 0.  flag (nullable): skip if
+// set.  ctl (nullable): skip unless ctl->apply, and take S, bc1, bc2 from it.
 hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float *master, float *m,
                             float *v, uint64_t count, const AdamScalars &s, const int32_t *flag,
-                            hipStream_t stream);
+                            const zero_device_ctl *ctl, hipStream_t stream);
 
 // Enqueue the unscale + overflow check of `count` gradients (count may be 0:
 // then only the outputs are cleared).  partials holds ZERO_SUMSQ_PARTIALS
-// doubles when sumsq is non-null.
+// doubles when sumsq is non-null.  loss_scale_dev (nullable) replaces
+// loss_scale with a value read on the device.
 hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
-                                 int32_t *flag, float *sumsq, double *partials, int num_cus,
-                                 hipStream_t stream);
+                                 const float *loss_scale_dev, int32_t *flag, float *sumsq,
+                                 double *partials, int num_cus, hipStream_t stream);
+
+// Enqueue the one-lane skip-or-apply decision on a device control block.
+hipError_t launch_scaler_decide(zero_device_ctl *ctl, const float *bias, uint64_t t_first,
+                                uint32_t len, hipStream_t stream);
 
 }  // namespace zs

@@ -21,6 +21,7 @@
 #include <stdint.h>
 
 #include "launch.h"
+#include "zero_shard.h"
 
 #pragma clang fp contract(off)
 
@@ -103,6 +104,18 @@ __device__ __forceinline__ void adam_one(uint16_t *__restrict__ w16,
     w16[i] = static_cast<uint16_t>(w);
 }
 
+// With a device control block, the update runs only if the decision applied
+// it, and S and the bias corrections come from the block.
+__device__ __forceinline__ bool take_device_scalars(const zero_device_ctl *__restrict__ ctl,
+                                                    AdamScalars &s) {
+    if (ctl == nullptr) return true;
+    if (ctl->apply == 0) return false;
+    s.loss_scale = ctl->loss_scale_used;
+    s.bc1 = ctl->bc1;
+    s.bc2 = ctl->bc2;
+    return true;
+}
+
 // ---- the step: aligned vector path ----------------------------------------
 //
 // Elements [0, head) and [head + n_tiles*U*kGroup, count) are done one at a
@@ -115,8 +128,10 @@ template <int DT, int U>
 __global__ __launch_bounds__(kThreads) void adam_step_vec(
     uint16_t *__restrict__ w16, const uint16_t *__restrict__ g16, float *__restrict__ master,
     float *__restrict__ m, float *__restrict__ v, uint64_t count, uint32_t head,
-    uint64_t n_tiles, AdamScalars s, const int32_t *__restrict__ flag) {
+    uint64_t n_tiles, AdamScalars s, const int32_t *__restrict__ flag,
+    const zero_device_ctl *__restrict__ ctl) {
     if (flag != nullptr && *flag != 0) return;
+    if (!take_device_scalars(ctl, s)) return;
     const uint32_t tid = threadIdx.x;
     if (blockIdx.x == 0 && tid < head) adam_one<DT>(w16, g16, master, m, v, tid, s);
 
@@ -164,8 +179,9 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void adam_step_elem(
     uint16_t *__restrict__ w16, const uint16_t *__restrict__ g16, float *__restrict__ master,
     float *__restrict__ m, float *__restrict__ v, uint64_t count, AdamScalars s,
-    const int32_t *__restrict__ flag) {
+    const int32_t *__restrict__ flag, const zero_device_ctl *__restrict__ ctl) {
     if (flag != nullptr && *flag != 0) return;
+    if (!take_device_scalars(ctl, s)) return;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < count;
          i += stride)
@@ -192,8 +208,9 @@ __global__ void check_init(int32_t *__restrict__ flag, float *__restrict__ sumsq
 template <int DT, int U>
 __global__ __launch_bounds__(kThreads) void overflow_flag_kernel(
     const uint16_t *__restrict__ g16, uint64_t count, uint32_t head, uint64_t n_vec,
-    float loss_scale, int32_t *__restrict__ flag) {
+    float loss_scale, const float *__restrict__ loss_scale_dev, int32_t *__restrict__ flag) {
     constexpr uint32_t kExpField = DT == 0 ? 0x7c00u : 0x7f80u;  // inf/NaN at or above
+    if (loss_scale_dev != nullptr) loss_scale = *loss_scale_dev;
     const uint32_t tid = threadIdx.x;
     u16x2 mx2 = {0, 0};
     uint32_t mx = 0;
@@ -226,7 +243,8 @@ __global__ __launch_bounds__(kThreads) void overflow_flag_kernel(
     }
     mx = mx > mx2.x ? mx : mx2.x;
     mx = mx > mx2.y ? mx : mx2.y;
-    const uint32_t bad = mx >= kExpField || not_finite(widen<DT>(mx) / loss_scale);
+    const uint32_t bad = mx >= kExpField || not_finite(widen<DT>(mx) / loss_scale) ||
+                         !(loss_scale > 0.0f) || not_finite(loss_scale);
     if (__any(bad)) {
         if ((tid & 63u) == 0) *flag = 1;
     }
@@ -239,9 +257,11 @@ __global__ __launch_bounds__(kThreads) void overflow_flag_kernel(
 template <int DT, int U>
 __global__ __launch_bounds__(kThreads) void overflow_sumsq_kernel(
     const uint16_t *__restrict__ g16, uint64_t count, uint32_t head, uint64_t n_vec,
-    float loss_scale, int32_t *__restrict__ flag, double *__restrict__ partials) {
+    float loss_scale, const float *__restrict__ loss_scale_dev, int32_t *__restrict__ flag,
+    double *__restrict__ partials) {
+    if (loss_scale_dev != nullptr) loss_scale = *loss_scale_dev;
     const uint32_t tid = threadIdx.x;
-    uint32_t bad = 0;
+    uint32_t bad = !(loss_scale > 0.0f) || not_finite(loss_scale);
     double acc = 0.0;
     auto visit = [&](uint32_t h) {
         const float q = widen<DT>(h) / loss_scale;
@@ -312,6 +332,51 @@ __global__ __launch_bounds__(kThreads) void sumsq_finalize(const double *__restr
     if (tid == 0) *sumsq = static_cast<float>(red[0]);
 }
 
+// ---- skip-or-apply decision on the device ---------------------------------
+//
+// One lane applies the host policy of zero_scaler_update to the control
+// block: overflow halves S; a clean step advances t, doubles S after a run of
+// growth_interval clean steps (unless 2S overflows), and records the S the
+// update unscales with and the bias corrections of t from the host's table.
+__global__ void scaler_decide(zero_device_ctl *__restrict__ ctl, const float *__restrict__ bias,
+                              uint64_t t_first, uint32_t len) {
+    if (threadIdx.x != 0) return;
+    zero_scaler sc = ctl->scaler;
+    const float S = sc.loss_scale;
+    if (!(S > 0.0f) || not_finite(S)) {
+        ctl->apply = 0;
+        ctl->status = ZERO_EINVAL;
+        return;
+    }
+    if (ctl->found_inf != 0) {
+        sc.loss_scale = S * 0.5f;
+        sc.clean_steps = 0;
+        ctl->scaler = sc;
+        ctl->apply = 0;
+        ctl->status = ZERO_OK;
+        return;
+    }
+    const uint64_t t = sc.step + 1;
+    if (t < t_first || t - t_first >= len) {
+        ctl->apply = 0;
+        ctl->status = ZERO_ERANGE;
+        return;
+    }
+    sc.step = t;
+    sc.clean_steps += 1;
+    if (sc.growth_interval != 0 && sc.clean_steps >= sc.growth_interval) {
+        const float grown = S * 2.0f;
+        if (!not_finite(grown)) sc.loss_scale = grown;
+        sc.clean_steps = 0;
+    }
+    ctl->scaler = sc;
+    ctl->loss_scale_used = S;
+    ctl->bc1 = bias[t - t_first];
+    ctl->bc2 = bias[len + (t - t_first)];
+    ctl->apply = 1;
+    ctl->status = ZERO_OK;
+}
+
 // ---- launch helpers --------------------------------------------------------
 
 constexpr int kAdamU = 2;              // groups in flight per lane in the step
@@ -327,7 +392,7 @@ inline uint32_t align_head(uintptr_t addr, uint32_t elem_bytes, uint32_t align) 
 template <int DT>
 hipError_t adam_dispatch(uint16_t *w16, const uint16_t *g16, float *master, float *m, float *v,
                          uint64_t count, const AdamScalars &s, const int32_t *flag,
-                         hipStream_t stream) {
+                         const zero_device_ctl *ctl, hipStream_t stream) {
     const uint64_t max_blocks = kMaxBlocks;
     uint32_t head = align_head(reinterpret_cast<uintptr_t>(master), 4, 16);
     const bool same_phase =
@@ -339,7 +404,7 @@ hipError_t adam_dispatch(uint16_t *w16, const uint16_t *g16, float *master, floa
         const uint64_t need = (count + kThreads - 1) / kThreads;
         const uint32_t blocks = static_cast<uint32_t>(need < max_blocks ? need : max_blocks);
         adam_step_elem<DT><<<blocks, kThreads, 0, stream>>>(w16, g16, master, m, v, count, s,
-                                                             flag);
+                                                             flag, ctl);
         return hipGetLastError();
     }
     if (head > count) head = static_cast<uint32_t>(count);
@@ -350,7 +415,7 @@ hipError_t adam_dispatch(uint16_t *w16, const uint16_t *g16, float *master, floa
     if (need == 0) need = 1;
     const uint32_t blocks = static_cast<uint32_t>(need < max_blocks ? need : max_blocks);
     adam_step_vec<DT, kAdamU><<<blocks, kThreads, 0, stream>>>(w16, g16, master, m, v, count,
-                                                               head, n_tiles, s, flag);
+                                                               head, n_tiles, s, flag, ctl);
     return hipGetLastError();
 }
 
@@ -380,16 +445,17 @@ inline CheckGrid check_grid(const uint16_t *g16, uint64_t count, bool sumsq, int
 }
 
 template <int DT>
-hipError_t check_dispatch(const uint16_t *g16, uint64_t count, float loss_scale, int32_t *flag,
-                          float *sumsq, double *partials, int num_cus, hipStream_t stream) {
+hipError_t check_dispatch(const uint16_t *g16, uint64_t count, float loss_scale,
+                          const float *loss_scale_dev, int32_t *flag, float *sumsq,
+                          double *partials, int num_cus, hipStream_t stream) {
     const CheckGrid c = check_grid(g16, count, sumsq != nullptr, num_cus);
     if (sumsq == nullptr) {
         overflow_flag_kernel<DT, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
-            g16, count, c.head, c.n_vec, loss_scale, flag);
+            g16, count, c.head, c.n_vec, loss_scale, loss_scale_dev, flag);
         return hipGetLastError();
     }
     overflow_sumsq_kernel<DT, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
-        g16, count, c.head, c.n_vec, loss_scale, flag, partials);
+        g16, count, c.head, c.n_vec, loss_scale, loss_scale_dev, flag, partials);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     sumsq_finalize<<<1, kThreads, 0, stream>>>(partials, c.blocks, sumsq);
@@ -400,20 +466,28 @@ hipError_t check_dispatch(const uint16_t *g16, uint64_t count, float loss_scale,
 
 hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float *master, float *m,
                             float *v, uint64_t count, const AdamScalars &s, const int32_t *flag,
-                            hipStream_t stream) {
-    if (dtype == 0) return adam_dispatch<0>(w16, g16, master, m, v, count, s, flag, stream);
-    return adam_dispatch<1>(w16, g16, master, m, v, count, s, flag, stream);
+                            const zero_device_ctl *ctl, hipStream_t stream) {
+    if (dtype == 0) return adam_dispatch<0>(w16, g16, master, m, v, count, s, flag, ctl, stream);
+    return adam_dispatch<1>(w16, g16, master, m, v, count, s, flag, ctl, stream);
 }
 
 hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
-                                 int32_t *flag, float *sumsq, double *partials, int num_cus,
-                                 hipStream_t stream) {
+                                 const float *loss_scale_dev, int32_t *flag, float *sumsq,
+                                 double *partials, int num_cus, hipStream_t stream) {
     check_init<<<1, 64, 0, stream>>>(flag, sumsq);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess || count == 0) return err;
     if (dtype == 0)
-        return check_dispatch<0>(g16, count, loss_scale, flag, sumsq, partials, num_cus, stream);
-    return check_dispatch<1>(g16, count, loss_scale, flag, sumsq, partials, num_cus, stream);
+        return check_dispatch<0>(g16, count, loss_scale, loss_scale_dev, flag, sumsq, partials,
+                                 num_cus, stream);
+    return check_dispatch<1>(g16, count, loss_scale, loss_scale_dev, flag, sumsq, partials,
+                             num_cus, stream);
+}
+
+hipError_t launch_scaler_decide(zero_device_ctl *ctl, const float *bias, uint64_t t_first,
+                                uint32_t len, hipStream_t stream) {
+    scaler_decide<<<1, 64, 0, stream>>>(ctl, bias, t_first, len);
+    return hipGetLastError();
 }
 
 }  // namespace zs
