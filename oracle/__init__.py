@@ -97,8 +97,14 @@ def _load():
                                          u64, f32]
         lib.oracle_adam_step_f64.argtypes = [vp, vp, vp, vp, i32, u64, f64, f64, f64, f64, f64,
                                              u64, f64]
+        lib.oracle_grad_accumulate.argtypes = [vp, vp, i32, u64, i32]
+        lib.oracle_overflow_check_g32.argtypes = [vp, u64, f32, vp, vp]
+        lib.oracle_adam_step_g32.argtypes = [vp, vp, vp, vp, vp, i32, u64, f32, f32, f32, f32,
+                                             f32, u64, f32]
         for name in ("oracle_decode16_array", "oracle_encode16_array", "oracle_overflow_check",
-                     "oracle_step_scalars", "oracle_adam_step", "oracle_adam_step_f64"):
+                     "oracle_step_scalars", "oracle_adam_step", "oracle_adam_step_f64",
+                     "oracle_grad_accumulate", "oracle_overflow_check_g32",
+                     "oracle_adam_step_g32"):
             getattr(lib, name).restype = None
         _lib = lib
     return _lib
@@ -198,6 +204,36 @@ def adam_step_f64(master, m, v, g16, dtype, *, lr, beta1, beta2, eps, weight_dec
                                  float(np.float32(beta2)), float(np.float32(eps)),
                                  float(np.float32(weight_decay)), step,
                                  float(np.float32(loss_scale)))
+
+
+def grad_accumulate(acc, g16, dtype, first: bool) -> None:
+    """acc = float(g16) if first else acc + float(g16), in FP32, in place."""
+    if acc.size != g16.size:
+        raise ValueError("length mismatch")
+    _load().oracle_grad_accumulate(_ptr(acc, np.float32), _ptr(g16, np.uint16), DTYPES[dtype],
+                                   g16.size, int(bool(first)))
+
+
+def overflow_check_g32(g32, loss_scale: float) -> tuple[int, float]:
+    """overflow_check over FP32 gradients: (found_inf, FP64 sum of unscaled squares)."""
+    flag = np.zeros(1, np.int32)
+    s = np.zeros(1, np.float64)
+    _load().oracle_overflow_check_g32(_ptr(g32, np.float32), g32.size, loss_scale,
+                                      flag.ctypes.data, s.ctypes.data)
+    return int(flag[0]), float(s[0])
+
+
+def adam_step_g32(w16, g32, master, m, v, dtype, *, lr, beta1, beta2, eps, weight_decay, step,
+                  loss_scale) -> None:
+    """adam_step with FP32 gradients (dtype is the working weights' format)."""
+    count = g32.size
+    for a in (w16, master, m, v):
+        if a.size != count:
+            raise ValueError("all shard arrays must have the same length")
+    _load().oracle_adam_step_g32(_ptr(w16, np.uint16), _ptr(g32, np.float32),
+                                 _ptr(master, np.float32), _ptr(m, np.float32),
+                                 _ptr(v, np.float32), DTYPES[dtype], count, lr, beta1, beta2, eps,
+                                 weight_decay, step, loss_scale)
 
 
 @dataclass

@@ -232,26 +232,78 @@ void oracle_step_scalars(float lr, float beta1, float beta2, float weight_decay,
 /* last line's product and quotient are taken left to right.               */
 /* ------------------------------------------------------------------------ */
 
+/* One element of the step from its unscaled-gradient input graw. */
+static void update_one(float graw, float loss_scale, float lr, float beta1, float beta2, float eps,
+                       const oracle_scalars_t *k, float *master, float *m, float *v,
+                       uint16_t *w16, int dtype)
+{
+    const float g = graw / loss_scale;
+    const float p = *master * k->decay;
+    const float m_new = beta1 * *m + k->omb1 * g;
+    const float v_new = beta2 * *v + k->omb2 * (g * g);
+    const float m_hat = m_new / k->bc1;
+    const float v_hat = v_new / k->bc2;
+    const float denom = sqrtf(v_hat) + eps;
+    const float p_new = p - lr * m_hat / denom;
+    *master = p_new;
+    *m = m_new;
+    *v = v_new;
+    *w16 = oracle_encode16((double)p_new, dtype);
+}
+
 void oracle_adam_step(uint16_t *w16, const uint16_t *g16, float *master, float *m, float *v,
                       int dtype, uint64_t count, float lr, float beta1, float beta2, float eps,
                       float weight_decay, uint64_t step, float loss_scale)
 {
     oracle_scalars_t k;
     oracle_step_scalars(lr, beta1, beta2, weight_decay, step, &k);
+    for (uint64_t i = 0; i < count; ++i)
+        update_one((float)oracle_decode16(g16[i], dtype), loss_scale, lr, beta1, beta2, eps, &k,
+                   &master[i], &m[i], &v[i], &w16[i], dtype);
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP32 gradients.  Accumulating many 16-bit micro-batch gradients in a     */
+/* 16-bit buffer loses the small contributions, so the accumulator is FP32  */
+/* ("How far does splitting the batch get you?", "What does gradient        */
+/* accumulation actually buy?").  The accumulate adds each micro-batch's    */
+/* 16-bit gradient in FP32 (the first one initialises it); the check and    */
+/* the step then read the FP32 gradients, with the same definitions.        */
+/* ------------------------------------------------------------------------ */
+
+void oracle_grad_accumulate(float *acc, const uint16_t *g16, int dtype, uint64_t count, int first)
+{
     for (uint64_t i = 0; i < count; ++i) {
-        const float g = (float)oracle_decode16(g16[i], dtype) / loss_scale;
-        const float p = master[i] * k.decay;
-        const float m_new = beta1 * m[i] + k.omb1 * g;
-        const float v_new = beta2 * v[i] + k.omb2 * (g * g);
-        const float m_hat = m_new / k.bc1;
-        const float v_hat = v_new / k.bc2;
-        const float denom = sqrtf(v_hat) + eps;
-        const float p_new = p - lr * m_hat / denom;
-        master[i] = p_new;
-        m[i] = m_new;
-        v[i] = v_new;
-        w16[i] = oracle_encode16((double)p_new, dtype);
+        const float g = (float)oracle_decode16(g16[i], dtype);
+        acc[i] = first ? g : acc[i] + g;
     }
+}
+
+void oracle_overflow_check_g32(const float *g32, uint64_t count, float loss_scale,
+                               int32_t *found_inf, double *sumsq)
+{
+    int32_t flag = 0;
+    double s = 0.0;
+    for (uint64_t i = 0; i < count; ++i) {
+        const float g = g32[i] / loss_scale;
+        if (!isfinite(g))
+            flag = 1;
+        s += (double)g * (double)g;
+    }
+    *found_inf = flag;
+    if (sumsq)
+        *sumsq = s;
+}
+
+void oracle_adam_step_g32(uint16_t *w16, const float *g32, float *master, float *m, float *v,
+                          int dtype, uint64_t count, float lr, float beta1, float beta2, float eps,
+                          float weight_decay, uint64_t step, float loss_scale)
+{
+    oracle_scalars_t k;
+    oracle_step_scalars(lr, beta1, beta2, weight_decay, step, &k);
+    for (uint64_t i = 0; i < count; ++i)
+        update_one(g32[i], loss_scale, lr, beta1, beta2, eps, &k, &master[i], &m[i], &v[i],
+                   &w16[i], dtype);
 }
 
 /* The same update carried out in FP64 from the same FP32 inputs and the    */
