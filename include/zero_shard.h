@@ -187,6 +187,43 @@ typedef struct {
 int zero_scaler_update(zero_scaler *s, int32_t found_inf, int32_t *apply);
 
 /* ---------------------------------------------------------------------------
+ * FP32 gradients.  Accumulating many 16-bit micro-batch gradients in a 16-bit
+ * buffer loses the small contributions, so the accumulator is FP32 and the
+ * reduction and the step read FP32 gradients ("How far does splitting the
+ * batch get you?", "What does gradient accumulation actually buy?").
+ * ------------------------------------------------------------------------- */
+
+/*
+ * zero_grad_accumulate -- acc[i] = float(g16[i]) when `first` is non-zero,
+ * acc[i] + float(g16[i]) (one FP32 addition) otherwise, for i in [0, count):
+ * one micro-batch into the FP32 accumulator of this rank's shard.  10 bytes
+ * of traffic per element (6 for the first micro-batch).
+ *   acc  device, FP32 shard view (4-byte aligned), read unless first, written.
+ *   g16  device, 16-bit shard view of format dt.
+ *   Errors: ZERO_EDTYPE; ZERO_EINVAL for bad layout arguments or a NULL or
+ *   misaligned pointer with count > 0; ZERO_EHIP.  count == 0: no-op.
+ */
+int zero_grad_accumulate(float *acc, const void *g16, zero_dtype dt, uint64_t psi, uint32_t n,
+                         uint32_t rank, int32_t first, void *stream);
+
+/*
+ * zero_overflow_check_g32 -- zero_overflow_check over FP32 gradients
+ * (4 bytes per element); same outputs, scratch and errors.
+ */
+int zero_overflow_check_g32(const float *g32, uint64_t psi, uint32_t n, uint32_t rank,
+                            float loss_scale, int32_t *d_found_inf, float *d_sumsq,
+                            double *d_partials, void *stream);
+
+/*
+ * zero_adam_step_g32 -- zero_adam_step with FP32 gradients: g = g32 / S, the
+ * rest identical; dt is the working weights' format.  30 bytes per element.
+ */
+int zero_adam_step_g32(void *w16, const float *g32, float *master, float *m, float *v,
+                       zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank, float lr,
+                       float beta1, float beta2, float eps, float weight_decay, uint64_t step,
+                       float loss_scale, const int32_t *d_found_inf, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Device-resident control: the same check -> decision -> step sequence with
  * the loss scale, the step counter and the flag kept in device memory, so a
  * training loop can enqueue step after step without reading anything back.

@@ -46,7 +46,8 @@ def test_no_forbidden_instructions(asm):
 def test_step_kernels_keep_each_operation_correctly_rounded(asm):
     _, kernels = asm
     steps = {k: b for k, b in kernels.items() if "adam_step" in k}
-    assert len(steps) == 4  # vector and element-wise kernels, FP16 and BF16
+    # vector and element-wise kernels, FP16 and BF16 weights, 16-bit and FP32 gradients
+    assert len(steps) == 8
     for name, body in steps.items():
         sq = count(body, "v_sqrt_f32_e32") + count(body, "v_sqrt_f32_e64")
         assert sq >= 1, name
@@ -64,10 +65,30 @@ def test_step_kernels_keep_each_operation_correctly_rounded(asm):
 
 def test_vector_step_uses_16_byte_accesses(asm):
     _, kernels = asm
-    vec = [b for k, b in kernels.items() if "adam_step_vec" in k]
-    assert len(vec) == 2
-    for body in vec:
-        assert count(body, "global_load_dwordx4") >= 6     # master, m, v x U groups
+    vec = {k: b for k, b in kernels.items() if "adam_step_vec" in k}
+    assert len(vec) == 4
+    for name, body in vec.items():
+        g32 = "EfLi" in name     # FP32 gradients: one more 16-B load per group
+        assert count(body, "global_load_dwordx4") >= (8 if g32 else 6)  # master, m, v (, g)
         assert count(body, "global_store_dwordx4") >= 6
-        assert count(body, "global_load_dwordx2") >= 2     # 4 gradients per lane per group
-        assert count(body, "global_store_dwordx2") >= 2    # 4 working weights
+        if not g32:
+            assert count(body, "global_load_dwordx2") >= 2  # 4 gradients per lane per group
+        assert count(body, "global_store_dwordx2") >= 2     # 4 working weights
+    acc = [b for k, b in kernels.items() if "accumulate_vec" in k]
+    assert len(acc) == 4
+    for body in acc:
+        assert count(body, "global_store_dwordx4") >= 2
+
+
+def test_sum_of_squares_visits_every_vector_lane(asm):
+    # each lane's 16-B vectors hold 8 (16-bit) or 4 (FP32) gradients; every one
+    # is widened to FP64 and squared: 4 vectors in flight + 1 remainder vector
+    # + the scalar head and tail
+    _, kernels = asm
+    sumsq = {k: b for k, b in kernels.items() if "overflow_sumsq_kernel" in k}
+    assert len(sumsq) == 3
+    for name, body in sumsq.items():
+        per_vec = 4 if "IfLi" in name else 8
+        assert count(body, "v_cvt_f64_f32_e32") == 5 * per_vec + 2, name
+        assert count(body, "v_mul_f64") == 5 * per_vec + 2, name
+        assert count(body, "global_load_dwordx4") == 5, name

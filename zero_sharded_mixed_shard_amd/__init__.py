@@ -15,6 +15,12 @@ Functions carry the names of the C entry points (include/zero_shard.h):
     zero_scaler_update(state: Scaler, found_inf) -> bool   (skip-or-apply, loss scale)
     zero_strerror(code) -> str
 
+FP32 gradients (accumulated across micro-batches):
+
+    zero_grad_accumulate(acc32, g16, psi, n, rank, first)
+    zero_overflow_check_g32(g32, psi, n, rank, loss_scale, found_inf, sumsq=None, partials=None)
+    zero_adam_step_g32(w16, g32, master, m, v, psi, n, rank, *, lr, ..., step, loss_scale)
+
 Device-resident control (no read-back between steps):
 
     ctl = device_ctl_new(loss_scale, device)            # zero_device_ctl in device memory
@@ -35,9 +41,12 @@ from ._binding import (  # noqa: F401
     device_ctl_read,
     zero_adam_step,
     zero_adam_step_dev,
+    zero_adam_step_g32,
     zero_bias_corrections,
+    zero_grad_accumulate,
     zero_overflow_check,
     zero_overflow_check_dev,
+    zero_overflow_check_g32,
     zero_scaler_update,
     zero_scaler_update_dev,
     zero_shard_layout,
@@ -60,4 +69,7 @@ __all__ = [
     "zero_overflow_check_dev",
     "zero_scaler_update_dev",
     "zero_adam_step_dev",
+    "zero_grad_accumulate",
+    "zero_overflow_check_g32",
+    "zero_adam_step_g32",
 ]

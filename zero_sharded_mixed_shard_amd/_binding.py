@@ -77,6 +77,13 @@ class DeviceCtl(ctypes.Structure):
                 ("bc2", ctypes.c_float), ("status", ctypes.c_int32)]
 
 
+lib.zero_grad_accumulate.argtypes = [_vp, _vp, _i32, _u64, _u32, _u32, ctypes.c_int32, _vp]
+lib.zero_grad_accumulate.restype = _i32
+lib.zero_overflow_check_g32.argtypes = [_vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _vp]
+lib.zero_overflow_check_g32.restype = _i32
+lib.zero_adam_step_g32.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32, _u32, _f32, _f32,
+                                   _f32, _f32, _f32, _u64, _f32, _vp, _vp]
+lib.zero_adam_step_g32.restype = _i32
 lib.zero_bias_corrections.argtypes = [_f32, _f32, _u64, _u32, _vp]
 lib.zero_bias_corrections.restype = _i32
 lib.zero_overflow_check_dev.argtypes = [_vp, _i32, _u64, _u32, _u32, _vp, _vp]
@@ -279,3 +286,64 @@ def zero_adam_step_dev(w16: torch.Tensor, g16: torch.Tensor, master: torch.Tenso
                                     _stream_handle(stream, dev))
     if rc != 0:
         raise ZeroError(rc, "zero_adam_step_dev")
+
+
+# ---- FP32 gradients ------------------------------------------------------------
+
+def zero_grad_accumulate(acc: torch.Tensor, g16: torch.Tensor, psi: int, n: int, rank: int,
+                         first: bool, stream=None) -> None:
+    """acc = float(g16) (first) or acc + float(g16): one micro-batch into the FP32 accumulator."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g16.device
+    p_g = _view(g16, "g16", _DTYPES, lay.count, dev)
+    p_a = _view(acc, "acc", (torch.float32,), lay.count, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_grad_accumulate(p_a, p_g, _DTYPES[g16.dtype], psi, n, rank, int(bool(first)),
+                                      _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_grad_accumulate")
+
+
+def zero_overflow_check_g32(g32: torch.Tensor, psi: int, n: int, rank: int, loss_scale: float,
+                            found_inf: torch.Tensor, sumsq: torch.Tensor | None = None,
+                            partials: torch.Tensor | None = None, stream=None) -> None:
+    """Overflow check (and optional sum of squares) over FP32 gradients."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g32.device
+    p_g = _view(g32, "g32", (torch.float32,), lay.count, dev)
+    p_f = _view(found_inf, "found_inf", (torch.int32,), 1, dev)
+    p_s = p_p = None
+    if sumsq is not None:
+        p_s = _view(sumsq, "sumsq", (torch.float32,), 1, dev)
+        if partials is None:
+            raise ValueError("sumsq needs a partials buffer of SUMSQ_PARTIALS float64")
+        p_p = _view(partials, "partials", (torch.float64,), SUMSQ_PARTIALS, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_overflow_check_g32(p_g, psi, n, rank, loss_scale, p_f, p_s, p_p,
+                                         _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_overflow_check_g32")
+
+
+def zero_adam_step_g32(w16: torch.Tensor, g32: torch.Tensor, master: torch.Tensor,
+                       m: torch.Tensor, v: torch.Tensor, psi: int, n: int, rank: int, *,
+                       lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                       step: int, loss_scale: float, found_inf: torch.Tensor | None = None,
+                       stream=None) -> None:
+    """Adam step reading FP32 gradients; w16's dtype sets the working weights' format."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g32.device
+    ptrs = [
+        _view(w16, "w16", _DTYPES, lay.count, dev),
+        _view(g32, "g32", (torch.float32,), lay.count, dev),
+        _view(master, "master", (torch.float32,), lay.count, dev),
+        _view(m, "m", (torch.float32,), lay.count, dev),
+        _view(v, "v", (torch.float32,), lay.count, dev),
+    ]
+    p_f = None if found_inf is None else _view(found_inf, "found_inf", (torch.int32,), 1, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_adam_step_g32(*ptrs, _DTYPES[w16.dtype], psi, n, rank, lr, beta1, beta2,
+                                    eps, weight_decay, step, loss_scale, p_f,
+                                    _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_adam_step_g32")

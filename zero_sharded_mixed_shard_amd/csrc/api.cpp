@@ -68,11 +68,12 @@ int check_args(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n, uint32_
     return ZERO_OK;
 }
 
-// Checks shared by both forms of the step, and the scalars that depend on
-// neither the step number nor the loss scale.
-int step_args(void *w16, const void *g16, float *master, float *m, float *v, zero_dtype dt,
-              uint64_t psi, uint32_t n, uint32_t rank, float lr, float beta1, float beta2,
-              float eps, float weight_decay, uint64_t *count, zs::AdamScalars *s) {
+// Checks shared by every form of the step, and the scalars that depend on
+// neither the step number nor the loss scale.  g is the gradient view and
+// g_align its element size (2 for 16-bit, 4 for FP32 gradients).
+int step_args(void *w16, const void *g, uintptr_t g_align, float *master, float *m, float *v,
+              zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank, float lr, float beta1,
+              float beta2, float eps, float weight_decay, uint64_t *count, zs::AdamScalars *s) {
     if (dt != ZERO_F16 && dt != ZERO_BF16) return ZERO_EDTYPE;
     zero_layout lay;
     if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
@@ -80,9 +81,9 @@ int step_args(void *w16, const void *g16, float *master, float *m, float *v, zer
     if (!(eps >= 0.0f) || !finite(eps) || !finite(lr) || !finite(weight_decay)) return ZERO_EINVAL;
     *count = lay.count;
     if (lay.count > 0) {
-        if (w16 == nullptr || g16 == nullptr || master == nullptr || m == nullptr || v == nullptr)
+        if (w16 == nullptr || g == nullptr || master == nullptr || m == nullptr || v == nullptr)
             return ZERO_EINVAL;
-        if (!aligned(w16, 2) || !aligned(g16, 2) || !aligned(master, 4) || !aligned(m, 4) ||
+        if (!aligned(w16, 2) || !aligned(g, g_align) || !aligned(master, 4) || !aligned(m, 4) ||
             !aligned(v, 4))
             return ZERO_EINVAL;
     }
@@ -129,7 +130,7 @@ extern "C" int zero_adam_step(void *w16, const void *g16, float *master, float *
                               void *stream) {
     uint64_t count = 0;
     zs::AdamScalars s;
-    const int rc = step_args(w16, g16, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
+    const int rc = step_args(w16, g16, 2, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
                              weight_decay, &count, &s);
     if (rc != ZERO_OK) return rc;
     if (step == 0) return ZERO_EINVAL;
@@ -143,6 +144,63 @@ extern "C" int zero_adam_step(void *w16, const void *g16, float *master, float *
         static_cast<int>(dt), static_cast<uint16_t *>(w16), static_cast<const uint16_t *>(g16),
         master, m, v, count, s, d_found_inf, nullptr, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step launch");
+}
+
+extern "C" int zero_grad_accumulate(float *acc, const void *g16, zero_dtype dt, uint64_t psi,
+                                    uint32_t n, uint32_t rank, int32_t first, void *stream) {
+    uint64_t count = 0;
+    const int rc = check_args(g16, dt, psi, n, rank, &count);
+    if (rc != ZERO_OK) return rc;
+    if (count == 0) return ZERO_OK;
+    if (acc == nullptr || !aligned(acc, 4)) return ZERO_EINVAL;
+    const hipError_t e =
+        zs::launch_grad_accumulate(static_cast<int>(dt), acc, static_cast<const uint16_t *>(g16),
+                                   count, first != 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_grad_accumulate launch");
+}
+
+extern "C" int zero_overflow_check_g32(const float *g32, uint64_t psi, uint32_t n, uint32_t rank,
+                                       float loss_scale, int32_t *d_found_inf, float *d_sumsq,
+                                       double *d_partials, void *stream) {
+    zero_layout lay;
+    if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
+    if (lay.count > 0 && (g32 == nullptr || !aligned(g32, 4))) return ZERO_EINVAL;
+    if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
+    if (d_found_inf == nullptr || !aligned(d_found_inf, 4)) return ZERO_EINVAL;
+    if (d_sumsq != nullptr &&
+        (!aligned(d_sumsq, 4) || d_partials == nullptr || !aligned(d_partials, 8)))
+        return ZERO_EINVAL;
+    int cus = 0;
+    const int rc = device_cus(&cus);
+    if (rc != ZERO_OK) return rc;
+    const hipError_t e =
+        zs::launch_overflow_check_g32(g32, lay.count, loss_scale, d_found_inf, d_sumsq,
+                                      d_partials, cus, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check_g32 launch");
+}
+
+extern "C" int zero_adam_step_g32(void *w16, const float *g32, float *master, float *m, float *v,
+                                  zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank,
+                                  float lr, float beta1, float beta2, float eps,
+                                  float weight_decay, uint64_t step, float loss_scale,
+                                  const int32_t *d_found_inf, void *stream) {
+    uint64_t count = 0;
+    zs::AdamScalars s;
+    const int rc = step_args(w16, g32, 4, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
+                             weight_decay, &count, &s);
+    if (rc != ZERO_OK) return rc;
+    if (step == 0) return ZERO_EINVAL;
+    if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
+    if (d_found_inf != nullptr && !aligned(d_found_inf, 4)) return ZERO_EINVAL;
+    if (count == 0) return ZERO_OK;
+    s.loss_scale = loss_scale;
+    s.bc1 = bias_correction(beta1, step);
+    s.bc2 = bias_correction(beta2, step);
+    const hipError_t e = zs::launch_adam_step_g32(static_cast<int>(dt),
+                                                  static_cast<uint16_t *>(w16), g32, master, m, v,
+                                                  count, s, d_found_inf,
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step_g32 launch");
 }
 
 extern "C" int zero_bias_corrections(float beta1, float beta2, uint64_t t_first, uint32_t len,
@@ -188,7 +246,7 @@ extern "C" int zero_adam_step_dev(void *w16, const void *g16, float *master, flo
                                   void *stream) {
     uint64_t count = 0;
     zs::AdamScalars s;
-    const int rc = step_args(w16, g16, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
+    const int rc = step_args(w16, g16, 2, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
                              weight_decay, &count, &s);
     if (rc != ZERO_OK) return rc;
     if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;

@@ -43,6 +43,20 @@ hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count,
                                  const float *loss_scale_dev, int32_t *flag, float *sumsq,
                                  double *partials, int num_cus, hipStream_t stream);
 
+// The step with FP32 gradients (dtype: the working weights' format).
+hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, float *master,
+                                float *m, float *v, uint64_t count, const AdamScalars &s,
+                                const int32_t *flag, hipStream_t stream);
+
+// acc = float(g16) (first) or acc + float(g16), in FP32; count > 0.
+hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, uint64_t count,
+                                  bool first, hipStream_t stream);
+
+// The check over FP32 gradients (count may be 0: only the outputs are cleared).
+hipError_t launch_overflow_check_g32(const float *g32, uint64_t count, float loss_scale,
+                                     int32_t *flag, float *sumsq, double *partials, int num_cus,
+                                     hipStream_t stream);
+
 // Enqueue the one-lane skip-or-apply decision on a device control block.
 hipError_t launch_scaler_decide(zero_device_ctl *ctl, const float *bias, uint64_t t_first,
                                 uint32_t len, hipStream_t stream);

@@ -1,22 +1,27 @@
 // gfx950 (MI355X) kernels of the ZeRO-sharded mixed-precision Adam step.
 //
-// The step is elementwise over five structure-of-arrays streams (16-bit
-// gradients, FP32 master / m / v, 16-bit working weights): 28 bytes of HBM
-// traffic and ~80 VALU operations per element, far below the FP32 ridge
-// point, so the kernels are built for bandwidth: every lane moves one 16-B
-// FP32 vector per array and one 8-B 16-bit vector per group of 4 elements,
-// a wave's accesses are contiguous 1 KiB (FP32) or 512 B (16-bit) runs, and
-// each lane keeps U groups in flight.  No LDS: nothing is reused.  Every
-// access of the streaming kernels is non-temporal (the data is touched once),
-// and the step launches one block per tile (a grid-stride loop only past 2^23
-// tiles): both measured faster on MI355X than a resident grid looping over
-// tiles.
+// The step is elementwise over five structure-of-arrays streams (gradients,
+// FP32 master / m / v, 16-bit working weights): 28 bytes of HBM traffic per
+// element with 16-bit gradients (30 with FP32 gradients) and ~80 VALU
+// operations, far below the FP32 ridge point, so the kernels are built for
+// bandwidth: every lane moves one 16-B FP32 vector per array and one 8-B
+// 16-bit vector per group of 4 elements, a wave's accesses are contiguous
+// 1 KiB (FP32) or 512 B (16-bit) runs, and each lane keeps U groups in
+// flight.  No LDS: nothing is reused.  Every access of the streaming kernels
+// is non-temporal (the data is touched once), and the step launches one block
+// per tile (a grid-stride loop only past 2^23 tiles): both measured faster on
+// MI355X than a resident grid looping over tiles.
 //
 // Numerics follow the update of "Training models too big for one GPU: ZeRO &
 // FSDP" ("Adam, and why it's expensive", "Mixed-precision training") with
 // one binary32 rounding per operation: contraction is off for this file,
 // FP32 division and square root stay correctly rounded (the HIP default),
 // denormals are kept, and the 16-bit conversions round to nearest even.
+//
+// Gradient element types: uint16_t holds FP16 (DT = 0) or BF16 (DT = 1) bit
+// patterns; float holds FP32 gradients (accumulated across micro-batches,
+// "How far does splitting the batch get you?", gradient accumulation).  DT is
+// always the working weights' format.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,12 +75,40 @@ __device__ __forceinline__ uint32_t not_finite(float x) {
     return (__builtin_bit_cast(uint32_t, x) & 0x7f800000u) == 0x7f800000u;
 }
 
+// ---- gradient access ------------------------------------------------------
+
+template <typename GT, int DT>
+__device__ __forceinline__ float grad_at(const GT *__restrict__ g, uint64_t i) {
+    if constexpr (sizeof(GT) == 2)
+        return widen<DT>(g[i]);
+    else
+        return g[i];
+}
+
+// Four consecutive gradients from an aligned address (8 B for 16-bit, 16 B for FP32).
+template <typename GT, int DT>
+__device__ __forceinline__ void grad4(const GT *__restrict__ g, uint64_t e, float out[4]) {
+    if constexpr (sizeof(GT) == 2) {
+        const u32x2 x = load_nt(reinterpret_cast<const u32x2 *>(g + e));
+        out[0] = widen<DT>(x.x & 0xffffu);
+        out[1] = widen<DT>(x.x >> 16);
+        out[2] = widen<DT>(x.y & 0xffffu);
+        out[3] = widen<DT>(x.y >> 16);
+    } else {
+        const f32x4 x = load_nt(reinterpret_cast<const f32x4 *>(g + e));
+        out[0] = x.x;
+        out[1] = x.y;
+        out[2] = x.z;
+        out[3] = x.w;
+    }
+}
+
 // ---- one element of the step ---------------------------------------------
 
 template <int DT>
-__device__ __forceinline__ void adam_update(uint32_t gbits, float &p, float &m, float &v,
-                                            uint32_t &w, const AdamScalars &s) {
-    const float g = widen<DT>(gbits) / s.loss_scale;
+__device__ __forceinline__ void adam_update(float graw, float &p, float &m, float &v, uint32_t &w,
+                                            const AdamScalars &s) {
+    const float g = graw / s.loss_scale;
     const float pd = p * s.decay;
     const float m_new = s.beta1 * m + s.omb1 * g;
     const float v_new = s.beta2 * v + s.omb2 * (g * g);
@@ -89,15 +122,14 @@ __device__ __forceinline__ void adam_update(uint32_t gbits, float &p, float &m, 
     w = narrow<DT>(p_new);
 }
 
-template <int DT>
-__device__ __forceinline__ void adam_one(uint16_t *__restrict__ w16,
-                                         const uint16_t *__restrict__ g16,
+template <int DT, typename GT>
+__device__ __forceinline__ void adam_one(uint16_t *__restrict__ w16, const GT *__restrict__ g,
                                          float *__restrict__ master, float *__restrict__ m,
                                          float *__restrict__ v, uint64_t i,
                                          const AdamScalars &s) {
     float p = master[i], mm = m[i], vv = v[i];
     uint32_t w;
-    adam_update<DT>(g16[i], p, mm, vv, w, s);
+    adam_update<DT>(grad_at<GT, DT>(g, i), p, mm, vv, w, s);
     master[i] = p;
     m[i] = mm;
     v[i] = vv;
@@ -121,29 +153,29 @@ __device__ __forceinline__ bool take_device_scalars(const zero_device_ctl *__res
 // Elements [0, head) and [head + n_tiles*U*kGroup, count) are done one at a
 // time; in between, tile t covers U groups of kGroup elements and lane l of
 // group u owns elements head + t*U*kGroup + u*kGroup + 4l .. +3.  The host
-// guarantees that master/m/v + head are 16-B aligned and g16/w16 + head are
-// 8-B aligned.
+// guarantees that master/m/v (and FP32 gradients) + head are 16-B aligned
+// and 16-bit arrays + head are 8-B aligned.
 
-template <int DT, int U>
+template <int DT, typename GT, int U>
 __global__ __launch_bounds__(kThreads) void adam_step_vec(
-    uint16_t *__restrict__ w16, const uint16_t *__restrict__ g16, float *__restrict__ master,
+    uint16_t *__restrict__ w16, const GT *__restrict__ g, float *__restrict__ master,
     float *__restrict__ m, float *__restrict__ v, uint64_t count, uint32_t head,
     uint64_t n_tiles, AdamScalars s, const int32_t *__restrict__ flag,
     const zero_device_ctl *__restrict__ ctl) {
     if (flag != nullptr && *flag != 0) return;
     if (!take_device_scalars(ctl, s)) return;
     const uint32_t tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid < head) adam_one<DT>(w16, g16, master, m, v, tid, s);
+    if (blockIdx.x == 0 && tid < head) adam_one<DT>(w16, g, master, m, v, tid, s);
 
     constexpr uint64_t kTile = static_cast<uint64_t>(U) * kGroup;
     for (uint64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
         const uint64_t base = head + t * kTile + static_cast<uint64_t>(tid) * kVec;
         f32x4 P[U], M[U], V[U];
-        u32x2 G[U];
+        float G[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint64_t e = base + static_cast<uint64_t>(u) * kGroup;
-            G[u] = load_nt(reinterpret_cast<const u32x2 *>(g16 + e));
+            grad4<GT, DT>(g, e, G[u]);
             P[u] = load_nt(reinterpret_cast<const f32x4 *>(master + e));
             M[u] = load_nt(reinterpret_cast<const f32x4 *>(m + e));
             V[u] = load_nt(reinterpret_cast<const f32x4 *>(v + e));
@@ -154,11 +186,9 @@ __global__ __launch_bounds__(kThreads) void adam_step_vec(
             float p[4] = {P[u].x, P[u].y, P[u].z, P[u].w};
             float mm[4] = {M[u].x, M[u].y, M[u].z, M[u].w};
             float vv[4] = {V[u].x, V[u].y, V[u].z, V[u].w};
-            const uint32_t gh[4] = {G[u].x & 0xffffu, G[u].x >> 16, G[u].y & 0xffffu,
-                                    G[u].y >> 16};
             uint32_t w[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) adam_update<DT>(gh[j], p[j], mm[j], vv[j], w[j], s);
+            for (int j = 0; j < 4; ++j) adam_update<DT>(G[u][j], p[j], mm[j], vv[j], w[j], s);
             store_nt(reinterpret_cast<f32x4 *>(master + e), f32x4{p[0], p[1], p[2], p[3]});
             store_nt(reinterpret_cast<f32x4 *>(m + e), f32x4{mm[0], mm[1], mm[2], mm[3]});
             store_nt(reinterpret_cast<f32x4 *>(v + e), f32x4{vv[0], vv[1], vv[2], vv[3]});
@@ -170,14 +200,14 @@ __global__ __launch_bounds__(kThreads) void adam_step_vec(
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     for (uint64_t i = head + n_tiles * kTile + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
          i < count; i += stride)
-        adam_one<DT>(w16, g16, master, m, v, i, s);
+        adam_one<DT>(w16, g, master, m, v, i, s);
 }
 
 // ---- the step: element-wise path for views of different alignment phase --
 
-template <int DT>
+template <int DT, typename GT>
 __global__ __launch_bounds__(kThreads) void adam_step_elem(
-    uint16_t *__restrict__ w16, const uint16_t *__restrict__ g16, float *__restrict__ master,
+    uint16_t *__restrict__ w16, const GT *__restrict__ g, float *__restrict__ master,
     float *__restrict__ m, float *__restrict__ v, uint64_t count, AdamScalars s,
     const int32_t *__restrict__ flag, const zero_device_ctl *__restrict__ ctl) {
     if (flag != nullptr && *flag != 0) return;
@@ -185,7 +215,63 @@ __global__ __launch_bounds__(kThreads) void adam_step_elem(
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < count;
          i += stride)
-        adam_one<DT>(w16, g16, master, m, v, i, s);
+        adam_one<DT>(w16, g, master, m, v, i, s);
+}
+
+// ---- FP32 accumulation of 16-bit micro-batch gradients ----------------------
+//
+// acc = float(g16) on the first micro-batch, acc + float(g16) after it: one
+// FP32 addition per element per micro-batch (10 B of traffic; 6 B for the
+// first).  Same head / tile / tail split and alignment rule as the step.
+
+template <int DT, bool FIRST>
+__device__ __forceinline__ void accumulate_one(float *__restrict__ acc,
+                                               const uint16_t *__restrict__ g16, uint64_t i) {
+    const float g = widen<DT>(g16[i]);
+    acc[i] = FIRST ? g : acc[i] + g;
+}
+
+template <int DT, bool FIRST, int U>
+__global__ __launch_bounds__(kThreads) void accumulate_vec(float *__restrict__ acc,
+                                                           const uint16_t *__restrict__ g16,
+                                                           uint64_t count, uint32_t head,
+                                                           uint64_t n_tiles) {
+    const uint32_t tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid < head) accumulate_one<DT, FIRST>(acc, g16, tid);
+    constexpr uint64_t kTile = static_cast<uint64_t>(U) * kGroup;
+    for (uint64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        const uint64_t base = head + t * kTile + static_cast<uint64_t>(tid) * kVec;
+        float G[U][4];
+        f32x4 A[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t e = base + static_cast<uint64_t>(u) * kGroup;
+            grad4<uint16_t, DT>(g16, e, G[u]);
+            if (!FIRST) A[u] = load_nt(reinterpret_cast<const f32x4 *>(acc + e));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t e = base + static_cast<uint64_t>(u) * kGroup;
+            const f32x4 r = FIRST ? f32x4{G[u][0], G[u][1], G[u][2], G[u][3]}
+                                  : f32x4{A[u].x + G[u][0], A[u].y + G[u][1], A[u].z + G[u][2],
+                                          A[u].w + G[u][3]};
+            store_nt(reinterpret_cast<f32x4 *>(acc + e), r);
+        }
+    }
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+    for (uint64_t i = head + n_tiles * kTile + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
+         i < count; i += stride)
+        accumulate_one<DT, FIRST>(acc, g16, i);
+}
+
+template <int DT, bool FIRST>
+__global__ __launch_bounds__(kThreads) void accumulate_elem(float *__restrict__ acc,
+                                                            const uint16_t *__restrict__ g16,
+                                                            uint64_t count) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < count;
+         i += stride)
+        accumulate_one<DT, FIRST>(acc, g16, i);
 }
 
 // ---- unscale + overflow check ----------------------------------------------
@@ -197,26 +283,57 @@ __global__ void check_init(int32_t *__restrict__ flag, float *__restrict__ sumsq
     }
 }
 
+// Elements per 16-B vector and the field of the magnitude bits at or above
+// which a value is inf or NaN.
+template <typename GT, int DT> struct GradBits;
+template <> struct GradBits<uint16_t, 0> {
+    static constexpr uint32_t kPerVec = 8, kExpField = 0x7c00u;
+};
+template <> struct GradBits<uint16_t, 1> {
+    static constexpr uint32_t kPerVec = 8, kExpField = 0x7f80u;
+};
+template <int DT> struct GradBits<float, DT> {
+    static constexpr uint32_t kPerVec = 4, kExpField = 0x7f800000u;
+};
+
 // Flag only.  Division by S > 0 correctly rounded is monotone in |g|, so
-// some float(g)/S is not finite iff some g is inf/NaN or the largest finite
-// |g| divided by S overflows.  For 16-bit patterns with the sign cleared the
-// integer order is the magnitude order, so each lane keeps the max of
-// (bits & 0x7fff) with packed 16-bit integer maxima and divides once at the
-// end: the pass is two integer operations per gradient and runs at read
-// bandwidth.  Elements [0, head) and [head + 8*n_vec, count) one at a time;
-// in between, 16-B vectors of 8 gradients, grid-stride, U in flight per lane.
-template <int DT, int U>
+// some g/S is not finite iff some g is inf/NaN or the largest finite |g|
+// divided by S overflows.  With the sign bit cleared, floating-point bit
+// patterns order like their magnitudes, so each lane keeps the maximum of
+// the magnitude bits (packed 16-bit maxima for 16-bit gradients) and divides
+// once at the end: the pass is two integer operations per gradient and runs
+// at read bandwidth.  Elements [0, head) and [head + kPerVec*n_vec, count)
+// one at a time; in between, 16-B vectors, grid-stride, U in flight per lane.
+template <typename GT, int DT, int U>
 __global__ __launch_bounds__(kThreads) void overflow_flag_kernel(
-    const uint16_t *__restrict__ g16, uint64_t count, uint32_t head, uint64_t n_vec,
-    float loss_scale, const float *__restrict__ loss_scale_dev, int32_t *__restrict__ flag) {
-    constexpr uint32_t kExpField = DT == 0 ? 0x7c00u : 0x7f80u;  // inf/NaN at or above
+    const GT *__restrict__ g, uint64_t count, uint32_t head, uint64_t n_vec, float loss_scale,
+    const float *__restrict__ loss_scale_dev, int32_t *__restrict__ flag) {
+    using B = GradBits<GT, DT>;
+    constexpr bool k16 = sizeof(GT) == 2;
     if (loss_scale_dev != nullptr) loss_scale = *loss_scale_dev;
     const uint32_t tid = threadIdx.x;
     u16x2 mx2 = {0, 0};
     uint32_t mx = 0;
-    if (blockIdx.x == 0 && tid < head) mx = g16[tid] & 0x7fffu;
+    auto mag = [](GT x) -> uint32_t {
+        if constexpr (k16)
+            return x & 0x7fffu;
+        else
+            return __builtin_bit_cast(uint32_t, x) & 0x7fffffffu;
+    };
+    if (blockIdx.x == 0 && tid < head) mx = mag(g[tid]);
 
-    const u32x4 *vec = reinterpret_cast<const u32x4 *>(g16 + head);
+    auto fold = [&](const u32x4 &x) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (k16) {
+                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, x[j] & 0x7fff7fffu));
+            } else {
+                const uint32_t a = x[j] & 0x7fffffffu;
+                mx = a > mx ? a : mx;
+            }
+        }
+    };
+    const u32x4 *vec = reinterpret_cast<const u32x4 *>(g + head);
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     uint64_t k = static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
     for (; k + (U - 1) * stride < n_vec; k += U * stride) {
@@ -224,26 +341,24 @@ __global__ __launch_bounds__(kThreads) void overflow_flag_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) x[u] = load_nt(vec + k + u * stride);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, x[u][j] & 0x7fff7fffu));
-        }
+        for (int u = 0; u < U; ++u) fold(x[u]);
     }
-    for (; k < n_vec; k += stride) {
-        const u32x4 x = load_nt(vec + k);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, x[j] & 0x7fff7fffu));
-    }
-    for (uint64_t i = head + n_vec * 8 + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
+    for (; k < n_vec; k += stride) fold(load_nt(vec + k));
+    for (uint64_t i = head + n_vec * B::kPerVec + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
          i < count; i += stride) {
-        const uint32_t a = g16[i] & 0x7fffu;
+        const uint32_t a = mag(g[i]);
         mx = a > mx ? a : mx;
     }
-    mx = mx > mx2.x ? mx : mx2.x;
-    mx = mx > mx2.y ? mx : mx2.y;
-    const uint32_t bad = mx >= kExpField || not_finite(widen<DT>(mx) / loss_scale) ||
+    if constexpr (k16) {
+        mx = mx > mx2.x ? mx : mx2.x;
+        mx = mx > mx2.y ? mx : mx2.y;
+    }
+    float largest;
+    if constexpr (k16)
+        largest = widen<DT>(mx);
+    else
+        largest = __builtin_bit_cast(float, mx);
+    const uint32_t bad = mx >= B::kExpField || not_finite(largest / loss_scale) ||
                          !(loss_scale > 0.0f) || not_finite(loss_scale);
     if (__any(bad)) {
         if ((tid & 63u) == 0) *flag = 1;
@@ -254,24 +369,39 @@ __global__ __launch_bounds__(kThreads) void overflow_flag_kernel(
 // its definition says; lanes accumulate in FP64, waves reduce by shuffles,
 // and block b writes its partial sum to partials[b].  Same element split as
 // the flag kernel.
-template <int DT, int U>
+template <typename GT, int DT, int U>
 __global__ __launch_bounds__(kThreads) void overflow_sumsq_kernel(
-    const uint16_t *__restrict__ g16, uint64_t count, uint32_t head, uint64_t n_vec,
-    float loss_scale, const float *__restrict__ loss_scale_dev, int32_t *__restrict__ flag,
+    const GT *__restrict__ g, uint64_t count, uint32_t head, uint64_t n_vec, float loss_scale,
+    const float *__restrict__ loss_scale_dev, int32_t *__restrict__ flag,
     double *__restrict__ partials) {
+    using B = GradBits<GT, DT>;
     if (loss_scale_dev != nullptr) loss_scale = *loss_scale_dev;
     const uint32_t tid = threadIdx.x;
     uint32_t bad = !(loss_scale > 0.0f) || not_finite(loss_scale);
     double acc = 0.0;
-    auto visit = [&](uint32_t h) {
-        const float q = widen<DT>(h) / loss_scale;
+    auto visit = [&](float graw) {
+        const float q = graw / loss_scale;
         bad |= not_finite(q);
         acc += static_cast<double>(q) * static_cast<double>(q);
     };
+    auto visit_vec = [&](const u32x4 &x) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (sizeof(GT) == 2) {
+                visit(widen<DT>(x[j] & 0xffffu));
+                visit(widen<DT>(x[j] >> 16));
+            } else {
+                // copy the lane out first: bit-casting the vector element in
+                // place made the compiler reuse one element for all four
+                const uint32_t bits = x[j];
+                visit(__builtin_bit_cast(float, bits));
+            }
+        }
+    };
 
-    if (blockIdx.x == 0 && tid < head) visit(g16[tid]);
+    if (blockIdx.x == 0 && tid < head) visit(grad_at<GT, DT>(g, tid));
 
-    const u32x4 *vec = reinterpret_cast<const u32x4 *>(g16 + head);
+    const u32x4 *vec = reinterpret_cast<const u32x4 *>(g + head);
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     uint64_t k = static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
     for (; k + (U - 1) * stride < n_vec; k += U * stride) {
@@ -279,25 +409,12 @@ __global__ __launch_bounds__(kThreads) void overflow_sumsq_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) x[u] = load_nt(vec + k + u * stride);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                visit(x[u][j] & 0xffffu);
-                visit(x[u][j] >> 16);
-            }
-        }
+        for (int u = 0; u < U; ++u) visit_vec(x[u]);
     }
-    for (; k < n_vec; k += stride) {
-        const u32x4 x = load_nt(vec + k);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            visit(x[j] & 0xffffu);
-            visit(x[j] >> 16);
-        }
-    }
-    for (uint64_t i = head + n_vec * 8 + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
+    for (; k < n_vec; k += stride) visit_vec(load_nt(vec + k));
+    for (uint64_t i = head + n_vec * B::kPerVec + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
          i < count; i += stride)
-        visit(g16[i]);
+        visit(grad_at<GT, DT>(g, i));
 
     if (__any(bad)) {
         if ((tid & 63u) == 0) *flag = 1;
@@ -380,60 +497,91 @@ __global__ void scaler_decide(zero_device_ctl *__restrict__ ctl, const float *__
 // ---- launch helpers --------------------------------------------------------
 
 constexpr int kAdamU = 2;              // groups in flight per lane in the step
+constexpr int kAccU = 2;               // groups in flight per lane in the accumulate
 constexpr int kCheckU = 4;             // 16-B vectors in flight per lane in the check
 constexpr int kCheckBlocksPerCU = 128; // flag-only check grid cap per CU (measured)
 
-inline uint32_t align_head(uintptr_t addr, uint32_t elem_bytes, uint32_t align) {
-    // elements to skip until addr is `align`-aligned (addr is elem-aligned)
-    const uintptr_t mis = addr % align;
+inline uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
+
+inline uint32_t align_head(uintptr_t a, uint32_t elem_bytes, uint32_t align) {
+    // elements to skip until a is `align`-aligned (a is elem-aligned)
+    const uintptr_t mis = a % align;
     return mis == 0 ? 0u : static_cast<uint32_t>((align - mis) / elem_bytes);
 }
 
-template <int DT>
-hipError_t adam_dispatch(uint16_t *w16, const uint16_t *g16, float *master, float *m, float *v,
+// Head that aligns the FP32 reference array to 16 B, and whether it also
+// aligns every other view: FP32 arrays (a, b, FP32 gradients) to 16 B and
+// 16-bit arrays (16-bit gradients, h16) to 8 B.  b and h16 may be null.
+template <typename GT>
+bool common_phase(const float *ref, const float *a, const float *b, const GT *g,
+                  const uint16_t *h16, uint32_t *head) {
+    *head = align_head(addr(ref), 4, 16);
+    const bool g_ok = sizeof(GT) == 2 ? (addr(g) + 2u * *head) % 8 == 0
+                                      : addr(g) % 16 == addr(ref) % 16;
+    return addr(a) % 16 == addr(ref) % 16 && (b == nullptr || addr(b) % 16 == addr(ref) % 16) &&
+           g_ok && (h16 == nullptr || (addr(h16) + 2u * *head) % 8 == 0);
+}
+
+inline uint32_t grid_for(uint64_t need) {
+    if (need == 0) need = 1;
+    return static_cast<uint32_t>(need < kMaxBlocks ? need : kMaxBlocks);
+}
+
+template <int DT, typename GT>
+hipError_t adam_dispatch(uint16_t *w16, const GT *g, float *master, float *m, float *v,
                          uint64_t count, const AdamScalars &s, const int32_t *flag,
                          const zero_device_ctl *ctl, hipStream_t stream) {
-    const uint64_t max_blocks = kMaxBlocks;
-    uint32_t head = align_head(reinterpret_cast<uintptr_t>(master), 4, 16);
-    const bool same_phase =
-        reinterpret_cast<uintptr_t>(m) % 16 == reinterpret_cast<uintptr_t>(master) % 16 &&
-        reinterpret_cast<uintptr_t>(v) % 16 == reinterpret_cast<uintptr_t>(master) % 16 &&
-        (reinterpret_cast<uintptr_t>(g16) + 2u * head) % 8 == 0 &&
-        (reinterpret_cast<uintptr_t>(w16) + 2u * head) % 8 == 0;
-    if (!same_phase) {
-        const uint64_t need = (count + kThreads - 1) / kThreads;
-        const uint32_t blocks = static_cast<uint32_t>(need < max_blocks ? need : max_blocks);
-        adam_step_elem<DT><<<blocks, kThreads, 0, stream>>>(w16, g16, master, m, v, count, s,
-                                                             flag, ctl);
+    uint32_t head = 0;
+    if (!common_phase<GT>(master, m, v, g, w16, &head)) {
+        adam_step_elem<DT, GT><<<grid_for((count + kThreads - 1) / kThreads), kThreads, 0,
+                                 stream>>>(w16, g, master, m, v, count, s, flag, ctl);
         return hipGetLastError();
     }
     if (head > count) head = static_cast<uint32_t>(count);
     constexpr uint64_t kTile = static_cast<uint64_t>(kAdamU) * kGroup;
     const uint64_t n_tiles = (count - head) / kTile;
     const uint64_t rest = count - head - n_tiles * kTile;
-    uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
-    if (need == 0) need = 1;
-    const uint32_t blocks = static_cast<uint32_t>(need < max_blocks ? need : max_blocks);
-    adam_step_vec<DT, kAdamU><<<blocks, kThreads, 0, stream>>>(w16, g16, master, m, v, count,
-                                                               head, n_tiles, s, flag, ctl);
+    const uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
+    adam_step_vec<DT, GT, kAdamU><<<grid_for(need), kThreads, 0, stream>>>(
+        w16, g, master, m, v, count, head, n_tiles, s, flag, ctl);
+    return hipGetLastError();
+}
+
+template <int DT, bool FIRST>
+hipError_t accumulate_dispatch(float *acc, const uint16_t *g16, uint64_t count,
+                               hipStream_t stream) {
+    uint32_t head = 0;
+    if (!common_phase<uint16_t>(acc, acc, nullptr, g16, nullptr, &head)) {
+        accumulate_elem<DT, FIRST><<<grid_for((count + kThreads - 1) / kThreads), kThreads, 0,
+                                     stream>>>(acc, g16, count);
+        return hipGetLastError();
+    }
+    if (head > count) head = static_cast<uint32_t>(count);
+    constexpr uint64_t kTile = static_cast<uint64_t>(kAccU) * kGroup;
+    const uint64_t n_tiles = (count - head) / kTile;
+    const uint64_t rest = count - head - n_tiles * kTile;
+    const uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
+    accumulate_vec<DT, FIRST, kAccU><<<grid_for(need), kThreads, 0, stream>>>(acc, g16, count,
+                                                                             head, n_tiles);
     return hipGetLastError();
 }
 
 struct CheckGrid {
     uint32_t head;    // elements done one at a time before the first 16-B vector
-    uint64_t n_vec;   // 16-B vectors of 8 gradients
+    uint64_t n_vec;   // 16-B vectors
     uint32_t blocks;  // grid size (with a sum of squares: the number of partials)
 };
 
 // With a sum of squares the grid depends on the size and the pointer's phase
 // only, never on the device, so the partial sums and their order are the
 // same everywhere.  The flag-only grid is sized per CU.
-inline CheckGrid check_grid(const uint16_t *g16, uint64_t count, bool sumsq, int num_cus) {
+template <typename GT, int DT>
+CheckGrid check_grid(const GT *g, uint64_t count, bool sumsq, int num_cus) {
     CheckGrid c;
-    c.head = align_head(reinterpret_cast<uintptr_t>(g16), 2, 16);
+    c.head = align_head(addr(g), sizeof(GT), 16);
     if (c.head > count) c.head = static_cast<uint32_t>(count);
-    c.n_vec = (count - c.head) / 8;
-    const uint64_t rest = count - c.head - 8 * c.n_vec;
+    c.n_vec = (count - c.head) / GradBits<GT, DT>::kPerVec;
+    const uint64_t rest = count - c.head - GradBits<GT, DT>::kPerVec * c.n_vec;
     const uint64_t per_block = static_cast<uint64_t>(kThreads) * kCheckU;
     uint64_t need = c.n_vec > 0 ? (c.n_vec + per_block - 1) / per_block
                                 : (rest + kThreads - 1) / kThreads;
@@ -444,19 +592,19 @@ inline CheckGrid check_grid(const uint16_t *g16, uint64_t count, bool sumsq, int
     return c;
 }
 
-template <int DT>
-hipError_t check_dispatch(const uint16_t *g16, uint64_t count, float loss_scale,
+template <typename GT, int DT>
+hipError_t check_dispatch(const GT *g, uint64_t count, float loss_scale,
                           const float *loss_scale_dev, int32_t *flag, float *sumsq,
                           double *partials, int num_cus, hipStream_t stream) {
-    const CheckGrid c = check_grid(g16, count, sumsq != nullptr, num_cus);
+    const CheckGrid c = check_grid<GT, DT>(g, count, sumsq != nullptr, num_cus);
     if (sumsq == nullptr) {
-        overflow_flag_kernel<DT, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
-            g16, count, c.head, c.n_vec, loss_scale, loss_scale_dev, flag);
+        overflow_flag_kernel<GT, DT, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
+            g, count, c.head, c.n_vec, loss_scale, loss_scale_dev, flag);
         return hipGetLastError();
     }
-    overflow_sumsq_kernel<DT, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
-        g16, count, c.head, c.n_vec, loss_scale, loss_scale_dev, flag, partials);
-    hipError_t err = hipGetLastError();
+    overflow_sumsq_kernel<GT, DT, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
+        g, count, c.head, c.n_vec, loss_scale, loss_scale_dev, flag, partials);
+    const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     sumsq_finalize<<<1, kThreads, 0, stream>>>(partials, c.blocks, sumsq);
     return hipGetLastError();
@@ -471,6 +619,23 @@ hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float
     return adam_dispatch<1>(w16, g16, master, m, v, count, s, flag, ctl, stream);
 }
 
+hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, float *master,
+                                float *m, float *v, uint64_t count, const AdamScalars &s,
+                                const int32_t *flag, hipStream_t stream) {
+    if (dtype == 0)
+        return adam_dispatch<0>(w16, g32, master, m, v, count, s, flag, nullptr, stream);
+    return adam_dispatch<1>(w16, g32, master, m, v, count, s, flag, nullptr, stream);
+}
+
+hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, uint64_t count,
+                                  bool first, hipStream_t stream) {
+    if (dtype == 0)
+        return first ? accumulate_dispatch<0, true>(acc, g16, count, stream)
+                     : accumulate_dispatch<0, false>(acc, g16, count, stream);
+    return first ? accumulate_dispatch<1, true>(acc, g16, count, stream)
+                 : accumulate_dispatch<1, false>(acc, g16, count, stream);
+}
+
 hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
                                  const float *loss_scale_dev, int32_t *flag, float *sumsq,
                                  double *partials, int num_cus, hipStream_t stream) {
@@ -478,10 +643,20 @@ hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count,
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess || count == 0) return err;
     if (dtype == 0)
-        return check_dispatch<0>(g16, count, loss_scale, loss_scale_dev, flag, sumsq, partials,
-                                 num_cus, stream);
-    return check_dispatch<1>(g16, count, loss_scale, loss_scale_dev, flag, sumsq, partials,
-                             num_cus, stream);
+        return check_dispatch<uint16_t, 0>(g16, count, loss_scale, loss_scale_dev, flag, sumsq,
+                                           partials, num_cus, stream);
+    return check_dispatch<uint16_t, 1>(g16, count, loss_scale, loss_scale_dev, flag, sumsq,
+                                       partials, num_cus, stream);
+}
+
+hipError_t launch_overflow_check_g32(const float *g32, uint64_t count, float loss_scale,
+                                     int32_t *flag, float *sumsq, double *partials, int num_cus,
+                                     hipStream_t stream) {
+    check_init<<<1, 64, 0, stream>>>(flag, sumsq);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess || count == 0) return err;
+    return check_dispatch<float, 0>(g32, count, loss_scale, nullptr, flag, sumsq, partials,
+                                    num_cus, stream);
 }
 
 hipError_t launch_scaler_decide(zero_device_ctl *ctl, const float *bias, uint64_t t_first,
