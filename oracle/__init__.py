@@ -101,6 +101,10 @@ def _load():
         lib.oracle_overflow_check_g32.argtypes = [vp, u64, f32, vp, vp]
         lib.oracle_adam_step_g32.argtypes = [vp, vp, vp, vp, vp, i32, u64, f32, f32, f32, f32,
                                              f32, u64, f32]
+        lib.oracle_reduce_shard.argtypes = [vp, i32, vp, i32, u64, u32, u32]
+        lib.oracle_gather_shards.argtypes = [vp, vp, i32, u64, u32]
+        lib.oracle_reduce_shard.restype = None
+        lib.oracle_gather_shards.restype = None
         for name in ("oracle_decode16_array", "oracle_encode16_array", "oracle_overflow_check",
                      "oracle_step_scalars", "oracle_adam_step", "oracle_adam_step_f64",
                      "oracle_grad_accumulate", "oracle_overflow_check_g32",
@@ -234,6 +238,82 @@ def adam_step_g32(w16, g32, master, m, v, dtype, *, lr, beta1, beta2, eps, weigh
                                  _ptr(master, np.float32), _ptr(m, np.float32),
                                  _ptr(v, np.float32), DTYPES[dtype], count, lr, beta1, beta2, eps,
                                  weight_decay, step, loss_scale)
+
+
+FORMATS = {"f16": 0, "bf16": 1, "f32": 2}
+
+
+def _ptr_array(arrays):
+    arr = (ctypes.c_void_p * len(arrays))()
+    for i, a in enumerate(arrays):
+        if not a.flags.c_contiguous:
+            raise ValueError("arrays must be C-contiguous")
+        arr[i] = a.ctypes.data
+    return arr
+
+
+def reduce_shard(replicas, in_fmt: str, out_fmt: str, psi: int, n: int, rank: int) -> np.ndarray:
+    """Rank `rank`'s chunk of the element-wise FP32 sum of n full replica buffers."""
+    if len(replicas) != n:
+        raise ValueError("one replica per rank")
+    in_dt = np.float32 if in_fmt == "f32" else np.uint16
+    for r in replicas:
+        if r.dtype != in_dt or r.size < psi:
+            raise ValueError("replica dtype or size")
+    lay = layout(psi, n, rank)
+    out = np.empty(lay.count, np.float32 if out_fmt == "f32" else np.uint16)
+    _load().oracle_reduce_shard(out.ctypes.data, FORMATS[out_fmt], _ptr_array(replicas),
+                                FORMATS[in_fmt], psi, n, rank)
+    return out
+
+
+def gather_shards(shards, psi: int, n: int, full: np.ndarray) -> np.ndarray:
+    """Copy shard k (count_k elements) to full[k*S : k*S + count_k] for every rank k."""
+    if len(shards) != n:
+        raise ValueError("one shard per rank")
+    for k, sh in enumerate(shards):
+        if sh.dtype != full.dtype or sh.size < layout(psi, n, k).count:
+            raise ValueError("shard dtype or size")
+    _load().oracle_gather_shards(full.ctypes.data, _ptr_array(shards), full.itemsize, psi, n)
+    return full
+
+
+# ---------------------------------------------------------------------------
+# Accounting the pages do in closed form (bytes and elements, integers).
+# ---------------------------------------------------------------------------
+
+def comm_volume(psi: int, n: int, stage: int, elem_bytes: int) -> dict:
+    """Communication of one data-parallel step, per rank.
+
+    elements: the pages' element count per rank per step -- 2 psi for plain
+    data parallelism and ZeRO stages 1 and 2 (a reduce-scatter of psi and an
+    all-gather of psi), 3 psi for stage 3 (a second all-gather) ("How far does
+    splitting the batch get you?", "What does each stage cost on the wire?";
+    "Stop Replicating What You Can Shard", FSDP communication equation).
+    ring_bytes: what a ring actually sends per rank: each collective over an
+    M-byte message sends (d-1)/d of it ("Why does the all-reduce not get more
+    expensive with more ranks?"), with the message padded to n equal chunks.
+    ring_hops: sequential hops of those collectives, 2(d-1) per all-reduce.
+    """
+    if stage not in (0, 1, 2, 3):
+        raise ValueError("stage must be 0..3")
+    lay = layout(psi, n, 0)
+    collectives = 3 if stage == 3 else 2
+    return {
+        "collectives": collectives,
+        "elements": collectives * psi,
+        "wire_bytes": collectives * psi * elem_bytes,
+        "ring_bytes": collectives * (n - 1) * lay.shard * elem_bytes,
+        "ring_hops": collectives * (n - 1),
+    }
+
+
+def peak_memory(psi: int, n: int, unit_params: int, units_resident: int,
+                activation_bytes: int) -> int:
+    """ZeRO-3 peak per rank: the persistent 16 psi / N shard, plus the 16-bit
+    weights of the units gathered at once, plus activations ("ZeRO Stage 3
+    Math", "Peak transient memory")."""
+    return layout(psi, n, 0).bytes_z3 + units_resident * unit_params * 2 + activation_bytes
 
 
 @dataclass

@@ -327,3 +327,55 @@ void oracle_adam_step_f64(double *master, double *m, double *v, const uint16_t *
         v[i] = v_new;
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* The exchanges around the step, computed on one host.                     */
+/*                                                                           */
+/* Reduce-scatter: after it, rank i holds the SUM over all ranks of chunk i */
+/* ("Training models too big for one GPU", "Data parallelism and the        */
+/* all-reduce").  Here the n replicas are n full flat buffers and the sum   */
+/* of each element is taken in FP32 over ranks 0..n-1 in order, then        */
+/* written as FP32 or rounded once to the 16-bit output format.             */
+/* All-gather: every rank's finished chunk is copied to its place in the    */
+/* full buffer.  Format codes: 0 FP16, 1 BF16, 2 FP32.                       */
+/* ------------------------------------------------------------------------ */
+
+static float load_any(const void *p, int fmt, uint64_t i)
+{
+    if (fmt == 2)
+        return ((const float *)p)[i];
+    return (float)oracle_decode16(((const uint16_t *)p)[i], fmt);
+}
+
+void oracle_reduce_shard(void *out, int out_fmt, const void *const *replicas, int in_fmt,
+                         uint64_t psi, uint32_t n, uint32_t rank)
+{
+    oracle_layout_t lay;
+    if (oracle_layout(psi, n, rank, &lay) != 0)
+        return;
+    for (uint64_t i = 0; i < lay.count; ++i) {
+        float s = 0.0f;
+        for (uint32_t k = 0; k < n; ++k)
+            s = s + load_any(replicas[k], in_fmt, lay.offset + i);
+        if (out_fmt == 2)
+            ((float *)out)[i] = s;
+        else
+            ((uint16_t *)out)[i] = oracle_encode16((double)s, out_fmt);
+    }
+}
+
+void oracle_gather_shards(void *full, const void *const *shards, int elem_bytes, uint64_t psi,
+                          uint32_t n)
+{
+    for (uint32_t k = 0; k < n; ++k) {
+        oracle_layout_t lay;
+        if (oracle_layout(psi, n, k, &lay) != 0)
+            return;
+        for (uint64_t i = 0; i < lay.count; ++i) {
+            if (elem_bytes == 4)
+                ((float *)full)[lay.offset + i] = ((const float *)shards[k])[i];
+            else
+                ((uint16_t *)full)[lay.offset + i] = ((const uint16_t *)shards[k])[i];
+        }
+    }
+}
