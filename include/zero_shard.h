@@ -44,8 +44,9 @@
 extern "C" {
 #endif
 
-/* Format of the 16-bit gradients and working weights (one for both). */
-typedef enum { ZERO_F16 = 0, ZERO_BF16 = 1 } zero_dtype;
+/* Format of the 16-bit gradients and working weights (one for both).
+ * ZERO_F32 is accepted only by the functions that say so. */
+typedef enum { ZERO_F16 = 0, ZERO_BF16 = 1, ZERO_F32 = 2 } zero_dtype;
 
 #define ZERO_OK 0
 #define ZERO_EINVAL (-1) /* an argument is out of its documented domain */
@@ -222,6 +223,76 @@ int zero_adam_step_g32(void *w16, const float *g32, float *master, float *m, flo
                        zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank, float lr,
                        float beta1, float beta2, float eps, float weight_decay, uint64_t step,
                        float loss_scale, const int32_t *d_found_inf, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The exchanges on either side of the step, on one GPU.  A reduce-scatter
+ * leaves rank i with the SUM over ranks of chunk i of the gradients; an
+ * all-gather copies every rank's finished chunk to all ("Training models too
+ * big for one GPU", "Data parallelism and the all-reduce").  These stand-ins
+ * take the n replicas or shards as views on one device, so the sharded path
+ * can be exercised end to end without a second GPU.
+ * ------------------------------------------------------------------------- */
+
+#define ZERO_MAX_LOCAL_RANKS 64 /* most replicas / shards one call takes */
+
+/*
+ * zero_reduce_shard -- rank `rank`'s chunk of the element-wise sum of n
+ * replica buffers: out[i] = sum over k = 0..n-1 of replica_k[offset + i],
+ * i < count, accumulated in FP32 in rank order and rounded once to out_dt.
+ *   replicas  HOST array of n device pointers; replica k is a full flat buffer
+ *             of at least psi elements of format in_dt (FP16, BF16 or FP32).
+ *   out       device, shard view of count elements of format out_dt.
+ *   Reads n x (2 or 4) bytes and writes 2 or 4 bytes per element.
+ *   Errors: ZERO_EDTYPE for a format outside FP16/BF16/FP32; ZERO_EINVAL for
+ *   bad layout arguments, n > ZERO_MAX_LOCAL_RANKS, a NULL or misaligned
+ *   pointer with count > 0; ZERO_EHIP.  count == 0: no-op.
+ */
+int zero_reduce_shard(void *out, zero_dtype out_dt, const void *const *replicas,
+                      zero_dtype in_dt, uint64_t psi, uint32_t n, uint32_t rank, void *stream);
+
+/*
+ * zero_gather_shards -- full[k*S + i] = shard_k[i] for every rank k < n and
+ * i < count(k): the flat buffer from its n shards.  Elements of full at
+ * psi and beyond (the padding) are not written.
+ *   full    device, flat buffer of at least psi elements of format dt.
+ *   shards  HOST array of n device pointers (NULL allowed for empty ranks).
+ *   Errors: ZERO_EDTYPE; ZERO_EINVAL for bad layout arguments,
+ *   n > ZERO_MAX_LOCAL_RANKS, a NULL or misaligned pointer; ZERO_EHIP.
+ */
+int zero_gather_shards(void *full, const void *const *shards, zero_dtype dt, uint64_t psi,
+                       uint32_t n, void *stream);
+
+/* Communication of one step per rank (see zero_comm_volume). */
+typedef struct {
+    uint32_t collectives; /* 2 (reduce-scatter + all-gather) or 3 at stage 3 */
+    uint32_t ring_hops;   /* sequential hops of those collectives on a ring: collectives*(n-1) */
+    uint64_t elements;    /* collectives * psi: 2 psi at stages 0-2, 3 psi at stage 3 */
+    uint64_t wire_bytes;  /* elements * elem_bytes */
+    uint64_t ring_bytes;  /* bytes a rank sends on a ring: collectives * (n-1) * S * elem_bytes */
+} zero_comm;
+
+/*
+ * zero_comm_volume -- what one data-parallel step moves per rank at ZeRO
+ * stage 0 (plain data parallelism) to 3: 2 psi elements at stages 0-2, 3 psi
+ * at stage 3 ("How far does splitting the batch get you?", "What does each
+ * stage cost on the wire?"; "Stop Replicating What You Can Shard", FSDP
+ * communication), and what a ring sends for it: (d-1)/d of each message in
+ * d-1 hops ("Why does the all-reduce not get more expensive with more
+ * ranks?").  Host only.  Errors: ZERO_EINVAL for bad layout arguments,
+ * stage > 3, elem_bytes outside 1..8 or a NULL out.
+ */
+int zero_comm_volume(uint64_t psi, uint32_t n, uint32_t stage, uint32_t elem_bytes,
+                     zero_comm *out);
+
+/*
+ * zero_peak_memory -- ZeRO-3 peak bytes per rank: the persistent 16 psi / N
+ * shard (padded: 16 S) plus units_resident gathered units of unit_params
+ * 16-bit weights plus activation_bytes ("ZeRO Stage 3 Math", "Peak transient
+ * memory").  Host only.  Errors: ZERO_EINVAL for bad layout arguments,
+ * unit_params > psi, overflow or a NULL out_bytes.
+ */
+int zero_peak_memory(uint64_t psi, uint32_t n, uint64_t unit_params, uint32_t units_resident,
+                     uint64_t activation_bytes, uint64_t *out_bytes);
 
 /* ---------------------------------------------------------------------------
  * Device-resident control: the same check -> decision -> step sequence with

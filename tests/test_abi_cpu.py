@@ -267,3 +267,72 @@ def test_device_path_argument_errors():
     assert L.zero_adam_step_dev(None, None, None, None, None, 0, 10, 8, 7, 1e-3, 0.9, 0.999,
                                 1e-8, 0.0, FAKE, None) == 0
     assert "table" in zs.zero_strerror(-4)
+
+
+@pytest.mark.parametrize("psi,n", [(8_810_000_000, 8), (8_810_000_000, 64), (10**9, 8),
+                                   (12345, 7), (1, 1), (2**56, 4096)])
+def test_comm_volume_matches_oracle(psi, n):
+    for stage in range(4):
+        for eb in (1, 2, 4, 8):
+            assert zs.zero_comm_volume(psi, n, stage, eb) == oracle.comm_volume(psi, n, stage, eb)
+
+
+def test_peak_memory_matches_oracle():
+    for psi, n, unit, units, act in ((10**10, 64, 10**10 // 60, 1, 0), (10**10, 64, 10**8, 2, 5),
+                                     (7_500_000_000, 8, 1, 0, 0), (12345, 7, 12345, 3, 99)):
+        assert zs.zero_peak_memory(psi, n, unit, units, act) == \
+            oracle.peak_memory(psi, n, unit, units, act)
+
+
+def test_accounting_errors_and_struct():
+    for args in ((0, 8, 0, 2), (10, 0, 0, 2), (10, 8, 4, 2), (10, 8, 0, 0), (10, 8, 0, 9)):
+        with pytest.raises(zs.ZeroError):
+            zs.zero_comm_volume(*args)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_peak_memory(10, 2, 11, 1, 0)        # a unit larger than the model
+    with pytest.raises(zs.ZeroError):
+        zs.zero_peak_memory(2**56, 1, 2**56, 2**31, 2**63)   # overflow
+    assert zs.lib.zero_comm_volume(10, 2, 0, 2, None) == -1
+    src = r"""
+    #include <stddef.h>
+    #include <stdio.h>
+    #include "zero_shard.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu %zu %zu %d %d", sizeof(zero_comm), offsetof(zero_comm, collectives),
+             offsetof(zero_comm, ring_hops), offsetof(zero_comm, elements),
+             offsetof(zero_comm, wire_bytes), offsetof(zero_comm, ring_bytes),
+             ZERO_MAX_LOCAL_RANKS, (int)ZERO_F32);
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), c, "-o", exe],
+                       check=True)
+        vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                               check=True).stdout.split()]
+    C = _binding._Comm
+    assert vals[0] == ctypes.sizeof(C)
+    assert vals[1:6] == [getattr(C, f).offset for f, _ in C._fields_]
+    assert vals[6] == _binding.MAX_LOCAL_RANKS and vals[7] == 2
+
+
+def test_exchange_argument_errors():
+    L = zs.lib
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    assert L.zero_reduce_shard(FAKE, 5, arr, 0, 100, 4, 0, None) == -2
+    assert L.zero_reduce_shard(FAKE, 0, arr, 7, 100, 4, 0, None) == -2
+    assert L.zero_reduce_shard(FAKE, 0, arr, 0, 100, 4, 4, None) == -1
+    assert L.zero_reduce_shard(FAKE, 0, arr, 0, 100, 65, 0, None) == -1
+    assert L.zero_reduce_shard(None, 0, arr, 0, 100, 4, 0, None) == -1
+    assert L.zero_reduce_shard(FAKE + 2, 2, arr, 0, 100, 4, 0, None) == -1   # FP32 out misaligned
+    bad = (ctypes.c_void_p * 4)(FAKE, None, FAKE, FAKE)
+    assert L.zero_reduce_shard(FAKE, 0, bad, 0, 100, 4, 0, None) == -1
+    assert L.zero_reduce_shard(None, 0, None, 0, 10, 8, 7, None) == 0        # empty rank
+    assert L.zero_gather_shards(FAKE, arr, 3, 100, 4, None) == -2
+    assert L.zero_gather_shards(None, arr, 0, 100, 4, None) == -1
+    assert L.zero_gather_shards(FAKE, bad, 0, 100, 4, None) == -1
+    assert L.zero_gather_shards(FAKE, arr, 0, 100, 65, None) == -1
+    # the 16-bit-only entry points reject FP32
+    assert L.zero_overflow_check(FAKE, 2, 100, 4, 0, 1.0, FAKE, None, None, None) == -2

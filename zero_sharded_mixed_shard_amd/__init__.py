@@ -21,6 +21,13 @@ FP32 gradients (accumulated across micro-batches):
     zero_overflow_check_g32(g32, psi, n, rank, loss_scale, found_inf, sumsq=None, partials=None)
     zero_adam_step_g32(w16, g32, master, m, v, psi, n, rank, *, lr, ..., step, loss_scale)
 
+The exchanges around the step on one GPU, and their accounting:
+
+    zero_reduce_shard(out, replicas, psi, n, rank)   # reduce-scatter result of one rank
+    zero_gather_shards(full, shards, psi, n)          # all-gather into the flat buffer
+    zero_comm_volume(psi, n, stage, elem_bytes) -> dict
+    zero_peak_memory(psi, n, unit_params, units_resident, activation_bytes) -> int
+
 Device-resident control (no read-back between steps):
 
     ctl = device_ctl_new(loss_scale, device)            # zero_device_ctl in device memory
@@ -43,10 +50,14 @@ from ._binding import (  # noqa: F401
     zero_adam_step_dev,
     zero_adam_step_g32,
     zero_bias_corrections,
+    zero_comm_volume,
+    zero_gather_shards,
     zero_grad_accumulate,
     zero_overflow_check,
     zero_overflow_check_dev,
     zero_overflow_check_g32,
+    zero_peak_memory,
+    zero_reduce_shard,
     zero_scaler_update,
     zero_scaler_update_dev,
     zero_shard_layout,
@@ -72,4 +83,8 @@ __all__ = [
     "zero_grad_accumulate",
     "zero_overflow_check_g32",
     "zero_adam_step_g32",
+    "zero_reduce_shard",
+    "zero_gather_shards",
+    "zero_comm_volume",
+    "zero_peak_memory",
 ]

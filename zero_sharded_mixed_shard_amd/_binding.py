@@ -10,8 +10,10 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero_shard.so")
 SUMSQ_PARTIALS = 4096  # ZERO_SUMSQ_PARTIALS
 
-ZERO_F16, ZERO_BF16 = 0, 1
+ZERO_F16, ZERO_BF16, ZERO_F32 = 0, 1, 2
+MAX_LOCAL_RANKS = 64  # ZERO_MAX_LOCAL_RANKS
 _DTYPES = {torch.float16: ZERO_F16, torch.bfloat16: ZERO_BF16}
+_FORMATS = {torch.float16: ZERO_F16, torch.bfloat16: ZERO_BF16, torch.float32: ZERO_F32}
 
 
 class ZeroError(RuntimeError):
@@ -84,6 +86,22 @@ lib.zero_overflow_check_g32.restype = _i32
 lib.zero_adam_step_g32.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32, _u32, _f32, _f32,
                                    _f32, _f32, _f32, _u64, _f32, _vp, _vp]
 lib.zero_adam_step_g32.restype = _i32
+lib.zero_reduce_shard.argtypes = [_vp, _i32, _vp, _i32, _u64, _u32, _u32, _vp]
+lib.zero_reduce_shard.restype = _i32
+lib.zero_gather_shards.argtypes = [_vp, _vp, _i32, _u64, _u32, _vp]
+lib.zero_gather_shards.restype = _i32
+
+
+class _Comm(ctypes.Structure):
+    _fields_ = [("collectives", ctypes.c_uint32), ("ring_hops", ctypes.c_uint32),
+                ("elements", ctypes.c_uint64), ("wire_bytes", ctypes.c_uint64),
+                ("ring_bytes", ctypes.c_uint64)]
+
+
+lib.zero_comm_volume.argtypes = [_u64, _u32, _u32, _u32, ctypes.POINTER(_Comm)]
+lib.zero_comm_volume.restype = _i32
+lib.zero_peak_memory.argtypes = [_u64, _u32, _u64, _u32, _u64, ctypes.POINTER(ctypes.c_uint64)]
+lib.zero_peak_memory.restype = _i32
 lib.zero_bias_corrections.argtypes = [_f32, _f32, _u64, _u32, _vp]
 lib.zero_bias_corrections.restype = _i32
 lib.zero_overflow_check_dev.argtypes = [_vp, _i32, _u64, _u32, _u32, _vp, _vp]
@@ -347,3 +365,70 @@ def zero_adam_step_g32(w16: torch.Tensor, g32: torch.Tensor, master: torch.Tenso
                                     _stream_handle(stream, dev))
     if rc != 0:
         raise ZeroError(rc, "zero_adam_step_g32")
+
+
+# ---- exchanges on one GPU and accounting ------------------------------------------
+
+def _ptr_list(tensors):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+def zero_reduce_shard(out: torch.Tensor, replicas, psi: int, n: int, rank: int,
+                      stream=None) -> None:
+    """Rank `rank`'s chunk of the FP32 sum of n full replica buffers, written in out's format."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = out.device
+    if len(replicas) != n:
+        raise ValueError(f"need {n} replicas, got {len(replicas)}")
+    in_dt = replicas[0].dtype
+    for k, r in enumerate(replicas):
+        _view(r, f"replica {k}", (in_dt,), psi, dev)
+    if in_dt not in _FORMATS:
+        raise TypeError(f"replica dtype {in_dt} not supported")
+    p_out = _view(out, "out", tuple(_FORMATS), lay.count, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_reduce_shard(p_out, _FORMATS[out.dtype], _ptr_list(replicas),
+                                   _FORMATS[in_dt], psi, n, rank, _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_reduce_shard")
+
+
+def zero_gather_shards(full: torch.Tensor, shards, psi: int, n: int, stream=None) -> None:
+    """full[k*S : k*S + count_k] = shards[k] for every rank k (all-gather semantics)."""
+    dev = full.device
+    if len(shards) != n:
+        raise ValueError(f"need {n} shards, got {len(shards)}")
+    p_full = _view(full, "full", tuple(_FORMATS), psi, dev)
+    for k, sh in enumerate(shards):
+        cnt = zero_shard_layout(psi, n, k).count
+        if sh is None:
+            if cnt:
+                raise ValueError(f"shard {k} holds {cnt} elements and cannot be None")
+            continue
+        _view(sh, f"shard {k}", (full.dtype,), cnt, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_gather_shards(p_full, _ptr_list(shards), _FORMATS[full.dtype], psi, n,
+                                    _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_gather_shards")
+
+
+def zero_comm_volume(psi: int, n: int, stage: int, elem_bytes: int) -> dict:
+    out = _Comm()
+    rc = lib.zero_comm_volume(psi, n, stage, elem_bytes, ctypes.byref(out))
+    if rc != 0:
+        raise ZeroError(rc, "zero_comm_volume")
+    return {f: getattr(out, f) for f, _ in _Comm._fields_}
+
+
+def zero_peak_memory(psi: int, n: int, unit_params: int, units_resident: int,
+                     activation_bytes: int) -> int:
+    out = ctypes.c_uint64(0)
+    rc = lib.zero_peak_memory(psi, n, unit_params, units_resident, activation_bytes,
+                              ctypes.byref(out))
+    if rc != 0:
+        raise ZeroError(rc, "zero_peak_memory")
+    return out.value

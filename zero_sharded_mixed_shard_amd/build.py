@@ -26,7 +26,8 @@ LIB = os.path.join(PKG, "libzero_shard.so")
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["layout.cpp", "scaler.cpp", "api.cpp", "shard_kernels.hip"]
+SOURCES = ["layout.cpp", "scaler.cpp", "accounting.cpp", "api.cpp", "shard_kernels.hip",
+           "exchange_kernels.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-ffp-contract=off",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

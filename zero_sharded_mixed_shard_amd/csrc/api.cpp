@@ -203,6 +203,53 @@ extern "C" int zero_adam_step_g32(void *w16, const float *g32, float *master, fl
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step_g32 launch");
 }
 
+extern "C" int zero_reduce_shard(void *out, zero_dtype out_dt, const void *const *replicas,
+                                 zero_dtype in_dt, uint64_t psi, uint32_t n, uint32_t rank,
+                                 void *stream) {
+    const auto fmt_ok = [](zero_dtype d) { return d == ZERO_F16 || d == ZERO_BF16 || d == ZERO_F32; };
+    if (!fmt_ok(out_dt) || !fmt_ok(in_dt)) return ZERO_EDTYPE;
+    zero_layout lay;
+    if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
+    if (n > zs::kMaxLocalRanks) return ZERO_EINVAL;
+    if (lay.count == 0) return ZERO_OK;
+    const uintptr_t in_b = in_dt == ZERO_F32 ? 4 : 2, out_b = out_dt == ZERO_F32 ? 4 : 2;
+    if (out == nullptr || !aligned(out, out_b) || replicas == nullptr) return ZERO_EINVAL;
+    zs::ReplicaSet set;
+    for (uint32_t k = 0; k < n; ++k) {
+        if (replicas[k] == nullptr || !aligned(replicas[k], in_b)) return ZERO_EINVAL;
+        set.p[k] = static_cast<const char *>(replicas[k]) + lay.offset * in_b;
+    }
+    const hipError_t e = zs::launch_reduce_shard(out, static_cast<int>(out_dt), set,
+                                                 static_cast<int>(in_dt), n, lay.count,
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_reduce_shard launch");
+}
+
+extern "C" int zero_gather_shards(void *full, const void *const *shards, zero_dtype dt,
+                                  uint64_t psi, uint32_t n, void *stream) {
+    if (dt != ZERO_F16 && dt != ZERO_BF16 && dt != ZERO_F32) return ZERO_EDTYPE;
+    zero_layout lay;
+    if (zero_shard_layout(psi, n, 0, &lay) != ZERO_OK) return ZERO_EINVAL;
+    if (n > zs::kMaxLocalRanks) return ZERO_EINVAL;
+    const uintptr_t eb = dt == ZERO_F32 ? 4 : 2;
+    if (full == nullptr || !aligned(full, eb) || shards == nullptr) return ZERO_EINVAL;
+    zs::GatherSet set;
+    uint64_t max_count = 0;
+    for (uint32_t k = 0; k < n; ++k) {
+        zero_layout lk;
+        zero_shard_layout(psi, n, k, &lk);
+        if (lk.count > 0 && (shards[k] == nullptr || !aligned(shards[k], eb))) return ZERO_EINVAL;
+        set.p[k] = shards[k];
+        set.count[k] = lk.count;
+        set.head[k] = 0;
+        set.vec[k] = 0;
+        if (lk.count > max_count) max_count = lk.count;
+    }
+    const hipError_t e = zs::launch_gather_shards(full, static_cast<int>(eb), set, n, lay.shard,
+                                                  max_count, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_gather_shards launch");
+}
+
 extern "C" int zero_bias_corrections(float beta1, float beta2, uint64_t t_first, uint32_t len,
                                      float *out) {
     if (out == nullptr || len == 0 || t_first == 0 || !beta_ok(beta1) || !beta_ok(beta2))

@@ -57,6 +57,27 @@ hipError_t launch_overflow_check_g32(const float *g32, uint64_t count, float los
                                      int32_t *flag, float *sumsq, double *partials, int num_cus,
                                      hipStream_t stream);
 
+// Views of up to ZERO_MAX_LOCAL_RANKS replicas or shards, passed by value.
+constexpr uint32_t kMaxLocalRanks = 64;  // == ZERO_MAX_LOCAL_RANKS
+struct ReplicaSet {
+    const void *p[kMaxLocalRanks];        // replica k advanced to the rank's first element
+};
+struct GatherSet {
+    const void *p[kMaxLocalRanks];        // shard k (shard-local)
+    uint64_t count[kMaxLocalRanks];       // real elements of shard k
+    uint32_t head[kMaxLocalRanks];        // filled by the launcher
+    uint32_t vec[kMaxLocalRanks];         // filled by the launcher
+};
+
+// out[i] = FP32 sum over k < n of in.p[k][i], rounded to out_fmt (0 FP16,
+// 1 BF16, 2 FP32), i < count; count > 0.
+hipError_t launch_reduce_shard(void *out, int out_fmt, const ReplicaSet &in, int in_fmt,
+                               uint32_t n, uint64_t count, hipStream_t stream);
+
+// full[k*shard + i] = set.p[k][i] for i < set.count[k], k < n.
+hipError_t launch_gather_shards(void *full, int elem_bytes, GatherSet &set, uint32_t n,
+                                uint64_t shard, uint64_t max_count, hipStream_t stream);
+
 // Enqueue the one-lane skip-or-apply decision on a device control block.
 hipError_t launch_scaler_decide(zero_device_ctl *ctl, const float *bias, uint64_t t_first,
                                 uint32_t len, hipStream_t stream);
