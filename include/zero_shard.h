@@ -52,6 +52,8 @@ typedef enum { ZERO_F16 = 0, ZERO_BF16 = 1, ZERO_F32 = 2 } zero_dtype;
 #define ZERO_EINVAL (-1) /* an argument is out of its documented domain */
 #define ZERO_EDTYPE (-2) /* dt is not a zero_dtype value */
 #define ZERO_EHIP (-3)   /* the HIP runtime reported an error (see zero_strerror) */
+#define ZERO_EIO (-5)    /* a checkpoint file could not be opened, written or read */
+#define ZERO_ECORRUPT (-6) /* a checkpoint file failed its header, size or hash check */
 
 /* Largest flat buffer accepted: keeps every byte count below 2^64. */
 #define ZERO_MAX_PSI (1ull << 56)
@@ -362,6 +364,83 @@ int zero_adam_step_dev(void *w16, const void *g16, float *master, float *m, floa
                        zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank, float lr,
                        float beta1, float beta2, float eps, float weight_decay,
                        const zero_device_ctl *d_ctl, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Sharded checkpoints: each rank writes its own slice of the model states to
+ * its own file, in parallel with the others ("Stop Replicating What You Can
+ * Shard", "Two memory levers you compose with sharding"); a run resumes on
+ * the same or another number of ranks.  Host pointers and host files only
+ * (copy device buffers to host memory first).
+ * ------------------------------------------------------------------------- */
+
+/* What a shard file records besides the four arrays. */
+typedef struct {
+    uint64_t psi;       /* flat buffer size */
+    uint32_t n, rank;   /* the layout the shard belongs to */
+    uint64_t offset;    /* rank * S (filled by the reader; ignored by the writer) */
+    uint64_t count;     /* real elements (filled by the reader; ignored by the writer) */
+    zero_dtype dtype;   /* working weights' format: ZERO_F16 or ZERO_BF16 */
+    zero_scaler scaler; /* loss scale, growth interval, applied steps, clean steps */
+} zero_ckpt_info;
+
+/*
+ * zero_ckpt_write -- write rank info->rank's slice: header, then count
+ * 16-bit working weights and count FP32 master, m and v values (count from
+ * the layout), with a 64-bit FNV-1a hash of the payload in the header.
+ *   w16, master, m, v  HOST arrays of count elements.
+ *   Errors: ZERO_EINVAL (bad layout, NULL pointers), ZERO_EDTYPE, ZERO_EIO.
+ */
+int zero_ckpt_write(const char *path, const zero_ckpt_info *info, const void *w16,
+                    const float *master, const float *m, const float *v);
+
+/* zero_ckpt_read_info -- header of a shard file, checked against its layout
+ * and the file size.  Errors: ZERO_EINVAL, ZERO_EIO, ZERO_ECORRUPT. */
+int zero_ckpt_read_info(const char *path, zero_ckpt_info *info);
+
+/* zero_ckpt_verify -- recompute the payload hash.  ZERO_OK, or ZERO_ECORRUPT /
+ * ZERO_EIO. */
+int zero_ckpt_verify(const char *path);
+
+/*
+ * zero_ckpt_read -- elements [first, first + count) of a shard file's arrays
+ * into HOST arrays (w16: 2-byte elements; master, m, v: FP32).  Errors:
+ * ZERO_EINVAL for a range outside the shard or NULL pointers with count > 0;
+ * ZERO_EIO; ZERO_ECORRUPT for a bad header or size.
+ */
+int zero_ckpt_read(const char *path, uint64_t first, uint64_t count, void *w16, float *master,
+                   float *m, float *v);
+
+/* One piece of a new rank's range: count elements starting at src_first of
+ * old rank src_rank's shard go to dst_first of the new shard. */
+typedef struct {
+    uint32_t src_rank;
+    uint64_t src_first;
+    uint64_t dst_first;
+    uint64_t count;
+} zero_ckpt_piece;
+
+/*
+ * zero_reshard_plan -- the pieces of the n_old shards that rank rank_new of a
+ * layout with n_new ranks reads, in flat order.  The concatenation of the
+ * shards is the flat buffer, so a new layout's range is read from the old
+ * shards that overlap it.  pieces may be NULL to count them only.
+ *   Errors: ZERO_EINVAL for bad layouts or a NULL n_pieces; ZERO_ERANGE if
+ *   more than max_pieces pieces are needed.
+ */
+int zero_reshard_plan(uint64_t psi, uint32_t n_old, uint32_t n_new, uint32_t rank_new,
+                      zero_ckpt_piece *pieces, uint32_t max_pieces, uint32_t *n_pieces);
+
+/*
+ * zero_ckpt_read_resharded -- rank rank_new's slice of a layout with n_new
+ * ranks, read from the n_old shard files of the same flat buffer (paths_old[k]
+ * is old rank k's file; only the files zero_reshard_plan names are opened),
+ * into HOST arrays of the new rank's count elements.  Every file read is
+ * checked against psi, n_old and its rank, and all must share one format.
+ *   Errors: ZERO_EINVAL, ZERO_EIO, ZERO_ECORRUPT.
+ */
+int zero_ckpt_read_resharded(const char *const *paths_old, uint32_t n_old, uint64_t psi,
+                             uint32_t n_new, uint32_t rank_new, void *w16, float *master,
+                             float *m, float *v);
 
 /*
  * zero_strerror -- text for a return code.  For ZERO_EHIP it names the HIP

@@ -1,0 +1,164 @@
+"""Sharded checkpoints (host side): round trip, integrity checks, the re-shard
+plan against brute force, resharded reads, and resume invariance with the
+oracle (N shards -> save -> N' shards -> continue equals the unsharded run).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import zero_sharded_mixed_shard_amd as zs
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def state(count, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.integers(0, 1 << 16, count, dtype=np.uint32).astype(np.uint16),
+            rng.standard_normal(count).astype(np.float32),
+            rng.standard_normal(count).astype(np.float32),
+            rng.random(count).astype(np.float32))
+
+
+def test_round_trip_and_info(tmp_path):
+    psi, n = 1_000_003, 8
+    for rank in (0, 7):
+        cnt = oracle.layout(psi, n, rank).count
+        st = state(cnt, rank)
+        sc = zs.Scaler(2048.0, growth_interval=77, step=1234)
+        sc.clean_steps = 5
+        p = str(tmp_path / f"r{rank}.zshard")
+        zs.zero_ckpt_write(p, psi, n, rank, "bf16", sc, *st)
+        info = zs.zero_ckpt_read_info(p)
+        assert (info.psi, info.n, info.rank, info.count, info.dtype) == (psi, n, rank, cnt, 1)
+        assert info.offset == oracle.layout(psi, n, rank).offset
+        assert (info.scaler.loss_scale, info.scaler.growth_interval, info.scaler.step,
+                info.scaler.clean_steps) == (2048.0, 77, 1234, 5)
+        zs.zero_ckpt_verify(p)
+        back = zs.zero_ckpt_read(p, 0, cnt)
+        for a, b in zip(st, back):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+        part = zs.zero_ckpt_read(p, 12345, 1000)
+        for a, b in zip(st, part):
+            assert np.array_equal(a[12345:13345].view(np.uint8), b.view(np.uint8))
+        assert os.path.getsize(p) == 128 + 14 * cnt
+
+
+def test_empty_rank_round_trip(tmp_path):
+    p = str(tmp_path / "e.zshard")
+    empty = [np.zeros(0, np.uint16)] + [np.zeros(0, np.float32)] * 3
+    zs.zero_ckpt_write(p, 10, 8, 7, "f16", zs.Scaler(1.0), *empty)
+    assert zs.zero_ckpt_read_info(p).count == 0
+    zs.zero_ckpt_verify(p)
+
+
+def test_integrity_errors(tmp_path):
+    psi, n, rank = 10_000, 4, 1
+    cnt = oracle.layout(psi, n, rank).count
+    p = str(tmp_path / "x.zshard")
+    zs.zero_ckpt_write(p, psi, n, rank, "f16", zs.Scaler(1.0), *state(cnt, 3))
+    raw = open(p, "rb").read()
+    # a flipped payload byte: the header still reads, the hash does not match
+    bad = bytearray(raw)
+    bad[128 + 5000] ^= 0x40
+    q = str(tmp_path / "flip.zshard")
+    open(q, "wb").write(bytes(bad))
+    zs.zero_ckpt_read_info(q)
+    with pytest.raises(zs.ZeroError) as e:
+        zs.zero_ckpt_verify(q)
+    assert e.value.code == -6
+    # truncated, wrong magic, inconsistent layout fields
+    for name, data in (("trunc", raw[:-4]), ("magic", b"X" + raw[1:]),
+                       ("count", raw[:40] + (cnt + 1).to_bytes(8, "little") + raw[48:])):
+        q = str(tmp_path / f"{name}.zshard")
+        open(q, "wb").write(data)
+        with pytest.raises(zs.ZeroError) as e:
+            zs.zero_ckpt_read_info(q)
+        assert e.value.code == -6, name
+    with pytest.raises(zs.ZeroError) as e:
+        zs.zero_ckpt_read_info(str(tmp_path / "missing.zshard"))
+    assert e.value.code == -5
+    with pytest.raises(zs.ZeroError) as e:
+        zs.zero_ckpt_read(p, cnt - 10, 11)
+    assert e.value.code == -1
+
+
+def brute_plan(psi, n_old, n_new, r_new):
+    """Walk the new rank's flat indices; group runs that come from one old shard."""
+    S = oracle.layout(psi, n_old, 0).shard
+    lay = oracle.layout(psi, n_new, r_new)
+    pieces = []
+    for j in range(lay.offset, lay.offset + lay.count):
+        k, pos, dst = j // S, j % S, j - lay.offset
+        if pieces and pieces[-1][0] == k and pieces[-1][1] + pieces[-1][3] == pos:
+            pieces[-1] = (k, pieces[-1][1], pieces[-1][2], pieces[-1][3] + 1)
+        else:
+            pieces.append((k, pos, dst, 1))
+    return pieces
+
+
+def test_reshard_plan_brute_force():
+    for psi in list(range(1, 40)) + [97, 1000]:
+        for n_old in range(1, 10):
+            for n_new in range(1, 10):
+                for r in range(n_new):
+                    assert zs.zero_reshard_plan(psi, n_old, n_new, r) == \
+                        brute_plan(psi, n_old, n_new, r), (psi, n_old, n_new, r)
+
+
+@pytest.mark.parametrize("psi,n_old,n_new", [(100_003, 8, 5), (100_003, 1, 8), (100_003, 8, 1),
+                                             (8_810, 64, 3), (10, 8, 3)])
+def test_resharded_read_matches_flat_slices(tmp_path, psi, n_old, n_new):
+    flat = state(psi, 11)
+    paths = []
+    for k in range(n_old):
+        lay = oracle.layout(psi, n_old, k)
+        sl = slice(lay.offset, lay.offset + lay.count)
+        p = str(tmp_path / f"old{k}.zshard")
+        zs.zero_ckpt_write(p, psi, n_old, k, "f16", zs.Scaler(8.0),
+                           *(np.ascontiguousarray(a[sl]) for a in flat))
+        paths.append(p)
+    for r in range(n_new):
+        lay = oracle.layout(psi, n_new, r)
+        got = zs.zero_ckpt_read_resharded(paths, psi, n_new, r)
+        for a, b in zip(flat, got):
+            assert np.array_equal(a[lay.offset:lay.offset + lay.count].view(np.uint8),
+                                  b.view(np.uint8))
+
+
+def test_resume_on_another_rank_count_is_exact(tmp_path):
+    # oracle-level invariant: 3 steps on 8 shards, save, resume on 5 shards,
+    # 2 more steps == 5 steps on the unsharded buffer
+    psi = 50_021
+    rng = np.random.default_rng(21)
+    grads = [(rng.standard_normal(psi) * 1e-3).astype(np.float16).view(np.uint16)
+             for _ in range(5)]
+    master0 = (rng.standard_normal(psi) * 0.02).astype(np.float32)
+    full = [np.zeros(psi, np.uint16), master0.copy(), np.zeros(psi, np.float32),
+            np.zeros(psi, np.float32)]
+    for t in range(1, 6):
+        oracle.adam_step(full[0], grads[t - 1], full[1], full[2], full[3], "f16", step=t,
+                         loss_scale=1.0, **HP)
+    paths = []
+    for k in range(8):
+        lay = oracle.layout(psi, 8, k)
+        sl = slice(lay.offset, lay.offset + lay.count)
+        sh = [np.zeros(lay.count, np.uint16), master0[sl].copy(),
+              np.zeros(lay.count, np.float32), np.zeros(lay.count, np.float32)]
+        for t in range(1, 4):
+            oracle.adam_step(sh[0], np.ascontiguousarray(grads[t - 1][sl]), sh[1], sh[2], sh[3],
+                             "f16", step=t, loss_scale=1.0, **HP)
+        p = str(tmp_path / f"k{k}.zshard")
+        zs.zero_ckpt_write(p, psi, 8, k, "f16", zs.Scaler(1.0, step=3), *sh)
+        paths.append(p)
+    for r in range(5):
+        lay = oracle.layout(psi, 5, r)
+        sl = slice(lay.offset, lay.offset + lay.count)
+        sh = list(zs.zero_ckpt_read_resharded(paths, psi, 5, r))
+        t0 = zs.zero_ckpt_read_info(paths[0]).scaler.step
+        for t in range(t0 + 1, t0 + 3):
+            oracle.adam_step(sh[0], np.ascontiguousarray(grads[t - 1][sl]), sh[1], sh[2], sh[3],
+                             "f16", step=t, loss_scale=1.0, **HP)
+        for a, b in zip(full, sh):
+            assert np.array_equal(a[sl].view(np.uint8), b.view(np.uint8))

@@ -28,6 +28,13 @@ The exchanges around the step on one GPU, and their accounting:
     zero_comm_volume(psi, n, stage, elem_bytes) -> dict
     zero_peak_memory(psi, n, unit_params, units_resident, activation_bytes) -> int
 
+Sharded checkpoints (host numpy arrays; one file per rank):
+
+    zero_ckpt_write(path, psi, n, rank, dtype, scaler, w16, master, m, v)
+    zero_ckpt_read_info(path) / zero_ckpt_verify(path) / zero_ckpt_read(path, first, count)
+    zero_reshard_plan(psi, n_old, n_new, rank_new) -> [(src_rank, src_first, dst_first, count)]
+    zero_ckpt_read_resharded(paths_old, psi, n_new, rank_new) -> (w16, master, m, v)
+
 Device-resident control (no read-back between steps):
 
     ctl = device_ctl_new(loss_scale, device)            # zero_device_ctl in device memory
@@ -38,6 +45,7 @@ Device-resident control (no read-back between steps):
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
+    CkptInfo,
     SUMSQ_PARTIALS,
     DeviceCtl,
     Layout,
@@ -50,6 +58,11 @@ from ._binding import (  # noqa: F401
     zero_adam_step_dev,
     zero_adam_step_g32,
     zero_bias_corrections,
+    zero_ckpt_read,
+    zero_ckpt_read_info,
+    zero_ckpt_read_resharded,
+    zero_ckpt_verify,
+    zero_ckpt_write,
     zero_comm_volume,
     zero_gather_shards,
     zero_grad_accumulate,
@@ -58,6 +71,7 @@ from ._binding import (  # noqa: F401
     zero_overflow_check_g32,
     zero_peak_memory,
     zero_reduce_shard,
+    zero_reshard_plan,
     zero_scaler_update,
     zero_scaler_update_dev,
     zero_shard_layout,
@@ -87,4 +101,11 @@ __all__ = [
     "zero_gather_shards",
     "zero_comm_volume",
     "zero_peak_memory",
+    "CkptInfo",
+    "zero_ckpt_write",
+    "zero_ckpt_read_info",
+    "zero_ckpt_verify",
+    "zero_ckpt_read",
+    "zero_reshard_plan",
+    "zero_ckpt_read_resharded",
 ]

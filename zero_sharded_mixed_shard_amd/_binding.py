@@ -5,6 +5,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero_shard.so")
@@ -432,3 +433,103 @@ def zero_peak_memory(psi: int, n: int, unit_params: int, units_resident: int,
     if rc != 0:
         raise ZeroError(rc, "zero_peak_memory")
     return out.value
+
+
+# ---- sharded checkpoints (host arrays) ---------------------------------------------
+
+class CkptInfo(ctypes.Structure):
+    """zero_ckpt_info."""
+    _fields_ = [("psi", ctypes.c_uint64), ("n", ctypes.c_uint32), ("rank", ctypes.c_uint32),
+                ("offset", ctypes.c_uint64), ("count", ctypes.c_uint64), ("dtype", ctypes.c_int),
+                ("scaler", Scaler)]
+
+
+class _Piece(ctypes.Structure):
+    _fields_ = [("src_rank", ctypes.c_uint32), ("src_first", ctypes.c_uint64),
+                ("dst_first", ctypes.c_uint64), ("count", ctypes.c_uint64)]
+
+
+_cp = ctypes.c_char_p
+lib.zero_ckpt_write.argtypes = [_cp, ctypes.POINTER(CkptInfo), _vp, _vp, _vp, _vp]
+lib.zero_ckpt_read_info.argtypes = [_cp, ctypes.POINTER(CkptInfo)]
+lib.zero_ckpt_verify.argtypes = [_cp]
+lib.zero_ckpt_read.argtypes = [_cp, _u64, _u64, _vp, _vp, _vp, _vp]
+lib.zero_reshard_plan.argtypes = [_u64, _u32, _u32, _u32, ctypes.POINTER(_Piece), _u32,
+                                  ctypes.POINTER(ctypes.c_uint32)]
+lib.zero_ckpt_read_resharded.argtypes = [_vp, _u32, _u64, _u32, _u32, _vp, _vp, _vp, _vp]
+for _f in ("zero_ckpt_write", "zero_ckpt_read_info", "zero_ckpt_verify", "zero_ckpt_read",
+           "zero_reshard_plan", "zero_ckpt_read_resharded"):
+    getattr(lib, _f).restype = _i32
+
+_DTYPE_CODES = {"f16": ZERO_F16, "bf16": ZERO_BF16, torch.float16: ZERO_F16,
+                torch.bfloat16: ZERO_BF16}
+
+
+def _host(a: np.ndarray, dtype, count: int, name: str) -> int:
+    if not isinstance(a, np.ndarray) or a.dtype != dtype or not a.flags.c_contiguous:
+        raise TypeError(f"{name} must be a C-contiguous numpy {np.dtype(dtype)} array")
+    if a.size < count:
+        raise ValueError(f"{name} holds {a.size} elements, the shard needs {count}")
+    return a.ctypes.data
+
+
+def zero_ckpt_write(path: str, psi: int, n: int, rank: int, dtype, scaler: Scaler,
+                    w16: np.ndarray, master: np.ndarray, m: np.ndarray, v: np.ndarray) -> None:
+    """Write one rank's slice (host numpy arrays: uint16 bit patterns and float32)."""
+    cnt = zero_shard_layout(psi, n, rank).count
+    info = CkptInfo(psi, n, rank, 0, 0, _DTYPE_CODES[dtype], scaler)
+    rc = lib.zero_ckpt_write(os.fsencode(path), ctypes.byref(info),
+                             _host(w16, np.uint16, cnt, "w16"), _host(master, np.float32, cnt, "master"),
+                             _host(m, np.float32, cnt, "m"), _host(v, np.float32, cnt, "v"))
+    if rc != 0:
+        raise ZeroError(rc, "zero_ckpt_write")
+
+
+def zero_ckpt_read_info(path: str) -> CkptInfo:
+    info = CkptInfo()
+    rc = lib.zero_ckpt_read_info(os.fsencode(path), ctypes.byref(info))
+    if rc != 0:
+        raise ZeroError(rc, "zero_ckpt_read_info")
+    return info
+
+
+def zero_ckpt_verify(path: str) -> None:
+    rc = lib.zero_ckpt_verify(os.fsencode(path))
+    if rc != 0:
+        raise ZeroError(rc, "zero_ckpt_verify")
+
+
+def zero_ckpt_read(path: str, first: int, count: int):
+    """Elements [first, first + count) of a shard file: (w16 uint16, master, m, v float32)."""
+    out = (np.empty(count, np.uint16), np.empty(count, np.float32), np.empty(count, np.float32),
+           np.empty(count, np.float32))
+    rc = lib.zero_ckpt_read(os.fsencode(path), first, count, *(a.ctypes.data for a in out))
+    if rc != 0:
+        raise ZeroError(rc, "zero_ckpt_read")
+    return out
+
+
+def zero_reshard_plan(psi: int, n_old: int, n_new: int, rank_new: int) -> list:
+    """[(src_rank, src_first, dst_first, count), ...] for rank_new of the new layout."""
+    cnt = ctypes.c_uint32(0)
+    rc = lib.zero_reshard_plan(psi, n_old, n_new, rank_new, None, 0, ctypes.byref(cnt))
+    if rc != 0:
+        raise ZeroError(rc, "zero_reshard_plan")
+    pieces = (_Piece * max(1, cnt.value))()
+    rc = lib.zero_reshard_plan(psi, n_old, n_new, rank_new, pieces, cnt.value, ctypes.byref(cnt))
+    if rc != 0:
+        raise ZeroError(rc, "zero_reshard_plan")
+    return [(p.src_rank, p.src_first, p.dst_first, p.count) for p in pieces[:cnt.value]]
+
+
+def zero_ckpt_read_resharded(paths_old, psi: int, n_new: int, rank_new: int):
+    """Rank rank_new's slice of an n_new-rank layout from the old shard files."""
+    cnt = zero_shard_layout(psi, n_new, rank_new).count
+    out = (np.empty(cnt, np.uint16), np.empty(cnt, np.float32), np.empty(cnt, np.float32),
+           np.empty(cnt, np.float32))
+    arr = (ctypes.c_char_p * len(paths_old))(*[os.fsencode(p) for p in paths_old])
+    rc = lib.zero_ckpt_read_resharded(ctypes.cast(arr, ctypes.c_void_p), len(paths_old), psi,
+                                      n_new, rank_new, *(a.ctypes.data for a in out))
+    if rc != 0:
+        raise ZeroError(rc, "zero_ckpt_read_resharded")
+    return out

@@ -26,7 +26,8 @@ LIB = os.path.join(PKG, "libzero_shard.so")
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["layout.cpp", "scaler.cpp", "accounting.cpp", "api.cpp", "shard_kernels.hip",
+SOURCES = ["layout.cpp", "scaler.cpp", "accounting.cpp", "checkpoint.cpp", "api.cpp",
+           "shard_kernels.hip",
            "exchange_kernels.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-ffp-contract=off",
           f"-I{INCLUDE}", f"-I{CSRC}"]
@@ -47,8 +48,8 @@ def build(verbose: bool = False) -> str:
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
-            lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-            cmd = [HIPCC, *lang, *DEVICE, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+            # every source goes through the HIP driver (host files include the runtime API)
+            cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd))
             _run(cmd)

@@ -315,7 +315,12 @@ extern "C" const char *zero_strerror(int code) {
         case ZERO_EHIP:
             return g_err[0] ? g_err : "HIP runtime error";
         case ZERO_ERANGE:
-            return "step outside the bias-correction table";
+            return "value out of range (step outside the bias-correction table, or too few "
+                   "reshard pieces)";
+        case ZERO_EIO:
+            return "checkpoint file could not be opened, written or read";
+        case ZERO_ECORRUPT:
+            return "checkpoint file failed its header, size or hash check";
         default:
             return "unknown error code";
     }
