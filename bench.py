@@ -155,6 +155,79 @@ def copy_bandwidth(dev, gib: int = 4):
     return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
+def measure_extras(dev, n_elem: int = 1 << 30, reps: int = 5) -> dict:
+    """Bandwidth of the path's other kernels on n_elem-element shards (HIP events).
+
+    Algorithmic bytes per element: accumulate 10 (read 2 + 4, write 4), FP32
+    check 4, FP32-gradient step 30, reduce of 8 FP16 replicas into FP16 18 (read
+    8 x 2, write 2), gather of 8 FP16 shards 4 (read 2, write 2), and the
+    device-controlled check + decision + step 30 (2 + 28)."""
+    import torch
+
+    import synth
+    import zero_sharded_mixed_shard_amd as zs
+
+    out = {}
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def record(name, ms, elems, bpe):
+        gbps = bpe * elems / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "elements": elems, "bytes_per_elem": bpe, "GBps": gbps,
+                     "frac": gbps / PEAK_HBM_GBPS}
+
+    n = n_elem
+    hp = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
+    g16 = synth.fill_normal_(torch.empty(n, dtype=torch.float16, device=dev), 1e-3, 1)
+    acc = torch.zeros(n, device=dev)
+    zs.zero_grad_accumulate(acc, g16, n, 1, 0, first=True)
+    record("grad_accumulate", timed(lambda: zs.zero_grad_accumulate(acc, g16, n, 1, 0,
+                                                                    first=False)), n, 10)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    record("overflow_check_g32", timed(lambda: zs.zero_overflow_check_g32(acc, n, 1, 0, 65536.0,
+                                                                          flag)), n, 4)
+    master = synth.fill_normal_(torch.empty(n, device=dev), 0.02, 2)
+    m = torch.zeros(n, device=dev)
+    v = torch.zeros(n, device=dev)
+    w16 = torch.zeros(n, dtype=torch.float16, device=dev)
+    record("adam_step_g32", timed(lambda: zs.zero_adam_step_g32(
+        w16, acc, master, m, v, n, 1, 0, step=1, loss_scale=65536.0 * 8, **hp)), n, 30)
+    ctl = zs.device_ctl_new(65536.0, dev)
+    bias = zs.zero_bias_corrections(0.9, 0.999, 1, 64).to(dev)
+
+    def dev_step():
+        zs.zero_overflow_check_dev(g16, n, 1, 0, ctl)
+        zs.zero_scaler_update_dev(ctl, bias, 1)
+        zs.zero_adam_step_dev(w16, g16, master, m, v, n, 1, 0, ctl=ctl, **hp)
+
+    record("device_controlled_step", timed(dev_step), n, 30)
+    del acc, m, v, master, ctl
+    torch.cuda.empty_cache()
+    # exchanges: 8 ranks, flat buffer of n elements
+    ranks = 8
+    reps16 = [synth.fill_normal_(torch.empty(n, dtype=torch.float16, device=dev), 1e-2, 10 + k)
+              for k in range(ranks)]
+    lay = zs.zero_shard_layout(n, ranks, 0)
+    shard = torch.empty(lay.count, dtype=torch.float16, device=dev)
+    record("reduce_shard_8x_f16", timed(lambda: zs.zero_reduce_shard(shard, reps16, n, ranks, 0)),
+           lay.count, 2 * ranks + 2)
+    shards = [r[:zs.zero_shard_layout(n, ranks, k).count].clone() for k, r in enumerate(reps16)]
+    del reps16
+    record("gather_shards_8x_f16", timed(lambda: zs.zero_gather_shards(w16, shards, n, ranks)),
+           n, 4)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +241,9 @@ def main():
                     help="parameters in the CPU baseline's sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy measurement")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time the accumulate / FP32-gradient / device-control / exchange "
+                         "kernels on 2^30-element shards (reported under 'extras')")
     ap.add_argument("--control", choices=["host", "device"], default="host",
                     help="skip-or-apply decision on the host (4-byte read-back per step) or in "
                          "device memory (no read-back)")
@@ -269,6 +345,12 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
         cpu = cpu_baseline(b, w, args.cpu_seconds, args.cpu_sample)
+    extras = None
+    if args.extras:
+        del b
+        torch.cuda.empty_cache()
+        log("[bench] extras ...")
+        extras = measure_extras(dev)
 
     out = {
         "metric": METRIC,
@@ -298,6 +380,8 @@ def main():
                     "device_copy_GBps": copy_gbps},
         "cpu_baseline": cpu,
     }
+    if extras is not None:
+        out["extras"] = extras
     print(json.dumps(out), flush=True)
 
 
