@@ -14,13 +14,13 @@ m = v = 0 at the start, AdamW lr 1e-4, wd 0.1.
 Prints one JSON line: params/s over the timed steps, the step kernel's HBM
 roofline (algorithmic 28 B/param over its HIP-event-timed average duration,
 against the 8 TB/s peak), the HBM traffic measured by rocprofv3 counters when
-the profiled kernel source matches, and the CPU oracle timed on a bounded
-sample of the same inputs.
+the profiled kernel's machine code matches the built one, and the CPU oracle
+timed on a bounded sample of the same inputs.
 
     python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload 4]
 """
 import argparse
-import hashlib
+import importlib.util
 import json
 import os
 import sys
@@ -33,7 +33,7 @@ METRIC = "shard Adam params/sec + achieved HBM GB/s (28 B/param) vs peak, 1×MI3
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
 STEP_BYTES_PER_PARAM = 28       # read g 2 + master/m/v 12; write master/m/v 12 + w16 2
 CHECK_BYTES_PER_PARAM = 2
-KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_shard_amd", "csrc", "shard_kernels.hip")
+BUILD_SCRIPT = os.path.join(ROOT, "zero_sharded_mixed_shard_amd", "build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adam_step_flat10B_hbm_traffic.md")
 
 
@@ -41,16 +41,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def built_isa_hashes() -> dict:
+    """Per-kernel machine-code hashes that the build wrote beside the library."""
+    spec = importlib.util.spec_from_file_location("zs_build", BUILD_SCRIPT)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.read_isa_hashes()
 
 
 def measured_traffic(workload_name: str):
     """HBM bytes per step-kernel launch from the committed rocprofv3 counter summary.
 
-    Returns None unless the summary was taken on this workload with the kernel
-    source that is built now."""
+    Returns None unless the summary was taken on this workload with the same
+    machine code of the step kernel as the library built now."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -59,7 +62,8 @@ def measured_traffic(workload_name: str):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 kv[k.strip()] = v.strip().strip("`")
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    symbol = kv.get("kernel_symbol")
+    if symbol is None or kv.get("kernel_isa_sha256") != built_isa_hashes().get(symbol):
         return None
     if kv.get("workload") != workload_name:
         return None
