@@ -253,6 +253,71 @@ def measure_extras(dev, n_elem: int = 1 << 30, reps: int = 5) -> dict:
     return out
 
 
+def measure_small(dev, steps: int = 300, warmup: int = 20) -> dict:
+    """Whole-step time of the launch-bound workloads under three kinds of control.
+
+    For each small workload (the 1M-parameter rank and one GPT-2-small rank):
+    host control (the flag read back every step, as the main loop does),
+    device control (check, decision and step enqueued with no read-back), and
+    the device-controlled step captured once into a HIP graph and replayed.
+    Times are wall-clock per step over `steps` steps between synchronisations."""
+    import torch
+
+    import zero_sharded_mixed_shard_amd as zs
+
+    out = {}
+    for cfg in (1, 2):
+        w, rank, lay, b = make_workload(cfg, dev)
+        psi, n, cnt = w.psi, w.n, lay.count
+        hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                  weight_decay=w.weight_decay)
+        flag = torch.zeros(1, dtype=torch.int32, device=dev)
+        scaler = zs.Scaler(w.loss_scale)
+        total = 3 * (warmup + steps) + 8
+        ctl = zs.device_ctl_new(w.loss_scale, dev)
+        bias = zs.zero_bias_corrections(w.beta1, w.beta2, 1, total).to(dev)
+
+        def host_step():
+            zs.zero_overflow_check(b["g16"], psi, n, rank, scaler.loss_scale, flag)
+            S = scaler.loss_scale
+            if zs.zero_scaler_update(scaler, int(flag.item())):
+                zs.zero_adam_step(b["w16"], b["g16"], b["master"], b["m"], b["v"], psi, n,
+                                  rank, step=scaler.step, loss_scale=S, found_inf=flag, **hp)
+
+        def device_step():
+            zs.zero_overflow_check_dev(b["g16"], psi, n, rank, ctl)
+            zs.zero_scaler_update_dev(ctl, bias, 1)
+            zs.zero_adam_step_dev(b["w16"], b["g16"], b["master"], b["m"], b["v"], psi, n,
+                                  rank, ctl=ctl, **hp)
+
+        def per_step_ms(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) / steps * 1e3
+
+        res = {"shard_params": cnt, "host_control_ms": per_step_ms(host_step),
+               "device_control_ms": per_step_ms(device_step)}
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            device_step()
+        res["graph_replay_ms"] = per_step_ms(graph.replay)
+        c = zs.device_ctl_read(ctl)
+        if c.status != 0 or c.scaler.step != 2 * (warmup + steps):
+            raise RuntimeError(f"device-controlled steps skipped: status {c.status}, "
+                               f"t {c.scaler.step}")
+        for k in ("host_control_ms", "device_control_ms", "graph_replay_ms"):
+            res[k.replace("_ms", "_params_per_s")] = cnt / (res[k] * 1e-3)
+        out[w.name] = res
+        del graph, b
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +334,9 @@ def main():
     ap.add_argument("--extras", action="store_true",
                     help="also time the accumulate / FP32-gradient / device-control / exchange "
                          "kernels on 2^30-element shards (reported under 'extras')")
+    ap.add_argument("--small", action="store_true",
+                    help="also time whole steps of the launch-bound small workloads under host "
+                         "control, device control and HIP-graph replay (reported under 'small')")
     ap.add_argument("--control", choices=["host", "device"], default="host",
                     help="skip-or-apply decision on the host (4-byte read-back per step) or in "
                          "device memory (no read-back)")
@@ -370,6 +438,10 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
         cpu = cpu_baseline(b, w, args.cpu_seconds, args.cpu_sample)
+    small = None
+    if args.small:
+        log("[bench] small workloads ...")
+        small = measure_small(dev)
     extras = None
     if args.extras:
         del b
@@ -407,6 +479,8 @@ def main():
     }
     if extras is not None:
         out["extras"] = extras
+    if small is not None:
+        out["small"] = small
     print(json.dumps(out), flush=True)
 
 
