@@ -4,17 +4,17 @@
 // full flat buffer ("Training models too big for one GPU: ZeRO & FSDP",
 // "Data parallelism and the all-reduce").  Both are streams over HBM: the
 // reduction reads n inputs and writes one output per element, the gather
-// copies; lanes move 4 consecutive elements (8 B of 16-bit or 16 B of FP32
-// data per array) with non-temporal accesses when every view shares one
-// alignment phase, one element otherwise.
+// copies.  When every view shares one 16-B alignment phase, each lane moves
+// 16 B of every input per access (8 elements of 16-bit data, 4 of FP32) with
+// non-temporal loads and stores, one 256-lane tile per block; the few
+// elements before the first aligned address and after the last whole vector
+// are done one at a time.  Views of different phases take an element loop.
 //
 // The sum of an element is taken in FP32 over ranks 0..n-1 in order and
 // rounded once to the output format, so the result does not depend on the
 // launch shape.  Format codes: 0 FP16, 1 BF16, 2 FP32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <type_traits>
 
 #include "launch.h"
 
@@ -24,15 +24,19 @@ namespace zs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVec = 4;
+constexpr uint32_t kVecBytes = 16;  // bytes of each input a lane moves per access
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int F> struct Fmt;  // element type of a format
 template <> struct Fmt<0> { using T = uint16_t; };
 template <> struct Fmt<1> { using T = uint16_t; };
 template <> struct Fmt<2> { using T = float; };
+
+template <int F> constexpr uint32_t kBytes = F == 2 ? 4 : 2;
+template <int F> constexpr int kPerVec = static_cast<int>(kVecBytes / kBytes<F>);
 
 template <int F>
 __device__ __forceinline__ float to_f32(typename Fmt<F>::T x) {
@@ -54,9 +58,9 @@ __device__ __forceinline__ typename Fmt<F>::T from_f32(float f) {
         return f;
 }
 
-// Four consecutive elements from a 8-B (16-bit) or 16-B (FP32) aligned address.
+// kPerVec<F> consecutive elements from a 16-B aligned address.
 template <int F>
-__device__ __forceinline__ void load4(const typename Fmt<F>::T *p, float out[4]) {
+__device__ __forceinline__ void load_vec(const typename Fmt<F>::T *p, float out[kPerVec<F>]) {
     if constexpr (F == 2) {
         const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
         out[0] = x.x;
@@ -64,82 +68,121 @@ __device__ __forceinline__ void load4(const typename Fmt<F>::T *p, float out[4])
         out[2] = x.z;
         out[3] = x.w;
     } else {
-        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-        out[0] = to_f32<F>(static_cast<uint16_t>(x.x & 0xffffu));
-        out[1] = to_f32<F>(static_cast<uint16_t>(x.x >> 16));
-        out[2] = to_f32<F>(static_cast<uint16_t>(x.y & 0xffffu));
-        out[3] = to_f32<F>(static_cast<uint16_t>(x.y >> 16));
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            out[2 * j] = to_f32<F>(static_cast<uint16_t>(w[j] & 0xffffu));
+            out[2 * j + 1] = to_f32<F>(static_cast<uint16_t>(w[j] >> 16));
+        }
     }
 }
 
-template <int F>
-__device__ __forceinline__ void store4(typename Fmt<F>::T *p, const float v[4]) {
+// K values stored in format F at an address aligned to min(16, K * bytes of F).
+template <int F, int K>
+__device__ __forceinline__ void store_vec(typename Fmt<F>::T *p, const float v[K]) {
     if constexpr (F == 2) {
-        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(p));
+#pragma unroll
+        for (int h = 0; h < K / 4; ++h)
+            __builtin_nontemporal_store(f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]},
+                                        reinterpret_cast<f32x4 *>(p + 4 * h));
     } else {
-        const uint32_t a = from_f32<F>(v[0]), b = from_f32<F>(v[1]);
-        const uint32_t c = from_f32<F>(v[2]), d = from_f32<F>(v[3]);
-        __builtin_nontemporal_store(u32x2{a | (b << 16), c | (d << 16)},
-                                    reinterpret_cast<u32x2 *>(p));
+        uint32_t w[K / 2];
+#pragma unroll
+        for (int j = 0; j < K / 2; ++j)
+            w[j] = static_cast<uint32_t>(from_f32<F>(v[2 * j])) |
+                   (static_cast<uint32_t>(from_f32<F>(v[2 * j + 1])) << 16);
+        if constexpr (K == 8)
+            __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]},
+                                        reinterpret_cast<u32x4 *>(p));
+        else
+            __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2 *>(p));
     }
 }
 
 // out[i] = sum over k < n of in_k[i] for i in [0, count), where in_k already
-// points at rank r's first element of replica k.  Elements [0, head) and
-// [head + 4*n_groups, count) one at a time; in between, 4 per lane.
+// points at rank r's first element of replica k.  With n_vec > 0: vector q
+// covers elements head + q*K .. +K-1 (K = kPerVec<IN>), one 256-vector tile
+// per block, and block 0 does [0, head) and [head + n_vec*K, count) one at a
+// time.  With n_vec == 0 the whole grid walks every element.
 template <int IN, int OUT>
 __global__ __launch_bounds__(kThreads) void reduce_shard_kernel(
     typename Fmt<OUT>::T *__restrict__ out, ReplicaSet in, uint32_t n, uint64_t count,
-    uint32_t head, uint64_t n_groups) {
+    uint32_t head, uint64_t n_vec) {
     using TI = typename Fmt<IN>::T;
-    const uint64_t tid = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+    constexpr int K = kPerVec<IN>;
     auto one = [&](uint64_t i) {
         float s = 0.0f;
         for (uint32_t k = 0; k < n; ++k) s = s + to_f32<IN>(static_cast<const TI *>(in.p[k])[i]);
         out[i] = from_f32<OUT>(s);
     };
-    if (tid < head) one(tid);
-    for (uint64_t q = tid; q < n_groups; q += stride) {
-        const uint64_t e = head + q * kVec;
-        float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (uint32_t k = 0; k < n; ++k) {
-            float x[4];
-            load4<IN>(static_cast<const TI *>(in.p[k]) + e, x);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s[j] = s[j] + x[j];
-        }
-        store4<OUT>(out + e, s);
+    if (n_vec == 0) {
+        const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+        for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < count;
+             i += stride)
+            one(i);
+        return;
     }
-    for (uint64_t i = head + n_groups * kVec + tid; i < count; i += stride) one(i);
+    const uint64_t n_tiles = (n_vec + kThreads - 1) / kThreads;
+    for (uint64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        const uint64_t q = t * kThreads + threadIdx.x;
+        if (q < n_vec) {
+            const uint64_t e = head + q * K;
+            float s[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) s[j] = 0.0f;
+            for (uint32_t k = 0; k < n; ++k) {
+                float x[K];
+                load_vec<IN>(static_cast<const TI *>(in.p[k]) + e, x);
+#pragma unroll
+                for (int j = 0; j < K; ++j) s[j] = s[j] + x[j];
+            }
+            store_vec<OUT, K>(out + e, s);
+        }
+    }
+    if (blockIdx.x == 0) {
+        if (threadIdx.x < head) one(threadIdx.x);
+        const uint64_t tail = head + n_vec * K + threadIdx.x;
+        if (tail < count) one(tail);
+    }
 }
 
 // full[k*S + i] = shard_k[i] for i < count_k; blockIdx.y = k.  A shard whose
-// source and destination share an alignment phase is copied 4 elements per
-// lane after its head; otherwise one at a time.
+// source and destination share a 16-B phase is copied 16 B per lane after its
+// head (one 256-vector tile per block, block 0 doing head and tail); otherwise
+// one element at a time over the whole grid.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gather_kernel(T *__restrict__ full, GatherSet set,
                                                           uint64_t shard) {
+    constexpr uint32_t K = kVecBytes / sizeof(T);
     const uint32_t k = blockIdx.y;
     const T *__restrict__ src = static_cast<const T *>(set.p[k]);
     T *__restrict__ dst = full + static_cast<uint64_t>(k) * shard;
     const uint64_t count = set.count[k];
     const uint32_t head = set.head[k];
-    const uint64_t tid = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     if (!set.vec[k]) {
-        for (uint64_t i = tid; i < count; i += stride) dst[i] = src[i];
+        const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+        for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < count;
+             i += stride)
+            dst[i] = src[i];
         return;
     }
-    if (tid < head) dst[tid] = src[tid];
-    const uint64_t n_groups = (count - head) / kVec;
-    using V = typename std::conditional<sizeof(T) == 4, f32x4, u32x2>::type;
-    for (uint64_t q = tid; q < n_groups; q += stride) {
-        const uint64_t e = head + q * kVec;
-        __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const V *>(src + e)),
-                                    reinterpret_cast<V *>(dst + e));
+    const uint64_t n_vec = (count - head) / K;
+    const uint64_t n_tiles = (n_vec + kThreads - 1) / kThreads;
+    for (uint64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+        const uint64_t q = t * kThreads + threadIdx.x;
+        if (q < n_vec) {
+            const uint64_t e = head + q * K;
+            __builtin_nontemporal_store(
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + e)),
+                reinterpret_cast<u32x4 *>(dst + e));
+        }
     }
-    for (uint64_t i = head + n_groups * kVec + tid; i < count; i += stride) dst[i] = src[i];
+    if (blockIdx.x == 0) {
+        if (threadIdx.x < head) dst[threadIdx.x] = src[threadIdx.x];
+        const uint64_t tail = head + n_vec * K + threadIdx.x;
+        if (tail < count) dst[tail] = src[tail];
+    }
 }
 
 inline uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
@@ -150,26 +193,26 @@ inline uint32_t blocks_for(uint64_t work) {
     return static_cast<uint32_t>(b < kMaxBlocks ? b : kMaxBlocks);
 }
 
+// Elements before the first 16-B aligned address of an element-aligned view.
+inline uint32_t head_to_16(const void *p, uint32_t elem_bytes) {
+    return static_cast<uint32_t>(((kVecBytes - addr(p) % kVecBytes) % kVecBytes) / elem_bytes);
+}
+
 template <int IN, int OUT>
 hipError_t reduce_dispatch(void *out, const ReplicaSet &in, uint32_t n, uint64_t count,
                            hipStream_t stream) {
-    constexpr uint32_t in_b = IN == 2 ? 4 : 2, out_b = OUT == 2 ? 4 : 2;
-    // head that aligns the output to 4 elements; vector path if it aligns every input too
-    const uint32_t out_align = 4 * out_b;
-    uint32_t head = static_cast<uint32_t>(((out_align - addr(out) % out_align) % out_align) / out_b);
-    bool vec = true;
-    for (uint32_t k = 0; k < n; ++k)
-        if ((addr(in.p[k]) + static_cast<uint64_t>(head) * in_b) % (4 * in_b) != 0) vec = false;
-    uint64_t n_groups = 0;
-    if (!vec) {
-        head = 0;  // every element one at a time, by the grid-stride tail loop
-    } else {
-        if (head > count) head = static_cast<uint32_t>(count);  // head < 4 <= block size
-        n_groups = (count - head) / kVec;
-    }
-    const uint64_t work = n_groups > 0 ? n_groups : count;
-    reduce_shard_kernel<IN, OUT><<<blocks_for(work), kThreads, 0, stream>>>(
-        static_cast<typename Fmt<OUT>::T *>(out), in, n, count, head, n_groups);
+    constexpr uint32_t in_b = kBytes<IN>, out_b = kBytes<OUT>;
+    constexpr uint32_t K = kPerVec<IN>;
+    constexpr uint32_t out_align = K * out_b < kVecBytes ? K * out_b : kVecBytes;
+    // the head that aligns replica 0 to 16 B; vectors if it aligns every view
+    uint32_t head = head_to_16(in.p[0], in_b);
+    bool vec = head <= count && (addr(out) + static_cast<uint64_t>(head) * out_b) % out_align == 0;
+    for (uint32_t k = 0; k < n && vec; ++k)
+        if ((addr(in.p[k]) + static_cast<uint64_t>(head) * in_b) % kVecBytes != 0) vec = false;
+    const uint64_t n_vec = vec ? (count - head) / K : 0;
+    if (n_vec == 0) head = 0;  // every element one at a time
+    reduce_shard_kernel<IN, OUT><<<blocks_for(n_vec > 0 ? n_vec : count), kThreads, 0, stream>>>(
+        static_cast<typename Fmt<OUT>::T *>(out), in, n, count, head, n_vec);
     return hipGetLastError();
 }
 
@@ -188,16 +231,16 @@ hipError_t launch_reduce_shard(void *out, int out_fmt, const ReplicaSet &in, int
 
 hipError_t launch_gather_shards(void *full, int elem_bytes, GatherSet &set, uint32_t n,
                                 uint64_t shard, uint64_t max_count, hipStream_t stream) {
-    const uint32_t vec_bytes = 4 * static_cast<uint32_t>(elem_bytes);
+    const uint32_t eb = static_cast<uint32_t>(elem_bytes);
     for (uint32_t k = 0; k < n; ++k) {
         const uintptr_t s = addr(set.p[k]);
-        const uintptr_t d = addr(full) + static_cast<uint64_t>(k) * shard * elem_bytes;
-        const uint32_t head =
-            static_cast<uint32_t>(((vec_bytes - s % vec_bytes) % vec_bytes) / elem_bytes);
-        set.vec[k] = (s % vec_bytes == d % vec_bytes) && head <= set.count[k];
+        const uintptr_t d = addr(full) + static_cast<uint64_t>(k) * shard * eb;
+        const uint32_t head = head_to_16(set.p[k], eb);
+        set.vec[k] = (s % kVecBytes == d % kVecBytes) && head <= set.count[k];
         set.head[k] = set.vec[k] ? head : 0;
     }
-    const dim3 grid(blocks_for((max_count + kVec - 1) / kVec), n);
+    const uint64_t per_vec = kVecBytes / eb;
+    const dim3 grid(blocks_for((max_count + per_vec - 1) / per_vec), n);
     if (elem_bytes == 4)
         gather_kernel<float><<<grid, kThreads, 0, stream>>>(static_cast<float *>(full), set, shard);
     else
