@@ -387,6 +387,9 @@ typedef struct {
  * zero_ckpt_write -- write rank info->rank's slice: header, then count
  * 16-bit working weights and count FP32 master, m and v values (count from
  * the layout), with a 64-bit FNV-1a hash of the payload in the header.
+ * The file is written as path + ".tmp", flushed to the device and renamed
+ * over path, so a reader finds either the previous file or the complete new
+ * one; on failure the temporary file is removed.
  *   w16, master, m, v  HOST arrays of count elements.
  *   Errors: ZERO_EINVAL (bad layout, NULL pointers), ZERO_EDTYPE, ZERO_EIO.
  */

@@ -53,6 +53,27 @@ def test_empty_rank_round_trip(tmp_path):
     zs.zero_ckpt_verify(p)
 
 
+def test_overwrite_replaces_whole_file_and_failed_write_keeps_old(tmp_path):
+    psi, n, rank = 50_000, 4, 2
+    cnt = oracle.layout(psi, n, rank).count
+    p = str(tmp_path / "w.zshard")
+    first, second = state(cnt, 10), state(cnt, 11)
+    zs.zero_ckpt_write(p, psi, n, rank, "f16", zs.Scaler(1.0, step=1), *first)
+    zs.zero_ckpt_write(p, psi, n, rank, "f16", zs.Scaler(1.0, step=2), *second)
+    assert sorted(os.listdir(tmp_path)) == ["w.zshard"]        # no temporary left behind
+    assert zs.zero_ckpt_read_info(p).scaler.step == 2
+    for a, b in zip(second, zs.zero_ckpt_read(p, 0, cnt)):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    # a write that cannot create its temporary file fails and leaves the old file whole
+    os.mkdir(p + ".tmp")
+    with pytest.raises(zs.ZeroError) as e:
+        zs.zero_ckpt_write(p, psi, n, rank, "f16", zs.Scaler(1.0, step=3), *first)
+    assert e.value.code == -5
+    os.rmdir(p + ".tmp")
+    zs.zero_ckpt_verify(p)
+    assert zs.zero_ckpt_read_info(p).scaler.step == 2
+
+
 def test_integrity_errors(tmp_path):
     psi, n, rank = 10_000, 4, 1
     cnt = oracle.layout(psi, n, rank).count

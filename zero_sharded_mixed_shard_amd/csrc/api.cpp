@@ -311,7 +311,7 @@ extern "C" const char *zero_strerror(int code) {
         case ZERO_EINVAL:
             return "invalid argument";
         case ZERO_EDTYPE:
-            return "unsupported dtype (expected ZERO_F16 or ZERO_BF16)";
+            return "unsupported dtype (ZERO_F16 or ZERO_BF16; the exchanges also take ZERO_F32)";
         case ZERO_EHIP:
             return g_err[0] ? g_err : "HIP runtime error";
         case ZERO_ERANGE:

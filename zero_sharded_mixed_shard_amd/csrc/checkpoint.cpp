@@ -12,8 +12,11 @@
 //   v       count x 4 bytes
 // The header carries a 64-bit FNV-1a hash of the payload, taken over 8-byte
 // little-endian words (the last word zero-padded).
+#include <unistd.h>
+
 #include <cstdio>
 #include <cstring>
+#include <string>
 #include <vector>
 
 #include "zero_shard.h"
@@ -176,12 +179,18 @@ extern "C" int zero_ckpt_write(const char *path, const zero_ckpt_info *info, con
     hs.add(v, lay.count * 4);
     h.payload_hash = hs.finish();
 
-    FILE *f = std::fopen(path, "wb");
+    // Written beside the target, flushed to the device, then renamed over it:
+    // a reader sees either the previous file or the whole new one.
+    const std::string tmp = std::string(path) + ".tmp";
+    FILE *f = std::fopen(tmp.c_str(), "wb");
     if (f == nullptr) return ZERO_EIO;
     bool ok = write_all(f, &h, sizeof h) && write_all(f, w16, lay.count * 2) &&
               write_all(f, master, lay.count * 4) && write_all(f, m, lay.count * 4) &&
               write_all(f, v, lay.count * 4);
+    ok = ok && std::fflush(f) == 0 && fsync(fileno(f)) == 0;
     ok = (std::fclose(f) == 0) && ok;
+    if (ok && std::rename(tmp.c_str(), path) != 0) ok = false;
+    if (!ok) std::remove(tmp.c_str());
     return ok ? ZERO_OK : ZERO_EIO;
 }
 
