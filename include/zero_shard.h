@@ -446,6 +446,18 @@ int zero_ckpt_read_resharded(const char *const *paths_old, uint32_t n_old, uint6
                              float *m, float *v);
 
 /*
+ * zero_set_grid_cap -- cap the grid of every streaming kernel at `blocks`
+ * workgroups of 256 threads (0, or a value above the default, restores the
+ * default of 2^23).  A shard with more tiles than the grid has blocks is
+ * walked by each block in turn, as shards of more than 2^23 tiles always
+ * are; tests use a small cap to run those loops at small sizes.  The
+ * sum-of-squares form of the check keeps its own size-only grid, so its
+ * partial sums do not change.  Process-wide; set it while no other thread is
+ * launching.  Returns ZERO_OK.
+ */
+int zero_set_grid_cap(uint32_t blocks);
+
+/*
  * zero_strerror -- text for a return code.  For ZERO_EHIP it names the HIP
  * error of the most recent failing call made by this thread.  The pointer
  * stays valid until this thread's next call into the library.

@@ -1,0 +1,126 @@
+"""The tile loops of the streaming kernels, driven at small sizes.
+
+A shard with more tiles than the launch has blocks (beyond 2^23 blocks, about
+1.7e10 elements for the step) is walked by each block in turn.  Such shards do
+not fit in one GPU's memory with the step's five arrays, so these tests lower
+the grid cap with zero_set_grid_cap to 1, 3 and 7 blocks and check every
+kernel against the oracle at sizes of many tiles with ragged heads and tails:
+the step (vector and element-wise paths, 16-bit and FP32 gradients), the
+accumulate, the flag check and both exchanges.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import zero_sharded_mixed_shard_amd as zs
+from gpu_util import GuardedView, SENT16, assert_close, f32, log, u16
+from test_gpu_a_small import run_case
+from test_gpu_d_g32 import HP, TD, micro_batches
+from test_gpu_e_exchange import host, make_replicas
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+CAPS = (1, 3, 7)
+COUNTS = (11_017, 40_965)     # 5 and 20 step tiles, with ragged tails
+
+
+@pytest.fixture(params=CAPS)
+def cap(request):
+    zs.zero_set_grid_cap(request.param)
+    yield request.param
+    torch.cuda.synchronize()
+    zs.zero_set_grid_cap(0)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_step_tile_loop(cap, dtype):
+    for count in COUNTS:
+        for phase in (0, 3):
+            run_case(count, dtype, dict.fromkeys(("g16", "w16", "master", "m", "v"), phase),
+                     steps=2, seed=count + phase)
+        # views of different phases: the element-wise kernel's grid-stride loop
+        run_case(count, dtype, dict(g16=1, w16=2, master=0, m=3, v=1), steps=2, seed=count)
+    log(f"step {dtype} cap {cap}: within the bar")
+
+
+def test_step_g32_and_accumulate_tile_loop(cap):
+    rng = np.random.default_rng(cap)
+    for count in COUNTS:
+        for dtype in ("f16", "bf16"):
+            acc = GuardedView(count, torch.float32, 1, DEV)
+            gv = GuardedView(count, TD[dtype], 1, DEV)
+            ref_acc = np.zeros(count, np.float32)
+            for j, g in enumerate(micro_batches(count, 3, dtype, 70 + cap)):
+                gv.view.copy_(g.to(DEV))
+                zs.zero_grad_accumulate(acc.view, gv.view, count, 1, 0, first=(j == 0))
+                oracle.grad_accumulate(ref_acc, u16(g), dtype, first=(j == 0))
+            torch.cuda.synchronize()
+            assert np.array_equal(f32(acc.view).view(np.uint32), ref_acc.view(np.uint32))
+            assert acc.guards_intact() and gv.guards_intact()
+
+            V = {k: GuardedView(count, torch.float32, 2, DEV) for k in ("master", "m", "v")}
+            V["w16"] = GuardedView(count, TD[dtype], 2, DEV)
+            master0 = (rng.standard_normal(count) * 0.02).astype(np.float32)
+            V["master"].view.copy_(torch.from_numpy(master0).to(DEV))
+            for k in ("m", "v", "w16"):
+                V[k].view.zero_()
+            ref = dict(master=master0.copy(), m=np.zeros(count, np.float32),
+                       v=np.zeros(count, np.float32), w16=np.zeros(count, np.uint16))
+            G = GuardedView(count, torch.float32, 2, DEV)
+            for t in (1, 2):
+                g = (rng.standard_normal(count) * 1e-3).astype(np.float32)
+                G.view.copy_(torch.from_numpy(g).to(DEV))
+                zs.zero_adam_step_g32(V["w16"].view, G.view, V["master"].view, V["m"].view,
+                                      V["v"].view, count, 1, 0, step=t, loss_scale=1.0, **HP)
+                oracle.adam_step_g32(ref["w16"], g, ref["master"], ref["m"], ref["v"], dtype,
+                                     step=t, loss_scale=1.0, **HP)
+            torch.cuda.synchronize()
+            got = dict(master=f32(V["master"].view), m=f32(V["m"].view), v=f32(V["v"].view),
+                       w16=u16(V["w16"].view))
+            assert_close(got, ref, dtype, f"g32 cap={cap} count={count}")
+            assert all(x.guards_intact() for x in list(V.values()) + [G])
+
+
+def test_flag_tile_loop(cap):
+    count = 200_003
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    g = synth.fill_normal_(torch.empty(count, dtype=torch.float16), 1e-3, 5)
+    gv = GuardedView(count, torch.float16, 3, DEV)
+    gv.view.copy_(g.to(DEV))
+    zs.zero_overflow_check(gv.view, count, 1, 0, 1024.0, flag)
+    assert flag.item() == 0
+    for pos in (0, 1, count // 2, count - 9, count - 1):
+        bad = g.clone()
+        bad[pos] = float("nan") if pos % 2 else float("inf")
+        gv.view.copy_(bad.to(DEV))
+        zs.zero_overflow_check(gv.view, count, 1, 0, 1024.0, flag)
+        assert flag.item() == oracle.overflow_check(u16(bad), "f16", 1024.0)[0] == 1, pos
+    x = torch.zeros(count, device=DEV)
+    x[count - 1] = float("inf")
+    zs.zero_overflow_check_g32(x, count, 1, 0, 1.0, flag)
+    assert flag.item() == 1
+    assert gv.guards_intact()
+
+
+def test_exchanges_tile_loop(cap):
+    for psi, n, phase in ((50_003, 3, 0), (50_003, 3, 1), (131_077, 4, 0)):
+        reps = make_replicas(psi, n, "f16", psi + n + cap, phase)
+        hreps = [host(r) for r in reps]
+        shards = []
+        for k in range(n):
+            lay = zs.zero_shard_layout(psi, n, k)
+            out = torch.empty(lay.count + 8, dtype=torch.float16, device=DEV)[phase:phase + lay.count]
+            zs.zero_reduce_shard(out, reps, psi, n, k)
+            ref = oracle.reduce_shard(hreps, "f16", "f16", psi, n, k)
+            assert np.array_equal(u16(out), ref), (psi, n, k, phase)
+            shards.append(out)
+        full = GuardedView(zs.zero_shard_layout(psi, n, 0).padded_total, torch.float16, 0, DEV)
+        zs.zero_gather_shards(full.view, shards, psi, n)
+        got = u16(full.view)
+        want = np.zeros(psi, np.uint16)
+        oracle.gather_shards([u16(s) for s in shards], psi, n, want)
+        assert np.array_equal(got[:psi], want)
+        assert np.all(got[psi:] == SENT16) and full.guards_intact()
+    log(f"exchanges cap {cap}: bitwise")

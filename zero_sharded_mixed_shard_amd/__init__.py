@@ -74,6 +74,7 @@ from ._binding import (  # noqa: F401
     zero_reshard_plan,
     zero_scaler_update,
     zero_scaler_update_dev,
+    zero_set_grid_cap,
     zero_shard_layout,
     zero_strerror,
 )
@@ -108,4 +109,5 @@ __all__ = [
     "zero_ckpt_read",
     "zero_reshard_plan",
     "zero_ckpt_read_resharded",
+    "zero_set_grid_cap",
 ]

@@ -112,12 +112,21 @@ lib.zero_scaler_update_dev.restype = _i32
 lib.zero_adam_step_dev.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32, _u32, _f32, _f32,
                                    _f32, _f32, _f32, _vp, _vp]
 lib.zero_adam_step_dev.restype = _i32
+lib.zero_set_grid_cap.argtypes = [_u32]
+lib.zero_set_grid_cap.restype = _i32
 lib.zero_strerror.argtypes = [_i32]
 lib.zero_strerror.restype = ctypes.c_char_p
 
 
 def zero_strerror(code: int) -> str:
     return lib.zero_strerror(code).decode()
+
+
+def zero_set_grid_cap(blocks: int) -> None:
+    """Cap every streaming kernel's grid at `blocks` workgroups (0 restores the default)."""
+    if not 0 <= blocks < 1 << 32:
+        raise ValueError("blocks must fit in 32 bits")
+    lib.zero_set_grid_cap(blocks)
 
 
 @dataclass(frozen=True)

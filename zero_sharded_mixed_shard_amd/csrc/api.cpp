@@ -46,6 +46,8 @@ int device_cus(int *cus) {
     return ZERO_OK;
 }
 
+std::atomic<uint64_t> g_grid_cap{zs::kMaxBlocks};
+
 bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 bool finite(float x) { return std::isfinite(x); }
@@ -102,6 +104,14 @@ int step_args(void *w16, const void *g, uintptr_t g_align, float *master, float 
 }
 
 }  // namespace
+
+uint64_t zs::max_blocks() { return g_grid_cap.load(std::memory_order_relaxed); }
+
+extern "C" int zero_set_grid_cap(uint32_t blocks) {
+    g_grid_cap.store(blocks == 0 || blocks > zs::kMaxBlocks ? zs::kMaxBlocks : blocks,
+                     std::memory_order_relaxed);
+    return ZERO_OK;
+}
 
 extern "C" int zero_overflow_check(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n,
                                    uint32_t rank, float loss_scale, int32_t *d_found_inf,

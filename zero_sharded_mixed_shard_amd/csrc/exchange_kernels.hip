@@ -190,7 +190,8 @@ inline uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 inline uint32_t blocks_for(uint64_t work) {
     uint64_t b = (work + kThreads - 1) / kThreads;
     if (b == 0) b = 1;
-    return static_cast<uint32_t>(b < kMaxBlocks ? b : kMaxBlocks);
+    const uint64_t cap = max_blocks();
+    return static_cast<uint32_t>(b < cap ? b : cap);
 }
 
 // Elements before the first 16-B aligned address of an element-aligned view.

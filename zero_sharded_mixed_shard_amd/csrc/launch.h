@@ -28,6 +28,10 @@ struct AdamScalars {
 // Larger shards loop over tiles.
 constexpr uint64_t kMaxBlocks = 1ull << 23;
 
+// The grid cap in force: kMaxBlocks, or the lower cap set by
+// zero_set_grid_cap (tests use it to run the tile loops at small sizes).
+uint64_t max_blocks();
+
 // Enqueue the Adam step over `count` elements of five shard views.  The
 // caller has validated every argument; count > 0.  flag (nullable): skip if
 // set.  ctl (nullable): skip unless ctl->apply, and take S, bc1, bc2 from it.

@@ -524,7 +524,8 @@ bool common_phase(const float *ref, const float *a, const float *b, const GT *g,
 
 inline uint32_t grid_for(uint64_t need) {
     if (need == 0) need = 1;
-    return static_cast<uint32_t>(need < kMaxBlocks ? need : kMaxBlocks);
+    const uint64_t cap = max_blocks();
+    return static_cast<uint32_t>(need < cap ? need : cap);
 }
 
 template <int DT, typename GT>
@@ -586,8 +587,8 @@ CheckGrid check_grid(const GT *g, uint64_t count, bool sumsq, int num_cus) {
     uint64_t need = c.n_vec > 0 ? (c.n_vec + per_block - 1) / per_block
                                 : (rest + kThreads - 1) / kThreads;
     if (need == 0) need = 1;
-    const uint64_t cap = sumsq ? kSumsqPartials
-                               : static_cast<uint64_t>(num_cus) * kCheckBlocksPerCU;
+    uint64_t cap = sumsq ? kSumsqPartials : static_cast<uint64_t>(num_cus) * kCheckBlocksPerCU;
+    if (!sumsq && cap > max_blocks()) cap = max_blocks();  // the partials' grid stays fixed
     c.blocks = static_cast<uint32_t>(need < cap ? need : cap);
     return c;
 }
