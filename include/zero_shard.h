@@ -23,16 +23,17 @@
  *     count is the layout's count for (psi, n, rank).  The padding of a short
  *     last shard and anything past count are never touched.
  *   - Any element-aligned pointer is accepted (4 bytes for FP32 arrays, 2
- *     for 16-bit ones).  The fast 16-byte vector path runs when one head of
- *     h < 4 elements brings all five views to 16-byte (FP32) and 8-byte
- *     (16-bit) alignment, which holds whenever all views sit at the same
- *     element offset into 16-byte-aligned buffers.  Otherwise a slower
- *     element-wise kernel gives the same results.
+ *     for 16-bit ones).  The kernels do a head of h < 32 elements one at a
+ *     time, h bringing the FP32 master view to a 128-byte line, and stream
+ *     the rest in vectors when at element h every FP32 view is 16-byte and
+ *     every 16-bit view 8-byte aligned.  That holds whenever all views sit at
+ *     the same element offset into 16-byte-aligned buffers.  Otherwise a
+ *     slower element-wise kernel gives the same results.
  *   - All device work is enqueued on `stream` (a hipStream_t; 0 = the null
  *     stream) of the current HIP device, and the call returns without
  *     synchronising.  Calls are thread-safe: the library has no mutable
  *     state shared between calls other than a per-device cache of the
- *     compute-unit count.
+ *     compute-unit count and the grid cap of zero_set_grid_cap.
  */
 #ifndef ZERO_SHARD_H_
 #define ZERO_SHARD_H_

@@ -63,6 +63,14 @@ class GuardedView:
         return bool(np.all(before == want) and np.all(after == want))
 
 
+def line_head(phase: int, elem_bytes: int, line: int = 128) -> int:
+    """Elements a kernel does one at a time before the first cache-line boundary
+    of a GuardedView at `phase` (its view starts phase + GUARD elements into a
+    256-B aligned allocation)."""
+    start = (phase + GUARD) * elem_bytes
+    return ((line - start % line) % line) // elem_bytes
+
+
 def assert_close(gpu: dict, ref: dict, dtype: str, what: str = "") -> dict:
     """Apply the parity bar to host copies {master, m, v, w16}; return statistics."""
     stats = {}

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 import zero_sharded_mixed_shard_amd as zs
-from gpu_util import (GuardedView, assert_close, f32, log, u16)
+from gpu_util import (GuardedView, assert_close, f32, line_head, log, u16)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -208,10 +208,10 @@ def test_overflow_flag_positions_and_phases(dtype):
     for count in (1, 7, 8, 9, 17, 4096 * 8 + 3, 300001):
         x = (rng.standard_normal(count) * 1e-3).astype(np.float32)
         bits = oracle.encode16(x, dtype)
-        for phase in range(8):
+        for phase in (0, 1, 2, 3, 5, 7, 39, 40):
             assert check_case(bits, dtype, phase, 1.0)[0] == 0
-            head = (8 - phase) % 8
-            cand = {0, head, head - 1, count // 2, count - 1, count - 8}
+            head = line_head(phase, 2)   # first element of the vector part
+            cand = {0, head, head - 1, head + 1, count // 2, count - 1, count - 8}
             for pos in sorted(p for p in cand if 0 <= p < count):
                 for bad in BAD[dtype]:
                     b = bits.copy()

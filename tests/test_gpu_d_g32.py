@@ -10,7 +10,7 @@ import torch
 import oracle
 import synth
 import zero_sharded_mixed_shard_amd as zs
-from gpu_util import GuardedView, assert_close, f32, log, u16
+from gpu_util import GuardedView, assert_close, f32, line_head, log, u16
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -59,8 +59,9 @@ def test_check_g32_matches_oracle(phase):
             rf, rs = oracle.overflow_check_g32(x, S)
             assert flag.item() == rf == 0
             assert oracle.ulp_distance32(np.float32(s.item()), np.float32(rs)).max() <= 1
-        head = (4 - phase) % 4
-        for pos in sorted({p for p in (0, head, count // 2, count - 1) if 0 <= p < count}):
+        head = line_head(phase, 4)   # first element of the vector part
+        for pos in sorted({p for p in (0, head - 1, head, count // 2, count - 1)
+                           if 0 <= p < count}):
             for bad in (np.inf, -np.inf, np.nan):
                 y = x.copy()
                 y[pos] = bad

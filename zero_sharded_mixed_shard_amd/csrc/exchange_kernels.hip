@@ -7,8 +7,9 @@
 // copies.  When every view shares one 16-B alignment phase, each lane moves
 // 16 B of every input per access (8 elements of 16-bit data, 4 of FP32) with
 // non-temporal loads and stores, one 256-lane tile per block; the few
-// elements before the first aligned address and after the last whole vector
-// are done one at a time.  Views of different phases take an element loop.
+// elements before the first cache-line boundary and after the last whole
+// vector are done one at a time.  Views of different phases take an element
+// loop.
 //
 // The sum of an element is taken in FP32 over ranks 0..n-1 in order and
 // rounded once to the output format, so the result does not depend on the
@@ -194,9 +195,12 @@ inline uint32_t blocks_for(uint64_t work) {
     return static_cast<uint32_t>(b < cap ? b : cap);
 }
 
-// Elements before the first 16-B aligned address of an element-aligned view.
-inline uint32_t head_to_16(const void *p, uint32_t elem_bytes) {
-    return static_cast<uint32_t>(((kVecBytes - addr(p) % kVecBytes) % kVecBytes) / elem_bytes);
+// Elements before the first cache-line (128-B) boundary of an element-aligned
+// view.  Vector parts start there, so each wave's accesses cover whole lines;
+// it is also 16-B aligned.
+constexpr uint32_t kLine = 128;
+inline uint32_t head_to_line(const void *p, uint32_t elem_bytes) {
+    return static_cast<uint32_t>(((kLine - addr(p) % kLine) % kLine) / elem_bytes);
 }
 
 template <int IN, int OUT>
@@ -205,8 +209,9 @@ hipError_t reduce_dispatch(void *out, const ReplicaSet &in, uint32_t n, uint64_t
     constexpr uint32_t in_b = kBytes<IN>, out_b = kBytes<OUT>;
     constexpr uint32_t K = kPerVec<IN>;
     constexpr uint32_t out_align = K * out_b < kVecBytes ? K * out_b : kVecBytes;
-    // the head that aligns replica 0 to 16 B; vectors if it aligns every view
-    uint32_t head = head_to_16(in.p[0], in_b);
+    // the head that puts replica 0 on a line; vectors if every view is then
+    // aligned for its accesses
+    uint32_t head = head_to_line(in.p[0], in_b);
     bool vec = head <= count && (addr(out) + static_cast<uint64_t>(head) * out_b) % out_align == 0;
     for (uint32_t k = 0; k < n && vec; ++k)
         if ((addr(in.p[k]) + static_cast<uint64_t>(head) * in_b) % kVecBytes != 0) vec = false;
@@ -236,7 +241,9 @@ hipError_t launch_gather_shards(void *full, int elem_bytes, GatherSet &set, uint
     for (uint32_t k = 0; k < n; ++k) {
         const uintptr_t s = addr(set.p[k]);
         const uintptr_t d = addr(full) + static_cast<uint64_t>(k) * shard * eb;
-        const uint32_t head = head_to_16(set.p[k], eb);
+        // the head that puts the destination on a line (the source shares its 16-B phase)
+        const uint32_t head =
+            static_cast<uint32_t>(((kLine - d % kLine) % kLine) / eb);
         set.vec[k] = (s % kVecBytes == d % kVecBytes) && head <= set.count[k];
         set.head[k] = set.vec[k] ? head : 0;
     }

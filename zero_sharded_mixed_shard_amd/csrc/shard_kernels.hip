@@ -509,13 +509,21 @@ inline uint32_t align_head(uintptr_t a, uint32_t elem_bytes, uint32_t align) {
     return mis == 0 ? 0u : static_cast<uint32_t>((align - mis) / elem_bytes);
 }
 
-// Head that aligns the FP32 reference array to 16 B, and whether it also
-// aligns every other view: FP32 arrays (a, b, FP32 gradients) to 16 B and
-// 16-bit arrays (16-bit gradients, h16) to 8 B.  b and h16 may be null.
+// Bytes of a cache line: vector parts start on one, so every wave's 1 KB (FP32)
+// or 512 B (16-bit) access covers whole lines.  A view that starts mid-line
+// otherwise costs about a fifth of the bandwidth (partial first and last line
+// of every access).
+constexpr uint32_t kLine = 128;
+
+// Head that aligns the FP32 reference array to a cache line, and whether it
+// also leaves every other view vector-aligned: FP32 arrays (a, b, FP32
+// gradients) at 16 B and 16-bit arrays (16-bit gradients, h16) at 8 B.  The
+// head is congruent mod 4 to the one that aligns ref to 16 B, so the test is
+// the same as for a 16-B head.  b and h16 may be null.
 template <typename GT>
 bool common_phase(const float *ref, const float *a, const float *b, const GT *g,
                   const uint16_t *h16, uint32_t *head) {
-    *head = align_head(addr(ref), 4, 16);
+    *head = align_head(addr(ref), 4, kLine);
     const bool g_ok = sizeof(GT) == 2 ? (addr(g) + 2u * *head) % 8 == 0
                                       : addr(g) % 16 == addr(ref) % 16;
     return addr(a) % 16 == addr(ref) % 16 && (b == nullptr || addr(b) % 16 == addr(ref) % 16) &&
@@ -568,7 +576,7 @@ hipError_t accumulate_dispatch(float *acc, const uint16_t *g16, uint64_t count,
 }
 
 struct CheckGrid {
-    uint32_t head;    // elements done one at a time before the first 16-B vector
+    uint32_t head;    // elements done one at a time before the first line-aligned vector
     uint64_t n_vec;   // 16-B vectors
     uint32_t blocks;  // grid size (with a sum of squares: the number of partials)
 };
@@ -579,7 +587,7 @@ struct CheckGrid {
 template <typename GT, int DT>
 CheckGrid check_grid(const GT *g, uint64_t count, bool sumsq, int num_cus) {
     CheckGrid c;
-    c.head = align_head(addr(g), sizeof(GT), 16);
+    c.head = align_head(addr(g), sizeof(GT), kLine);
     if (c.head > count) c.head = static_cast<uint32_t>(count);
     c.n_vec = (count - c.head) / GradBits<GT, DT>::kPerVec;
     const uint64_t rest = count - c.head - GradBits<GT, DT>::kPerVec * c.n_vec;
