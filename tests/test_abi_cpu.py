@@ -336,3 +336,8 @@ def test_exchange_argument_errors():
     assert L.zero_gather_shards(FAKE, arr, 0, 100, 65, None) == -1
     # the 16-bit-only entry points reject FP32
     assert L.zero_overflow_check(FAKE, 2, 100, 4, 0, 1.0, FAKE, None, None, None) == -2
+
+
+def test_short_layout_name_is_the_same_call():
+    for psi, n, rank in ((10, 8, 5), (1_000_003, 8, 7), (8_810_000_003, 64, 63)):
+        assert zs.layout(psi, n, rank) == zs.zero_shard_layout(psi, n, rank)

@@ -249,3 +249,32 @@ def test_overflow_check_of_empty_rank_clears_outputs():
     zs.zero_overflow_check(empty, 10, 8, 6, 1.0, flag, s, parts)
     torch.cuda.synchronize()
     assert flag.item() == 0 and s.item() == 0.0
+
+
+def test_short_names_match_the_entry_points():
+    # adam_step(betas=...) and overflow_check(sumsq=...) without partials are the
+    # same calls as zero_adam_step / zero_overflow_check
+    count, psi, n, rank = 70_001, 560_008, 8, 7
+    g = synth.fill_normal_(torch.empty(count, dtype=torch.float16), 1e-3, 61).to(DEV)
+    master0 = synth.fill_normal_(torch.empty(count), 0.02, 62).to(DEV)
+    A = dict(master=master0.clone(), m=torch.zeros(count, device=DEV),
+             v=torch.zeros(count, device=DEV), w16=torch.zeros(count, dtype=torch.float16, device=DEV))
+    B = {k: t.clone() for k, t in A.items()}
+    for t in (1, 2):
+        zs.adam_step(A["w16"], g, A["master"], A["m"], A["v"], psi, n, rank, lr=1e-3,
+                     betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step=t, loss_scale=4.0)
+        zs.zero_adam_step(B["w16"], g, B["master"], B["m"], B["v"], psi, n, rank, lr=1e-3,
+                          beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=t,
+                          loss_scale=4.0)
+    torch.cuda.synchronize()
+    for k in A:
+        assert torch.equal(A[k].view(torch.int16 if A[k].dtype == torch.float16 else torch.int32),
+                           B[k].view(torch.int16 if B[k].dtype == torch.float16 else torch.int32)), k
+    f1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    f2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    s1, s2 = torch.zeros(1, device=DEV), torch.zeros(1, device=DEV)
+    parts = torch.empty(zs.SUMSQ_PARTIALS, dtype=torch.float64, device=DEV)
+    zs.overflow_check(g, psi, n, rank, 4.0, f1, sumsq=s1)
+    zs.zero_overflow_check(g, psi, n, rank, 4.0, f2, s2, parts)
+    torch.cuda.synchronize()
+    assert f1.item() == f2.item() == 0 and s1.item() == s2.item() > 0

@@ -15,6 +15,10 @@ Functions carry the names of the C entry points (include/zero_shard.h):
     zero_scaler_update(state: Scaler, found_inf) -> bool   (skip-or-apply, loss scale)
     zero_strerror(code) -> str
 
+and under short names: layout(psi, n, rank); overflow_check(g16, psi, n, rank,
+loss_scale, found_inf, sumsq=None); adam_step(..., lr, betas=(b1, b2), eps,
+weight_decay, step, loss_scale, found_inf=None).
+
 FP32 gradients (accumulated across micro-batches):
 
     zero_grad_accumulate(acc32, g16, psi, n, rank, first)
@@ -51,7 +55,10 @@ from ._binding import (  # noqa: F401
     Layout,
     Scaler,
     ZeroError,
+    adam_step,
+    layout,
     lib,
+    overflow_check,
     device_ctl_new,
     device_ctl_read,
     zero_adam_step,
@@ -110,4 +117,7 @@ __all__ = [
     "zero_reshard_plan",
     "zero_ckpt_read_resharded",
     "zero_set_grid_cap",
+    "layout",
+    "overflow_check",
+    "adam_step",
 ]

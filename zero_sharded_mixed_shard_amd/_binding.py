@@ -223,6 +223,34 @@ def zero_adam_step(w16: torch.Tensor, g16: torch.Tensor, master: torch.Tensor, m
         raise ZeroError(rc, "zero_adam_step")
 
 
+# ---- short names of the three path calls ----------------------------------------
+
+def layout(psi: int, n: int, rank: int) -> Layout:
+    """zero_shard_layout under its short name."""
+    return zero_shard_layout(psi, n, rank)
+
+
+def overflow_check(g16: torch.Tensor, psi: int, n: int, rank: int, loss_scale: float,
+                   found_inf: torch.Tensor, sumsq: torch.Tensor | None = None,
+                   partials: torch.Tensor | None = None, stream=None) -> None:
+    """zero_overflow_check under its short name; with `sumsq` and no `partials`, the
+    partial-sum buffer is taken from torch's allocator for this call."""
+    if sumsq is not None and partials is None:
+        partials = torch.empty(SUMSQ_PARTIALS, dtype=torch.float64, device=g16.device)
+    zero_overflow_check(g16, psi, n, rank, loss_scale, found_inf, sumsq, partials, stream)
+
+
+def adam_step(w16: torch.Tensor, g16: torch.Tensor, master: torch.Tensor, m: torch.Tensor,
+              v: torch.Tensor, psi: int, n: int, rank: int, *, lr: float, betas, eps: float,
+              weight_decay: float, step: int, loss_scale: float,
+              found_inf: torch.Tensor | None = None, stream=None) -> None:
+    """zero_adam_step under its short name, with the two betas as one pair."""
+    beta1, beta2 = betas
+    zero_adam_step(w16, g16, master, m, v, psi, n, rank, lr=lr, beta1=beta1, beta2=beta2,
+                   eps=eps, weight_decay=weight_decay, step=step, loss_scale=loss_scale,
+                   found_inf=found_inf, stream=stream)
+
+
 def zero_scaler_update(state: Scaler, found_inf: int) -> bool:
     """Skip-or-apply decision; returns True when the update must run (see the header)."""
     apply = ctypes.c_int32(0)
