@@ -12,6 +12,7 @@ import re
 import subprocess
 import tempfile
 
+import numpy as np
 import pytest
 
 import oracle
@@ -341,3 +342,58 @@ def test_exchange_argument_errors():
 def test_short_layout_name_is_the_same_call():
     for psi, n, rank in ((10, 8, 5), (1_000_003, 8, 7), (8_810_000_003, 64, 63)):
         assert zs.layout(psi, n, rank) == zs.zero_shard_layout(psi, n, rank)
+
+
+def test_plain_c_client_links_and_calls_the_host_entry_points():
+    # A C99 program with every warning an error, linked against the library,
+    # drives the host-side entry points with no Python in between.
+    src = r"""
+    #include <inttypes.h>
+    #include <stdio.h>
+    #include <string.h>
+    #include "zero_shard.h"
+    int main(void) {
+      zero_layout lay;
+      if (zero_shard_layout(8810000003ULL, 64, 63, &lay) != ZERO_OK) return 1;
+      printf("%" PRIu64 " %" PRIu64 " %" PRIu64 " %" PRIu64 "\n", lay.shard, lay.offset,
+             lay.count, lay.pad);
+      if (zero_shard_layout(10, 0, 0, &lay) != ZERO_EINVAL) return 2;
+      zero_scaler sc;
+      memset(&sc, 0, sizeof sc);
+      sc.loss_scale = 65536.0f;
+      sc.growth_interval = 2000;
+      int32_t apply = -1;
+      if (zero_scaler_update(&sc, 1, &apply) != ZERO_OK) return 3;
+      printf("%d %g %" PRIu64 "\n", (int)apply, (double)sc.loss_scale, sc.step);
+      if (zero_scaler_update(&sc, 0, &apply) != ZERO_OK) return 4;
+      printf("%d %g %" PRIu64 "\n", (int)apply, (double)sc.loss_scale, sc.step);
+      zero_comm c;
+      if (zero_comm_volume(8810000003ULL, 64, 3, 2, &c) != ZERO_OK) return 5;
+      printf("%u %" PRIu64 "\n", c.collectives, c.elements);
+      float bc[4];
+      if (zero_bias_corrections(0.9f, 0.999f, 1, 2, bc) != ZERO_OK) return 6;
+      printf("%.9g %.9g %.9g %.9g\n", (double)bc[0], (double)bc[1], (double)bc[2],
+             (double)bc[3]);
+      printf("%s\n", zero_strerror(ZERO_EINVAL));
+      return 0;
+    }
+    """
+    lib_dir = os.path.dirname(zs.LIB_PATH)
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "client.c")
+        exe = os.path.join(d, "client")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", os.path.dirname(HEADER), c, "-o", exe, "-L", lib_dir,
+                        "-lzero_shard", f"-Wl,-rpath,{lib_dir}"], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    lay = oracle.layout(8_810_000_003, 64, 63)
+    assert out[0].split() == [str(lay.shard), str(lay.offset), str(lay.count), str(lay.pad)]
+    assert out[1].split() == ["0", "32768", "0"]       # overflow: skip, S halves, t unchanged
+    assert out[2].split() == ["1", "32768", "1"]       # clean: apply, t = 1
+    assert out[3].split() == ["3", str(3 * 8_810_000_003)]
+    b = [np.float32(x) for x in out[4].split()]        # %.9g round-trips FP32 exactly
+    # 1 - beta^t with the FP32 beta widened to FP64, rounded once to FP32
+    want = [np.float32(1.0 - float(np.float32(beta)) ** t) for beta in (0.9, 0.999) for t in (1, 2)]
+    assert b == want
+    assert out[5] == "invalid argument"
