@@ -23,6 +23,7 @@ import argparse
 import importlib.util
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -474,6 +475,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic},
         "kernels": {"adam_step_ms": avg_step_ms, "adam_step_ms_min": min(step_ms),
+                    "adam_step_ms_median": statistics.median(step_ms),
                     "overflow_check_ms": avg_check_ms,
                     "overflow_check_GBps": CHECK_BYTES_PER_PARAM * cnt / (avg_check_ms * 1e-3)
                     / 1e9,
