@@ -208,7 +208,3 @@ WORKLOADS = {
 def to_numpy_u16(t: torch.Tensor) -> np.ndarray:
     """Host copy of a 16-bit tensor as raw uint16 bit patterns."""
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16).copy()
-
-
-def to_numpy_f32(t: torch.Tensor) -> np.ndarray:
-    return t.detach().cpu().numpy().astype(np.float32, copy=True)
