@@ -322,6 +322,75 @@ def measure_small(dev, steps: int = 300, warmup: int = 20) -> dict:
     return out
 
 
+def measure_checkpoint(n_elem: int = 1 << 26) -> dict:
+    """Host throughput of the sharded checkpoint calls on two ranks' shards.
+
+    psi = 2 * n_elem over N = 2: each rank's file holds n_elem elements (14 B
+    each plus a 128-B header).  Timed, each twice (first and repeat): writing
+    both files (temporary file, fsync, rename), verifying both payload hashes,
+    reading one shard back, and reading rank 1 of a 3-rank layout from the two
+    files.  Beside them, the same bytes written with numpy's tofile plus fsync
+    and read back with fromfile: the file system's practical rate."""
+    import tempfile
+
+    import numpy as np
+
+    import zero_sharded_mixed_shard_amd as zs
+
+    n_old, n_new = 2, 3
+    psi = n_old * n_elem
+    rng = np.random.default_rng(7)
+    shards = [(rng.integers(0, 1 << 16, n_elem, dtype=np.uint16),
+               rng.standard_normal(n_elem, dtype=np.float32),
+               rng.standard_normal(n_elem, dtype=np.float32),
+               rng.random(n_elem, dtype=np.float32)) for _ in range(n_old)]
+    file_bytes = 14 * n_elem + 128
+    out = {"elements_per_shard": n_elem, "file_bytes": file_bytes}
+
+    def timed(key, nbytes, fn):
+        """Run fn twice; the first call after a write can wait on the file system."""
+        rates = []
+        for _ in range(2):
+            t0 = time.perf_counter()
+            fn()
+            rates.append(nbytes / (time.perf_counter() - t0) / 1e9)
+        out[key + "_GBps"] = rates[0]
+        out[key + "_repeat_GBps"] = rates[1]
+
+    def write_plain(path):
+        with open(path, "wb") as f:
+            for r in range(n_old):
+                for a in shards[r]:
+                    a.tofile(f)
+            f.flush()
+            os.fsync(f.fileno())
+
+    def read_plain(path):
+        with open(path, "rb") as f:
+            for dt in (np.uint16, np.float32, np.float32, np.float32):
+                np.fromfile(f, dtype=dt, count=n_elem)
+
+    with tempfile.TemporaryDirectory(dir=os.environ.get("TMPDIR")) as d:
+        paths = [os.path.join(d, f"rank{r}.zshard") for r in range(n_old)]
+        timed("write", n_old * file_bytes, lambda: [
+            zs.zero_ckpt_write(paths[r], psi, n_old, r, "f16", zs.Scaler(65536.0, step=10),
+                               *shards[r]) for r in range(n_old)])
+        timed("verify", n_old * file_bytes, lambda: [zs.zero_ckpt_verify(p) for p in paths])
+        timed("read", 14 * n_elem, lambda: zs.zero_ckpt_read(paths[0], 0, n_elem))
+        back = zs.zero_ckpt_read(paths[0], 0, n_elem)
+        if not all(np.array_equal(a.view(np.uint8), b.view(np.uint8))
+                   for a, b in zip(back, shards[0])):
+            raise RuntimeError("checkpoint read-back differs from what was written")
+        del back
+        cnt_new = zs.zero_shard_layout(psi, n_new, 1).count
+        timed("read_resharded", 14 * cnt_new,
+              lambda: zs.zero_ckpt_read_resharded(paths, psi, n_new, 1))
+        plain = os.path.join(d, "plain.bin")
+        timed("plain_write", n_old * 14 * n_elem, lambda: write_plain(plain))
+        timed("plain_read", 14 * n_elem, lambda: read_plain(plain))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -341,6 +410,9 @@ def main():
     ap.add_argument("--small", action="store_true",
                     help="also time whole steps of the launch-bound small workloads under host "
                          "control, device control and HIP-graph replay (reported under 'small')")
+    ap.add_argument("--ckpt", action="store_true",
+                    help="also time the sharded checkpoint calls on two 2^26-element shard "
+                         "files (reported under 'checkpoint')")
     ap.add_argument("--control", choices=["host", "device"], default="host",
                     help="skip-or-apply decision on the host (4-byte read-back per step) or in "
                          "device memory (no read-back)")
@@ -442,6 +514,10 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
         cpu = cpu_baseline(b, w, args.cpu_seconds, args.cpu_sample)
+    ckpt = None
+    if args.ckpt:
+        log("[bench] checkpoint files ...")
+        ckpt = measure_checkpoint()
     small = None
     if args.small:
         log("[bench] small workloads ...")
@@ -486,6 +562,8 @@ def main():
         out["extras"] = extras
     if small is not None:
         out["small"] = small
+    if ckpt is not None:
+        out["checkpoint"] = ckpt
     print(json.dumps(out), flush=True)
 
 
