@@ -385,9 +385,17 @@ typedef struct {
 } zero_ckpt_info;
 
 /*
- * zero_ckpt_write -- write rank info->rank's slice: header, then count
- * 16-bit working weights and count FP32 master, m and v values (count from
- * the layout), with a 64-bit FNV-1a hash of the payload in the header.
+ * zero_ckpt_write -- write rank info->rank's slice: a 128-byte header, then
+ * count 16-bit working weights and count FP32 master, m and v values (count
+ * from the layout), little-endian.  Header (byte offset: field): 0 magic
+ * "ZSHARD01", 8 version (u32, 2), 12 dtype (u32), 16 psi (u64), 24 n (u32),
+ * 28 rank (u32), 32 offset (u64), 40 count (u64), 48 step (u64), 56
+ * clean_steps (u64), 64 loss_scale (f32), 68 growth_interval (u32), 72
+ * payload bytes (u64), 80 payload hash (u64), then zeros.  The hash reads
+ * the payload as 8-byte little-endian words (the last zero-padded), folds
+ * word i into lane i mod 4 by FNV-1a (h = (h ^ w) * 0x100000001b3, each lane
+ * starting at 0xcbf29ce484222325), then folds the four lanes, lane 0 first,
+ * into one more FNV-1a state from the same start.
  * The file is written as path + ".tmp", flushed to the device and renamed
  * over path, so a reader finds either the previous file or the complete new
  * one; on failure the temporary file is removed.

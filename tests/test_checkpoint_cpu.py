@@ -3,6 +3,7 @@ plan against brute force, resharded reads, and resume invariance with the
 oracle (N shards -> save -> N' shards -> continue equals the unsharded run).
 """
 import os
+import struct
 
 import numpy as np
 import pytest
@@ -72,6 +73,40 @@ def test_overwrite_replaces_whole_file_and_failed_write_keeps_old(tmp_path):
     os.rmdir(p + ".tmp")
     zs.zero_ckpt_verify(p)
     assert zs.zero_ckpt_read_info(p).scaler.step == 2
+
+
+def payload_hash(payload: bytes) -> int:
+    """The file's payload hash from its definition: FNV-1a over 8-byte little-endian
+    words in four lanes (word i to lane i mod 4), the lanes then folded in order."""
+    mask, prime, start = (1 << 64) - 1, 0x100000001B3, 0xCBF29CE484222325
+    padded = payload + b"\0" * (-len(payload) % 8)
+    words = np.frombuffer(padded, dtype="<u8")
+    lanes = [start] * 4
+    for i, w in enumerate(words.tolist()):
+        lanes[i % 4] = ((lanes[i % 4] ^ w) * prime) & mask
+    h = start
+    for x in lanes:
+        h = ((h ^ x) * prime) & mask
+    return h
+
+
+@pytest.mark.parametrize("psi,n,rank", [(1_000, 4, 1), (1_003, 4, 3), (9, 8, 3), (10, 8, 6)])
+def test_file_format_and_hash_follow_their_definition(tmp_path, psi, n, rank):
+    # counts 250, 250, 2 and 0 elements: payloads of 3500, 3500, 28 and 0 bytes
+    lay = oracle.layout(psi, n, rank)
+    st = state(lay.count, psi + rank)
+    p = str(tmp_path / "f.zshard")
+    zs.zero_ckpt_write(p, psi, n, rank, "bf16", zs.Scaler(512.0, growth_interval=9, step=4), *st)
+    raw = open(p, "rb").read()
+    hdr, payload = raw[:128], raw[128:]
+    assert hdr[:8] == b"ZSHARD01"
+    version, dtype, psi_, n_, rank_, off, cnt, step, clean = struct.unpack_from("<IIQIIQQQQ", hdr, 8)
+    scale, growth, nbytes, h = struct.unpack_from("<fIQQ", hdr, 64)
+    assert (version, dtype, psi_, n_, rank_, off, cnt, step, clean) == \
+        (2, 1, psi, n, rank, lay.offset, lay.count, 4, 0)
+    assert (scale, growth, nbytes) == (512.0, 9, 14 * lay.count) and hdr[88:] == bytes(40)
+    assert payload == b"".join(a.tobytes() for a in st)
+    assert h == payload_hash(payload)
 
 
 def test_integrity_errors(tmp_path):
