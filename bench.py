@@ -188,7 +188,8 @@ def measure_extras(dev, n_elem: int = 1 << 30, reps: int = 5) -> dict:
     """Bandwidth of the path's other kernels on n_elem-element shards (HIP events).
 
     Algorithmic bytes per element: accumulate 10 (read 2 + 4, write 4), FP32
-    check 4, FP32-gradient step 30, reduce of 8 FP16 replicas into FP16 18 (read
+    check 4, 16-bit check with the sum of squares 2 (S a power of two, and S = 3),
+    FP32-gradient step 30, reduce of 8 FP16 replicas into FP16 18 (read
     8 x 2, write 2), gather of 8 FP16 shards 4 (read 2, write 2), and the
     device-controlled check + decision + step 30 (2 + 28)."""
     import torch
@@ -225,6 +226,12 @@ def measure_extras(dev, n_elem: int = 1 << 30, reps: int = 5) -> dict:
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     record("overflow_check_g32", timed(lambda: zs.zero_overflow_check_g32(acc, n, 1, 0, 65536.0,
                                                                           flag)), n, 4)
+    sumsq = torch.zeros(1, device=dev)
+    parts = torch.empty(zs.SUMSQ_PARTIALS, dtype=torch.float64, device=dev)
+    record("overflow_check_sumsq_f16", timed(lambda: zs.zero_overflow_check(
+        g16, n, 1, 0, 65536.0, flag, sumsq, parts)), n, 2)
+    record("overflow_check_sumsq_f16_S3", timed(lambda: zs.zero_overflow_check(
+        g16, n, 1, 0, 3.0, flag, sumsq, parts)), n, 2)
     master = synth.fill_normal_(torch.empty(n, device=dev), 0.02, 2)
     m = torch.zeros(n, device=dev)
     v = torch.zeros(n, device=dev)

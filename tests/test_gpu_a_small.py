@@ -278,3 +278,20 @@ def test_short_names_match_the_entry_points():
     zs.zero_overflow_check(g, psi, n, rank, 4.0, f2, s2, parts)
     torch.cuda.synchronize()
     assert f1.item() == f2.item() == 0 and s1.item() == s2.item() > 0
+
+
+def test_sumsq_power_of_two_scales_and_their_edges():
+    # S a power of two with a normal reciprocal takes the multiply path; the
+    # others (non-powers, subnormal S, reciprocal below the normal range)
+    # divide.  Flag and sum of squares agree with the oracle on both sides.
+    rng = np.random.default_rng(8)
+    count = 50_021
+    x = (rng.standard_normal(count) * 1e-3).astype(np.float32)
+    x[::97] *= 1e-4                      # some gradients deep in the FP16 subnormal range
+    for dtype in ("f16", "bf16"):
+        bits = oracle.encode16(x, dtype)
+        for S in (2.0 ** -149, 2.0 ** -127, 2.0 ** -126, 2.0 ** -125, 0.75, 1.0, 3.0, 1024.0,
+                  65536.0, float(np.nextafter(np.float32(65536.0), np.float32(0))),
+                  2.0 ** 126, 2.0 ** 127):
+            for phase in (0, 3):
+                check_case(bits, dtype, phase, S)    # flag bit-exact; sum within 1 ulp

@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "launch.h"
 #include "zero_shard.h"
 
@@ -365,10 +367,40 @@ __global__ __launch_bounds__(kThreads) void overflow_flag_kernel(
     }
 }
 
-// Flag and sum of squares: each gradient is unscaled, tested and squared as
-// its definition says; lanes accumulate in FP64, waves reduce by shuffles,
-// and block b writes its partial sum to partials[b].  Same element split as
-// the flag kernel.
+// One DPP move of a double (both 32-bit halves with the same control); lanes
+// whose source is outside the row, or whose row is masked off, read 0.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ double dpp_move(double x) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(b)), kCtrl, kRowMask, 0xf, true));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(b >> 32)), kCtrl, kRowMask, 0xf, true));
+    return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+}
+
+// Sum of a wave's 64 doubles, left in lane 63, by DPP row operations in a
+// fixed order: pairs and quads (quad permutes), then rows of 16 (row shifts
+// by 4 and 8), then the four rows (row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ double wave_sum_to_lane63(double x) {
+    x += dpp_move<0xb1>(x);        // quad_perm [1,0,3,2]
+    x += dpp_move<0x4e>(x);        // quad_perm [2,3,0,1]
+    x += dpp_move<0x114>(x);       // row_shr:4
+    x += dpp_move<0x118>(x);       // row_shr:8  (lane 15 of a row: the row's sum)
+    x += dpp_move<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_move<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Flag and sum of squares.  Every gradient is unscaled and squared as its
+// definition says, with three exact shortcuts: when S is a power of two whose
+// reciprocal is a normal number, g * (1/S) is the same correctly rounded
+// value as g / S; q*q is exact in FP64 (a 24-bit significand squared), so one
+// FP64 fma equals the square followed by the addition; and a lane's FP64 sum
+// is not finite iff one of its q is (finite squares of FP32 values cannot
+// overflow an FP64 sum of fewer than 2^60 terms), so the flag is read off the
+// sums.  Lanes accumulate in FP64, waves reduce by DPP, and block b writes
+// its partial sum to partials[b].  Same element split as the flag kernel.
 template <typename GT, int DT, int U>
 __global__ __launch_bounds__(kThreads) void overflow_sumsq_kernel(
     const GT *__restrict__ g, uint64_t count, uint32_t head, uint64_t n_vec, float loss_scale,
@@ -377,52 +409,64 @@ __global__ __launch_bounds__(kThreads) void overflow_sumsq_kernel(
     using B = GradBits<GT, DT>;
     if (loss_scale_dev != nullptr) loss_scale = *loss_scale_dev;
     const uint32_t tid = threadIdx.x;
-    uint32_t bad = !(loss_scale > 0.0f) || not_finite(loss_scale);
+    const bool scale_ok = loss_scale > 0.0f && !not_finite(loss_scale);
+    const uint32_t sbits = __builtin_bit_cast(uint32_t, loss_scale);
+    const uint32_t sexp = (sbits >> 23) & 0xffu;
+    const bool pow2 = scale_ok && (sbits & 0x7fffffu) == 0 && sexp >= 1 && sexp <= 253;
+    const float inv = 1.0f / loss_scale;  // exact when pow2
     double acc = 0.0;
-    auto visit = [&](float graw) {
-        const float q = graw / loss_scale;
-        bad |= not_finite(q);
-        acc += static_cast<double>(q) * static_cast<double>(q);
-    };
-    auto visit_vec = [&](const u32x4 &x) {
+
+    auto run = [&](auto pow2_tag) {
+        constexpr bool kPow2 = decltype(pow2_tag)::value;
+        auto visit = [&](float graw) {
+            const float q = kPow2 ? graw * inv : graw / loss_scale;
+            const double qd = static_cast<double>(q);
+            acc = __builtin_fma(qd, qd, acc);
+        };
+        auto visit_vec = [&](const u32x4 &x) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (sizeof(GT) == 2) {
-                visit(widen<DT>(x[j] & 0xffffu));
-                visit(widen<DT>(x[j] >> 16));
-            } else {
-                // copy the lane out first: bit-casting the vector element in
-                // place made the compiler reuse one element for all four
-                const uint32_t bits = x[j];
-                visit(__builtin_bit_cast(float, bits));
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (sizeof(GT) == 2) {
+                    visit(widen<DT>(x[j] & 0xffffu));
+                    visit(widen<DT>(x[j] >> 16));
+                } else {
+                    // copy the lane out first: bit-casting the vector element in
+                    // place made the compiler reuse one element for all four
+                    const uint32_t bits = x[j];
+                    visit(__builtin_bit_cast(float, bits));
+                }
             }
+        };
+        if (blockIdx.x == 0 && tid < head) visit(grad_at<GT, DT>(g, tid));
+        const u32x4 *vec = reinterpret_cast<const u32x4 *>(g + head);
+        const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+        uint64_t k = static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
+        for (; k + (U - 1) * stride < n_vec; k += U * stride) {
+            u32x4 x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[u] = load_nt(vec + k + u * stride);
+#pragma unroll
+            for (int u = 0; u < U; ++u) visit_vec(x[u]);
         }
+        for (; k < n_vec; k += stride) visit_vec(load_nt(vec + k));
+        for (uint64_t i = head + n_vec * B::kPerVec + static_cast<uint64_t>(blockIdx.x) * kThreads +
+                          tid;
+             i < count; i += stride)
+            visit(grad_at<GT, DT>(g, i));
     };
+    if (pow2)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 
-    if (blockIdx.x == 0 && tid < head) visit(grad_at<GT, DT>(g, tid));
-
-    const u32x4 *vec = reinterpret_cast<const u32x4 *>(g + head);
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
-    uint64_t k = static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
-    for (; k + (U - 1) * stride < n_vec; k += U * stride) {
-        u32x4 x[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = load_nt(vec + k + u * stride);
-#pragma unroll
-        for (int u = 0; u < U; ++u) visit_vec(x[u]);
-    }
-    for (; k < n_vec; k += stride) visit_vec(load_nt(vec + k));
-    for (uint64_t i = head + n_vec * B::kPerVec + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
-         i < count; i += stride)
-        visit(grad_at<GT, DT>(g, i));
-
+    const uint64_t abits = __builtin_bit_cast(uint64_t, acc);
+    const bool bad = !scale_ok || ((abits >> 52) & 0x7ffu) == 0x7ffu;
     if (__any(bad)) {
         if ((tid & 63u) == 0) *flag = 1;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    acc = wave_sum_to_lane63(acc);
     __shared__ double wave_sum[kThreads / 64];
-    if ((tid & 63u) == 0) wave_sum[tid >> 6] = acc;
+    if ((tid & 63u) == 63u) wave_sum[tid >> 6] = acc;
     __syncthreads();
     if (tid == 0) {
         double b = 0.0;
