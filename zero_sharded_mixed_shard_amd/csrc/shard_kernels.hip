@@ -38,7 +38,7 @@ namespace {
 constexpr int kThreads = 256;              // 4 wave64s
 constexpr int kVec = 4;                    // elements per lane per group
 constexpr int kGroup = kThreads * kVec;    // elements per block per group
-constexpr uint32_t kSumsqPartials = 4096;  // == ZERO_SUMSQ_PARTIALS
+constexpr uint32_t kSumsqPartials = 4096;  // == ZERO_SUMSQ_PARTIALS (room for the grid)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -543,7 +543,17 @@ __global__ void scaler_decide(zero_device_ctl *__restrict__ ctl, const float *__
 constexpr int kAdamU = 2;              // groups in flight per lane in the step
 constexpr int kAccU = 2;               // groups in flight per lane in the accumulate
 constexpr int kCheckU = 4;             // 16-B vectors in flight per lane in the check
-constexpr int kCheckBlocksPerCU = 128; // flag-only check grid cap per CU (measured)
+// Check grids (measured on MI355X, 256 CUs).  Up to 8 GiB of gradients, one
+// round of 7 blocks per CU streams fastest (6.7-7.1 TB/s against 6.3-6.8 for
+// larger grids); beyond it, 128 blocks per CU (7.0 TB/s at 20 GB against 6.65
+// for one round).  The sum of squares takes at most 1792 blocks (one round
+// on 256 CUs) whatever the device, so its partial sums depend on the size
+// and the view's phase only.
+constexpr int kCheckBlocksPerCURound = 7;
+constexpr int kCheckBlocksPerCU = 128;
+constexpr uint64_t kCheckRoundBytes = 8ull << 30;
+constexpr uint32_t kSumsqBlocks = 1792;
+static_assert(kSumsqBlocks <= kSumsqPartials, "one partial per block");
 
 inline uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
@@ -639,7 +649,9 @@ CheckGrid check_grid(const GT *g, uint64_t count, bool sumsq, int num_cus) {
     uint64_t need = c.n_vec > 0 ? (c.n_vec + per_block - 1) / per_block
                                 : (rest + kThreads - 1) / kThreads;
     if (need == 0) need = 1;
-    uint64_t cap = sumsq ? kSumsqPartials : static_cast<uint64_t>(num_cus) * kCheckBlocksPerCU;
+    const int per_cu = count * sizeof(GT) < kCheckRoundBytes ? kCheckBlocksPerCURound
+                                                             : kCheckBlocksPerCU;
+    uint64_t cap = sumsq ? kSumsqBlocks : static_cast<uint64_t>(num_cus) * per_cu;
     if (!sumsq && cap > max_blocks()) cap = max_blocks();  // the partials' grid stays fixed
     c.blocks = static_cast<uint32_t>(need < cap ? need : cap);
     return c;
