@@ -22,6 +22,13 @@
  *     Exactly elements [0, count) of each view are read or written, where
  *     count is the layout's count for (psi, n, rank).  The padding of a short
  *     last shard and anything past count are never touched.
+ *   - The views of one call may not overlap one another (the kernels stream
+ *     them as independent arrays); overlapping views are rejected with
+ *     ZERO_EINVAL.  Read-only views may repeat (the same replica passed twice
+ *     to zero_reduce_shard); zero_reduce_shard's output may be exactly rank
+ *     r's chunk of one replica (an in-place reduce-scatter), and a shard
+ *     passed to zero_gather_shards may sit exactly at its place in the full
+ *     buffer (an in-place all-gather).
  *   - Any element-aligned pointer is accepted (4 bytes for FP32 arrays, 2
  *     for 16-bit ones).  The kernels do a head of h < 32 elements one at a
  *     time, h bringing the FP32 master view to a 128-byte line, and stream

@@ -397,3 +397,26 @@ def test_plain_c_client_links_and_calls_the_host_entry_points():
     want = [np.float32(1.0 - float(np.float32(beta)) ** t) for beta in (0.9, 0.999) for t in (1, 2)]
     assert b == want
     assert out[5] == "invalid argument"
+
+
+# Overlapping views are rejected before anything reaches a device.
+@pytest.mark.parametrize("ptrs", [
+    (FAKE, FAKE, FAKE * 4, FAKE * 8, FAKE * 12),             # w16 and g16 at one address
+    (FAKE, FAKE * 2, FAKE * 4, FAKE * 4 + 396, FAKE * 12),   # m starts inside master's last element
+    (FAKE * 16 + 8, FAKE * 2, FAKE * 4, FAKE * 8, FAKE * 16),  # w16 inside v
+])
+def test_adam_step_rejects_overlapping_views(ptrs):
+    # psi = 400 over 4 ranks: count 100, so FP32 views span 400 bytes
+    assert adam(psi=400, n=4, rank=0, ptrs=ptrs) == -1
+
+
+def test_overlap_checks_of_accumulate_reduce_and_gather():
+    # accumulate: acc (FP32) over the gradients
+    assert zs.lib.zero_grad_accumulate(FAKE, FAKE + 200, 0, 400, 4, 0, 0, None) == -1
+    # reduce: the output partly over one replica's chunk (rank 0: offset 0); exactly on
+    # it (in place) is allowed
+    reps = (ctypes.c_void_p * 2)(FAKE * 4, FAKE * 8)
+    assert zs.lib.zero_reduce_shard(FAKE * 8 + 64, 0, reps, 0, 400, 4, 0, None) == -1
+    # gather: a shard overlapping the full buffer somewhere other than its own place
+    shards = (ctypes.c_void_p * 4)(FAKE * 8, FAKE * 8 + 2, FAKE * 8 + 400, FAKE * 8 + 600)
+    assert zs.lib.zero_gather_shards(FAKE * 8, shards, 0, 400, 4, None) == -1

@@ -147,3 +147,43 @@ def sum_f32(arrays):
     for a in arrays:
         acc = acc + a
     return acc
+
+
+@pytest.mark.parametrize("fmt", ["f16", "f32"])
+def test_in_place_reduce_scatter_and_all_gather(fmt):
+    # In place, as collective libraries allow it: rank k's reduce-scatter result
+    # overwrites its own chunk of replica k, and the all-gather reads shards that
+    # already sit at their places in the full buffer (here: even ranks) beside
+    # shards held elsewhere (odd ranks).  Partial overlaps are rejected.
+    psi, n = 100_003, 4
+    reps = make_replicas(psi, n, fmt, 4100 + len(fmt))
+    hreps = [host(r) for r in reps]
+    want = [oracle.reduce_shard(hreps, fmt, fmt, psi, n, k) for k in range(n)]
+    lays = [zs.zero_shard_layout(psi, n, k) for k in range(n)]
+    for k, lay in enumerate(lays):
+        zs.zero_reduce_shard(reps[k][lay.offset:lay.offset + lay.count], reps, psi, n, k)
+    for k, lay in enumerate(lays):
+        got = host(reps[k][lay.offset:lay.offset + lay.count])
+        assert np.array_equal(got.view(np.uint8), want[k].view(np.uint8)), (fmt, k)
+    full = GuardedView(lays[0].padded_total, TD[fmt], 0, DEV)
+    shards = []
+    for k, lay in enumerate(lays):
+        if k % 2 == 0:
+            s = full.view[lay.offset:lay.offset + lay.count]
+        else:
+            s = torch.empty(lay.count, dtype=TD[fmt], device=DEV)
+        s.copy_(reps[k][lay.offset:lay.offset + lay.count])
+        shards.append(s)
+    zs.zero_gather_shards(full.view, shards, psi, n)
+    got = host(full.view)[:psi]
+    assert np.array_equal(got.view(np.uint8), np.concatenate(want).view(np.uint8))
+    assert full.guards_intact()
+    # a shard overlapping the full buffer anywhere but at its place
+    bad = list(shards)
+    bad[1] = full.view[7:7 + lays[1].count]
+    with pytest.raises(zs.ZeroError):
+        zs.zero_gather_shards(full.view, bad, psi, n)
+    lay0 = lays[0]
+    with pytest.raises(zs.ZeroError):      # the output straddling replica 1's chunk
+        zs.zero_reduce_shard(reps[1][lay0.offset + 3:lay0.offset + 3 + lay0.count], reps, psi, n, 0)
+    log(f"in-place reduce-scatter / all-gather {fmt}: bitwise")

@@ -50,6 +50,21 @@ std::atomic<uint64_t> g_grid_cap{zs::kMaxBlocks};
 
 bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
+// Byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+// No two of the n views (pointer, bytes) overlap: the kernels stream them as
+// independent arrays.
+bool disjoint(const void *const *p, const uint64_t *bytes, int n) {
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if (overlap(p[i], bytes[i], p[j], bytes[j])) return false;
+    return true;
+}
+
 bool finite(float x) { return std::isfinite(x); }
 
 bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; }
@@ -88,6 +103,10 @@ int step_args(void *w16, const void *g, uintptr_t g_align, float *master, float 
         if (!aligned(w16, 2) || !aligned(g, g_align) || !aligned(master, 4) || !aligned(m, 4) ||
             !aligned(v, 4))
             return ZERO_EINVAL;
+        const void *views[5] = {w16, g, master, m, v};
+        const uint64_t c = lay.count;
+        const uint64_t bytes[5] = {2 * c, g_align * c, 4 * c, 4 * c, 4 * c};
+        if (!disjoint(views, bytes, 5)) return ZERO_EINVAL;
     }
     s->lr = lr;
     s->beta1 = beta1;
@@ -163,6 +182,7 @@ extern "C" int zero_grad_accumulate(float *acc, const void *g16, zero_dtype dt, 
     if (rc != ZERO_OK) return rc;
     if (count == 0) return ZERO_OK;
     if (acc == nullptr || !aligned(acc, 4)) return ZERO_EINVAL;
+    if (overlap(acc, 4 * count, g16, 2 * count)) return ZERO_EINVAL;
     const hipError_t e =
         zs::launch_grad_accumulate(static_cast<int>(dt), acc, static_cast<const uint16_t *>(g16),
                                    count, first != 0, static_cast<hipStream_t>(stream));
@@ -228,6 +248,11 @@ extern "C" int zero_reduce_shard(void *out, zero_dtype out_dt, const void *const
     for (uint32_t k = 0; k < n; ++k) {
         if (replicas[k] == nullptr || !aligned(replicas[k], in_b)) return ZERO_EINVAL;
         set.p[k] = static_cast<const char *>(replicas[k]) + lay.offset * in_b;
+        // the output may be exactly a replica's chunk (in place: each element is
+        // written after every replica's element was read) but may not overlap one
+        // otherwise; replicas may repeat one another
+        if (out != set.p[k] && overlap(out, out_b * lay.count, set.p[k], in_b * lay.count))
+            return ZERO_EINVAL;
     }
     const hipError_t e = zs::launch_reduce_shard(out, static_cast<int>(out_dt), set,
                                                  static_cast<int>(in_dt), n, lay.count,
@@ -249,6 +274,11 @@ extern "C" int zero_gather_shards(void *full, const void *const *shards, zero_dt
         zero_layout lk;
         zero_shard_layout(psi, n, k, &lk);
         if (lk.count > 0 && (shards[k] == nullptr || !aligned(shards[k], eb))) return ZERO_EINVAL;
+        // a shard may sit exactly at its place in the full buffer (an in-place
+        // all-gather: the copy is then the identity), but may not overlap it otherwise
+        const char *dst = static_cast<const char *>(full) + lk.offset * eb;
+        if (shards[k] != dst && overlap(full, psi * eb, shards[k], lk.count * eb))
+            return ZERO_EINVAL;
         set.p[k] = shards[k];
         set.count[k] = lk.count;
         set.head[k] = 0;

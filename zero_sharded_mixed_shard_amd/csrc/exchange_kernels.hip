@@ -106,9 +106,11 @@ __device__ __forceinline__ void store_vec(typename Fmt<F>::T *p, const float v[K
 // covers elements head + q*K .. +K-1 (K = kPerVec<IN>), one 256-vector tile
 // per block, and block 0 does [0, head) and [head + n_vec*K, count) one at a
 // time.  With n_vec == 0 the whole grid walks every element.
+// out is not restrict-qualified: it may be one of the replicas' chunks (in
+// place); every lane reads all replicas at its elements before it writes them.
 template <int IN, int OUT>
 __global__ __launch_bounds__(kThreads) void reduce_shard_kernel(
-    typename Fmt<OUT>::T *__restrict__ out, ReplicaSet in, uint32_t n, uint64_t count,
+    typename Fmt<OUT>::T *out, ReplicaSet in, uint32_t n, uint64_t count,
     uint32_t head, uint64_t n_vec) {
     using TI = typename Fmt<IN>::T;
     constexpr int K = kPerVec<IN>;
@@ -152,13 +154,14 @@ __global__ __launch_bounds__(kThreads) void reduce_shard_kernel(
 // source and destination share a 16-B phase is copied 16 B per lane after its
 // head (one 256-vector tile per block, block 0 doing head and tail); otherwise
 // one element at a time over the whole grid.
+// Not restrict-qualified: a shard may already sit at its place in full (an
+// in-place all-gather), when each copy rewrites the value it read.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void gather_kernel(T *__restrict__ full, GatherSet set,
-                                                          uint64_t shard) {
+__global__ __launch_bounds__(kThreads) void gather_kernel(T *full, GatherSet set, uint64_t shard) {
     constexpr uint32_t K = kVecBytes / sizeof(T);
     const uint32_t k = blockIdx.y;
-    const T *__restrict__ src = static_cast<const T *>(set.p[k]);
-    T *__restrict__ dst = full + static_cast<uint64_t>(k) * shard;
+    const T *src = static_cast<const T *>(set.p[k]);
+    T *dst = full + static_cast<uint64_t>(k) * shard;
     const uint64_t count = set.count[k];
     const uint32_t head = set.head[k];
     if (!set.vec[k]) {
