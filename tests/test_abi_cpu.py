@@ -420,3 +420,34 @@ def test_overlap_checks_of_accumulate_reduce_and_gather():
     # gather: a shard overlapping the full buffer somewhere other than its own place
     shards = (ctypes.c_void_p * 4)(FAKE * 8, FAKE * 8 + 2, FAKE * 8 + 400, FAKE * 8 + 600)
     assert zs.lib.zero_gather_shards(FAKE * 8, shards, 0, 400, 4, None) == -1
+
+
+def test_binding_rejects_host_tensors_before_any_device_call():
+    # every device argument must be a device tensor: a host pointer reaching a
+    # kernel would fault the GPU, so the binding refuses it first
+    import torch
+    n = 64
+    h16 = torch.zeros(n, dtype=torch.float16)
+    h32 = torch.zeros(n, dtype=torch.float32)
+    flag = torch.zeros(1, dtype=torch.int32)
+    ctl = torch.zeros(256, dtype=torch.uint8)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+    calls = [
+        lambda: zs.zero_overflow_check(h16, n, 1, 0, 1.0, flag),
+        lambda: zs.zero_adam_step(h16, h16.clone(), h32, h32.clone(), h32.clone(), n, 1, 0,
+                                  step=1, loss_scale=1.0, **hp),
+        lambda: zs.zero_adam_step_g32(h16, h32, h32.clone(), h32.clone(), h32.clone(), n, 1, 0,
+                                      step=1, loss_scale=1.0, **hp),
+        lambda: zs.zero_grad_accumulate(h32, h16, n, 1, 0, first=True),
+        lambda: zs.zero_overflow_check_g32(h32, n, 1, 0, 1.0, flag),
+        lambda: zs.zero_overflow_check_dev(h16, n, 1, 0, ctl),
+        lambda: zs.zero_scaler_update_dev(ctl, torch.zeros(8), 1),
+        lambda: zs.zero_adam_step_dev(h16, h16.clone(), h32, h32.clone(), h32.clone(), n, 1, 0,
+                                      ctl=ctl, **hp),
+        lambda: zs.zero_reduce_shard(h16[:32], [h16, h16.clone()], n, 2, 0),
+        lambda: zs.zero_gather_shards(h16, [h16[:32].clone(), h16[:32].clone()], n, 2),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(ValueError) as e:
+            call()
+        assert "device" in str(e.value), (i, str(e.value))

@@ -163,6 +163,9 @@ def _view(t: torch.Tensor, name: str, dtypes, count: int, device) -> int:
     """Pointer of a 1-D contiguous device tensor holding at least `count` elements."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device}): the kernels "
+                         "read and write device memory only")
     if t.dtype not in dtypes:
         raise TypeError(f"{name}: dtype {t.dtype} not in {list(dtypes)}")
     if t.device != device:
@@ -278,9 +281,9 @@ def device_ctl_read(ctl: torch.Tensor) -> DeviceCtl:
 
 def _ctl_ptr(ctl: torch.Tensor, device) -> int:
     if ctl.dtype != torch.uint8 or ctl.numel() < ctypes.sizeof(DeviceCtl) or \
-            ctl.device != device or not ctl.is_contiguous():
-        raise ValueError(f"ctl must be a contiguous uint8 tensor of {ctypes.sizeof(DeviceCtl)} "
-                         f"bytes on {device}")
+            ctl.device != device or ctl.device.type != "cuda" or not ctl.is_contiguous():
+        raise ValueError(f"ctl must be a contiguous uint8 device tensor of "
+                         f"{ctypes.sizeof(DeviceCtl)} bytes on {device}")
     return ctl.data_ptr()
 
 
@@ -310,8 +313,8 @@ def zero_scaler_update_dev(ctl: torch.Tensor, bias: torch.Tensor, t_first: int,
                            stream=None) -> None:
     """Skip-or-apply decision on the device; `bias` is a device copy of zero_bias_corrections."""
     dev = ctl.device
-    if bias.dtype != torch.float32 or bias.device != dev or bias.dim() != 1 or \
-            bias.numel() % 2 or not bias.is_contiguous():
+    if bias.dtype != torch.float32 or bias.device != dev or dev.type != "cuda" or \
+            bias.dim() != 1 or bias.numel() % 2 or not bias.is_contiguous():
         raise ValueError("bias must be a 1-D float32 device tensor of 2*length entries")
     with torch.cuda.device(dev):
         rc = lib.zero_scaler_update_dev(_ctl_ptr(ctl, dev), bias.data_ptr(), t_first,
