@@ -400,16 +400,18 @@ def measure_checkpoint(n_elem: int = 1 << 26) -> dict:
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--gpus", type=int, default=1,
+                    help="GPUs (only 1: the step runs on one rank's shard)")
+    ap.add_argument("--steps", type=int, default=5, help="timed steps")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed steps before them")
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="workload id (4 = 1e10 params, N=1; the reported configuration)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle baseline")
     ap.add_argument("--cpu-sample", type=int, default=1 << 24,
                     help="parameters in the CPU baseline's sample")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle baseline")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy measurement")
     ap.add_argument("--extras", action="store_true",
                     help="also time the accumulate / FP32-gradient / device-control / exchange "
