@@ -243,12 +243,15 @@ extern "C" int zero_ckpt_verify(const char *path) {
     int rc = read_header(f, &h);
     if (rc == ZERO_OK && fseeko(f, sizeof h, SEEK_SET) != 0) rc = ZERO_EIO;
     Hasher hs;
-    static thread_local char buf[1 << 20];
+    std::vector<char> buf(1 << 20);
     uint64_t left = rc == ZERO_OK ? h.payload_bytes : 0;
     while (rc == ZERO_OK && left > 0) {
-        const size_t chunk = left > sizeof buf ? sizeof buf : static_cast<size_t>(left);
-        if (std::fread(buf, 1, chunk, f) != chunk) rc = ZERO_EIO;
-        hs.add(buf, chunk);
+        const size_t chunk = left > buf.size() ? buf.size() : static_cast<size_t>(left);
+        if (std::fread(buf.data(), 1, chunk, f) != chunk) {
+            rc = ZERO_EIO;
+            break;
+        }
+        hs.add(buf.data(), chunk);
         left -= chunk;
     }
     std::fclose(f);
