@@ -92,3 +92,89 @@ def test_random_sweep_matches_oracle():
         stats["mixed_phase"] += len(set(phases.values())) > 1
     log(f"random sweep: {stats}")
     assert stats["skipped_steps"] > 0 and stats["applied_steps"] > 0 and stats["mixed_phase"] > 0
+
+
+def test_random_fp32_gradients_device_control_and_exchanges():
+    rng = np.random.default_rng(4242)
+    for case in range(120):
+        count = int(rng.choice([1, 5, 1023, 2049, 4096 + 31, 70_001, 200_003]))
+        dtype = "f16" if case % 2 else "bf16"
+        pa, pg = int(rng.integers(0, 8)), int(rng.integers(0, 8))
+        S = float(rng.choice([1.0, 256.0, 3.0, 65536.0]))
+        std = float(10.0 ** rng.uniform(-6, 1))
+        hp = dict(lr=float(rng.choice([1e-4, 1e-3])), beta1=0.9, beta2=0.999,
+                  eps=float(rng.choice([0.0, 1e-8])), weight_decay=float(rng.choice([0.0, 0.01])))
+        # micro-batches into an FP32 accumulator, the FP32 check with its sum of squares
+        acc = GuardedView(count, torch.float32, pa, DEV)
+        gv = GuardedView(count, TD[dtype], pg, DEV)
+        ref_acc = np.zeros(count, np.float32)
+        for j in range(int(rng.integers(1, 4))):
+            g = synth.fill_normal_(torch.empty(count, dtype=TD[dtype]), std, 20_000 + 10 * case + j)
+            gv.view.copy_(g.to(DEV))
+            zs.zero_grad_accumulate(acc.view, gv.view, count, 1, 0, first=(j == 0))
+            oracle.grad_accumulate(ref_acc, u16(g), dtype, first=(j == 0))
+        torch.cuda.synchronize()
+        assert np.array_equal(f32(acc.view).view(np.uint32), ref_acc.view(np.uint32)), case
+        flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+        ssq = torch.zeros(1, device=DEV)
+        parts = torch.empty(zs.SUMSQ_PARTIALS, dtype=torch.float64, device=DEV)
+        zs.zero_overflow_check_g32(acc.view, count, 1, 0, S, flag, ssq, parts)
+        rf, rs = oracle.overflow_check_g32(ref_acc, S)
+        assert int(flag.item()) == rf, case
+        if rf == 0:
+            assert oracle.ulp_distance32(np.float32(ssq.item()), np.float32(rs)).max() <= 1, case
+            V = {k: GuardedView(count, torch.float32, pa, DEV) for k in ("master", "m", "v")}
+            V["w16"] = GuardedView(count, TD[dtype], pa, DEV)
+            master0 = synth.fill_normal_(torch.empty(count), 0.02, 21_000 + case)
+            V["master"].view.copy_(master0.to(DEV))
+            for k in ("m", "v", "w16"):
+                V[k].view.zero_()
+            zs.zero_adam_step_g32(V["w16"].view, acc.view, V["master"].view, V["m"].view,
+                                  V["v"].view, count, 1, 0, step=1, loss_scale=S, **hp)
+            ref = dict(master=master0.numpy().copy(), m=np.zeros(count, np.float32),
+                       v=np.zeros(count, np.float32), w16=np.zeros(count, np.uint16))
+            oracle.adam_step_g32(ref["w16"], ref_acc, ref["master"], ref["m"], ref["v"], dtype,
+                                 step=1, loss_scale=S, **hp)
+            torch.cuda.synchronize()
+            got = dict(master=f32(V["master"].view), m=f32(V["m"].view), v=f32(V["v"].view),
+                       w16=u16(V["w16"].view))
+            assert_close(got, ref, dtype, f"g32 case {case}")
+        # the exchanges over a random rank count and formats
+        psi = int(rng.integers(1, 150_000))
+        n = int(rng.integers(1, 17))
+        fin, fout = rng.choice(["f16", "bf16", "f32"], 2)
+        tdi = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+        reps = []
+        for k in range(n):
+            x = synth.fill_normal_(torch.empty(psi, dtype=tdi[fin]), 1e-2, 30_000 + 100 * case + k)
+            reps.append(x.to(DEV))
+        hreps = [f32(r) if fin == "f32" else u16(r) for r in reps]
+        rank = int(rng.integers(0, n))
+        lay = zs.zero_shard_layout(psi, n, rank)
+        out = GuardedView(lay.count, tdi[fout], int(rng.integers(0, 8)), DEV)
+        zs.zero_reduce_shard(out.view, reps, psi, n, rank)
+        want = oracle.reduce_shard(hreps, fin, fout, psi, n, rank)
+        got = f32(out.view) if fout == "f32" else u16(out.view)
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (case, psi, n, fin, fout)
+        assert out.guards_intact()
+    log("random FP32-gradient and exchange sweep: 120 cases")
+
+
+def test_random_device_control_schedules():
+    # random overflow schedules and growth intervals, enqueued without read-back
+    from test_gpu_c_device_ctl import make_grads, run_device, run_oracle
+    rng = np.random.default_rng(777)
+    for case in range(12):
+        count = int(rng.choice([3, 4099, 65_537]))
+        steps = int(rng.integers(2, 9))
+        bad = tuple(int(s) for s in np.nonzero(rng.random(steps) < 0.3)[0] + 1)
+        growth = int(rng.choice([1, 2, 3, 2000]))
+        dtype = "f16" if case % 2 else "bf16"
+        S0 = float(rng.choice([1.0, 1024.0, 65536.0]))
+        grads = make_grads(count, steps, dtype, 600 + 50 * case, bad_steps=bad)
+        got, ctl, master0 = run_device(count, dtype, grads, S0, growth, phase=case % 4)
+        ref, st, trace = run_oracle(master0, grads, dtype, S0, growth)
+        assert (ctl.scaler.step, ctl.scaler.loss_scale, ctl.scaler.clean_steps) == \
+            (st.step, st.loss_scale, st.clean_steps), (case, trace)
+        assert_close(got, ref, dtype, f"device-control case {case}: bad {bad} growth {growth}")
+    log("random device-control schedules: 12 cases")
