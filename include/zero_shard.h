@@ -30,8 +30,9 @@
  *     passed to zero_gather_shards may sit exactly at its place in the full
  *     buffer (an in-place all-gather).
  *   - Any element-aligned pointer is accepted (4 bytes for FP32 arrays, 2
- *     for 16-bit ones).  The kernels do a head of h < 32 elements one at a
- *     time, h bringing the FP32 master view to a 128-byte line, and stream
+ *     for 16-bit ones).  The kernels do a head of h < 64 elements one at a
+ *     time, h bringing the FP32 master view (and, where one head does both,
+ *     the 16-bit views) to a 128-byte line, and stream
  *     the rest in vectors when at element h every FP32 view is 16-byte and
  *     every 16-bit view 8-byte aligned.  That holds whenever all views sit at
  *     the same element offset into 16-byte-aligned buffers.  Otherwise a

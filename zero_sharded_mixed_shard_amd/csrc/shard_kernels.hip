@@ -571,13 +571,22 @@ constexpr uint32_t kLine = 128;
 
 // Head that aligns the FP32 reference array to a cache line, and whether it
 // also leaves every other view vector-aligned: FP32 arrays (a, b, FP32
-// gradients) at 16 B and 16-bit arrays (16-bit gradients, h16) at 8 B.  The
-// head is congruent mod 4 to the one that aligns ref to 16 B, so the test is
-// the same as for a 16-B head.  b and h16 may be null.
+// gradients) at 16 B and 16-bit arrays (16-bit gradients, h16) at 8 B.  When
+// a head of up to 63 elements puts the 16-bit view on a line as well (it
+// does whenever the views share one element phase), that one is taken: a
+// wave's 512-B 16-bit access then covers whole lines too.  Either head is
+// congruent mod 4 to the one that aligns ref to 16 B, so the test is the same
+// as for a 16-B head.  b and h16 may be null.
 template <typename GT>
 bool common_phase(const float *ref, const float *a, const float *b, const GT *g,
                   const uint16_t *h16, uint32_t *head) {
     *head = align_head(addr(ref), 4, kLine);
+    const uint16_t *v16 = h16;
+    if constexpr (sizeof(GT) == 2) v16 = g;
+    if (v16 != nullptr) {
+        const uint32_t h2 = align_head(addr(v16), 2, kLine);
+        if ((addr(ref) + 4ull * h2) % kLine == 0) *head = h2;
+    }
     const bool g_ok = sizeof(GT) == 2 ? (addr(g) + 2u * *head) % 8 == 0
                                       : addr(g) % 16 == addr(ref) % 16;
     return addr(a) % 16 == addr(ref) % 16 && (b == nullptr || addr(b) % 16 == addr(ref) % 16) &&
