@@ -1,4 +1,6 @@
-"""Compile the oracle's C into oracle/liboracle.so with gcc (the checker, not the product).
+"""Compile the oracle's C into oracle/liboracle.so with gcc.
+
+The oracle is test infrastructure, not part of the product path.
 
     python oracle/build_oracle.py
 """
