@@ -451,3 +451,14 @@ def test_binding_rejects_host_tensors_before_any_device_call():
         with pytest.raises(ValueError) as e:
             call()
         assert "device" in str(e.value), (i, str(e.value))
+
+
+def test_library_depends_on_the_hip_runtime_only():
+    # the boundary is plain C over HIP: no PyTorch library is linked into it
+    out = subprocess.run(["readelf", "-d", zs.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    needed = re.findall(r"\(NEEDED\)\s+Shared library: \[([^\]]+)\]", out)
+    assert any(n.startswith("libamdhip64") for n in needed), needed
+    allowed = ("libamdhip64", "libstdc++", "libm.", "libgcc_s", "libc.", "ld-linux")
+    assert all(n.startswith(allowed) for n in needed), needed
+    assert not any("torch" in n or "c10" in n for n in needed), needed
