@@ -295,3 +295,31 @@ def test_sumsq_power_of_two_scales_and_their_edges():
                   2.0 ** 126, 2.0 ** 127):
             for phase in (0, 3):
                 check_case(bits, dtype, phase, S)    # flag bit-exact; sum within 1 ulp
+
+
+def test_calls_return_without_synchronising():
+    # A bounded spin kernel ahead of them on the stream: the check and the step
+    # are enqueued behind it and the calls return while it still runs.
+    count = 50_000
+    g = synth.fill_normal_(torch.empty(count, dtype=torch.float16), 1e-3, 71).to(DEV)
+    master = synth.fill_normal_(torch.empty(count), 0.02, 72).to(DEV)
+    m = torch.zeros(count, device=DEV)
+    v = torch.zeros(count, device=DEV)
+    w = torch.zeros(count, dtype=torch.float16, device=DEV)
+    flag = torch.full((1,), 5, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)             # bounded spin: tens of ms at shader clocks
+    zs.zero_overflow_check(g, count, 1, 0, 1.0, flag)
+    zs.zero_adam_step(w, g, master, m, v, count, 1, 0, step=1, loss_scale=1.0, found_inf=flag,
+                      **HP)
+    done = torch.cuda.Event()
+    done.record()
+    pending = not done.query()
+    torch.cuda.synchronize()
+    assert pending, "a call waited for the stream"
+    h_master = synth.fill_normal_(torch.empty(count), 0.02, 72).numpy().copy()
+    h_m, h_v, h_w = np.zeros(count, np.float32), np.zeros(count, np.float32), np.zeros(count, np.uint16)
+    oracle.adam_step(h_w, u16(g), h_master, h_m, h_v, "f16", step=1, loss_scale=1.0, **HP)
+    assert flag.item() == 0
+    assert_close(dict(master=f32(master), m=f32(m), v=f32(v), w16=u16(w)),
+                 dict(master=h_master, m=h_m, v=h_v, w16=h_w), "f16", "async")
