@@ -323,3 +323,52 @@ def test_calls_return_without_synchronising():
     assert flag.item() == 0
     assert_close(dict(master=f32(master), m=f32(m), v=f32(v), w16=u16(w)),
                  dict(master=h_master, m=h_m, v=h_v, w16=h_w), "f16", "async")
+
+
+def test_concurrent_host_threads_on_their_own_streams():
+    # The library keeps no per-call state; four host threads step four shards
+    # on four streams at once and each result equals its sequential twin.
+    import threading
+    count, steps, nthreads = 120_001, 4, 4
+    grads = [[synth.fill_normal_(torch.empty(count, dtype=torch.float16), 1e-3, 900 + 10 * k + t)
+              .to(DEV) for t in range(steps)] for k in range(nthreads)]
+    master0 = [synth.fill_normal_(torch.empty(count), 0.02, 950 + k).to(DEV) for k in range(nthreads)]
+
+    def fresh(k):
+        return dict(master=master0[k].clone(), m=torch.zeros(count, device=DEV),
+                    v=torch.zeros(count, device=DEV),
+                    w16=torch.zeros(count, dtype=torch.float16, device=DEV),
+                    flag=torch.zeros(1, dtype=torch.int32, device=DEV))
+
+    def run(k, st, stream, errors):
+        try:
+            with torch.cuda.stream(stream):
+                for t in range(steps):
+                    zs.zero_overflow_check(grads[k][t], count, 1, 0, 1024.0, st["flag"],
+                                           stream=stream)
+                    zs.zero_adam_step(st["w16"], grads[k][t], st["master"], st["m"], st["v"],
+                                      count, 1, 0, step=t + 1, loss_scale=1024.0,
+                                      found_inf=st["flag"], stream=stream, **HP)
+        except Exception as e:          # noqa: BLE001  (reported below)
+            errors.append(e)
+
+    torch.cuda.synchronize()
+    par = [fresh(k) for k in range(nthreads)]
+    streams = [torch.cuda.Stream() for _ in range(nthreads)]
+    errors = []
+    threads = [threading.Thread(target=run, args=(k, par[k], streams[k], errors))
+               for k in range(nthreads)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in range(nthreads):
+        seq = fresh(k)
+        run(k, seq, torch.cuda.current_stream(), errors)
+        torch.cuda.synchronize()
+        for key in ("master", "m", "v"):
+            assert torch.equal(par[k][key].view(torch.int32), seq[key].view(torch.int32)), (k, key)
+        assert torch.equal(par[k]["w16"].view(torch.int16), seq["w16"].view(torch.int16)), k
+    assert not errors, errors
