@@ -26,7 +26,8 @@
  *     them as independent arrays); overlapping views are rejected with
  *     ZERO_EINVAL.  Read-only views may repeat (the same replica passed twice
  *     to zero_reduce_shard); zero_reduce_shard's output may be exactly rank
- *     r's chunk of one replica (an in-place reduce-scatter), and a shard
+ *     r's chunk of one replica in the same format (an in-place
+ *     reduce-scatter), and a shard
  *     passed to zero_gather_shards may sit exactly at its place in the full
  *     buffer (an in-place all-gather).
  *   - Any element-aligned pointer is accepted (4 bytes for FP32 arrays, 2

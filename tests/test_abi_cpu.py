@@ -417,6 +417,8 @@ def test_overlap_checks_of_accumulate_reduce_and_gather():
     # it (in place) is allowed
     reps = (ctypes.c_void_p * 2)(FAKE * 4, FAKE * 8)
     assert zs.lib.zero_reduce_shard(FAKE * 8 + 64, 0, reps, 0, 400, 4, 0, None) == -1
+    # exactly on a replica's chunk but in a wider format: not in place, rejected
+    assert zs.lib.zero_reduce_shard(FAKE * 8, 2, reps, 0, 400, 4, 0, None) == -1
     # gather: a shard overlapping the full buffer somewhere other than its own place
     shards = (ctypes.c_void_p * 4)(FAKE * 8, FAKE * 8 + 2, FAKE * 8 + 400, FAKE * 8 + 600)
     assert zs.lib.zero_gather_shards(FAKE * 8, shards, 0, 400, 4, None) == -1

@@ -248,10 +248,11 @@ extern "C" int zero_reduce_shard(void *out, zero_dtype out_dt, const void *const
     for (uint32_t k = 0; k < n; ++k) {
         if (replicas[k] == nullptr || !aligned(replicas[k], in_b)) return ZERO_EINVAL;
         set.p[k] = static_cast<const char *>(replicas[k]) + lay.offset * in_b;
-        // the output may be exactly a replica's chunk (in place: each element is
-        // written after every replica's element was read) but may not overlap one
-        // otherwise; replicas may repeat one another
-        if (out != set.p[k] && overlap(out, out_b * lay.count, set.p[k], in_b * lay.count))
+        // the output may be exactly a replica's chunk in the same format (in place:
+        // each element is written after every replica's element was read) but may
+        // not overlap one otherwise; replicas may repeat one another
+        const bool in_place = out == set.p[k] && out_b == in_b;
+        if (!in_place && overlap(out, out_b * lay.count, set.p[k], in_b * lay.count))
             return ZERO_EINVAL;
     }
     const hipError_t e = zs::launch_reduce_shard(out, static_cast<int>(out_dt), set,
