@@ -22,8 +22,9 @@
  *     Exactly elements [0, count) of each view are read or written, where
  *     count is the layout's count for (psi, n, rank).  The padding of a short
  *     last shard and anything past count are never touched.
- *   - The views of one call may not overlap one another (the kernels stream
- *     them as independent arrays); overlapping views are rejected with
+ *   - The views of one call may not overlap one another, nor the flag,
+ *     sum-of-squares, partial-sum or control-block memory of the call (the
+ *     kernels stream them as independent arrays); overlaps are rejected with
  *     ZERO_EINVAL.  Read-only views may repeat (the same replica passed twice
  *     to zero_reduce_shard); zero_reduce_shard's output may be exactly rank
  *     r's chunk of one replica in the same format (an in-place

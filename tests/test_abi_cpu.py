@@ -464,3 +464,16 @@ def test_library_depends_on_the_hip_runtime_only():
     allowed = ("libamdhip64", "libstdc++", "libm.", "libgcc_s", "libc.", "ld-linux")
     assert all(n.startswith(allowed) for n in needed), needed
     assert not any("torch" in n or "c10" in n for n in needed), needed
+
+
+def test_flag_control_and_check_outputs_may_not_overlap_the_views():
+    # the step's skip flag inside master; the check's flag inside the gradients;
+    # the partial sums over the flag
+    assert adam(psi=400, n=4, rank=0, ptrs=(FAKE, FAKE * 2, FAKE * 4, FAKE * 8, FAKE * 12),
+                flag=FAKE * 4 + 40) == -1
+    assert check(psi=400, n=4, rank=0, g=FAKE * 4, flag=FAKE * 4 + 100) == -1
+    assert check(psi=400, n=4, rank=0, g=FAKE * 4, flag=FAKE * 64, sumsq=FAKE * 96,
+                 parts=FAKE * 64 - 8) == -1
+    # the device control block inside the working weights
+    assert zs.lib.zero_adam_step_dev(FAKE, FAKE * 2, FAKE * 4, FAKE * 8, FAKE * 12, 0, 400, 4, 0,
+                                     1e-3, 0.9, 0.999, 1e-8, 0.0, FAKE + 64, None) == -1

@@ -65,6 +65,16 @@ bool disjoint(const void *const *p, const uint64_t *bytes, int n) {
     return true;
 }
 
+// The check's outputs (flag, sum, partial sums) may not overlap the gradients
+// it reads, nor one another.
+bool check_outputs_ok(const void *g, uint64_t g_bytes, const void *flag, uint64_t flag_bytes,
+                      const float *sumsq, const double *partials) {
+    const void *p[4] = {g, flag, sumsq, partials};
+    const uint64_t b[4] = {g_bytes, flag_bytes, sumsq != nullptr ? 4u : 0u,
+                           partials != nullptr ? 8ull * ZERO_SUMSQ_PARTIALS : 0u};
+    return disjoint(p, b, 4);
+}
+
 bool finite(float x) { return std::isfinite(x); }
 
 bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; }
@@ -90,7 +100,8 @@ int check_args(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n, uint32_
 // g_align its element size (2 for 16-bit, 4 for FP32 gradients).
 int step_args(void *w16, const void *g, uintptr_t g_align, float *master, float *m, float *v,
               zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank, float lr, float beta1,
-              float beta2, float eps, float weight_decay, uint64_t *count, zs::AdamScalars *s) {
+              float beta2, float eps, float weight_decay, const void *ctl, uint64_t ctl_bytes,
+              uint64_t *count, zs::AdamScalars *s) {
     if (dt != ZERO_F16 && dt != ZERO_BF16) return ZERO_EDTYPE;
     zero_layout lay;
     if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
@@ -103,10 +114,12 @@ int step_args(void *w16, const void *g, uintptr_t g_align, float *master, float 
         if (!aligned(w16, 2) || !aligned(g, g_align) || !aligned(master, 4) || !aligned(m, 4) ||
             !aligned(v, 4))
             return ZERO_EINVAL;
-        const void *views[5] = {w16, g, master, m, v};
+        // the five views, and the flag or control block every block reads
+        const void *views[6] = {w16, g, master, m, v, ctl};
         const uint64_t c = lay.count;
-        const uint64_t bytes[5] = {2 * c, g_align * c, 4 * c, 4 * c, 4 * c};
-        if (!disjoint(views, bytes, 5)) return ZERO_EINVAL;
+        const uint64_t bytes[6] = {2 * c, g_align * c, 4 * c, 4 * c, 4 * c,
+                                   ctl != nullptr ? ctl_bytes : 0};
+        if (!disjoint(views, bytes, 6)) return ZERO_EINVAL;
     }
     s->lr = lr;
     s->beta1 = beta1;
@@ -143,6 +156,9 @@ extern "C" int zero_overflow_check(const void *g16, zero_dtype dt, uint64_t psi,
     if (d_sumsq != nullptr &&
         (!aligned(d_sumsq, 4) || d_partials == nullptr || !aligned(d_partials, 8)))
         return ZERO_EINVAL;
+    if (!check_outputs_ok(g16, 2 * count, d_found_inf, 4, d_sumsq,
+                          d_sumsq != nullptr ? d_partials : nullptr))
+        return ZERO_EINVAL;
     int cus = 0;
     rc = device_cus(&cus);
     if (rc != ZERO_OK) return rc;
@@ -160,7 +176,7 @@ extern "C" int zero_adam_step(void *w16, const void *g16, float *master, float *
     uint64_t count = 0;
     zs::AdamScalars s;
     const int rc = step_args(w16, g16, 2, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
-                             weight_decay, &count, &s);
+                             weight_decay, d_found_inf, 4, &count, &s);
     if (rc != ZERO_OK) return rc;
     if (step == 0) return ZERO_EINVAL;
     if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
@@ -200,6 +216,9 @@ extern "C" int zero_overflow_check_g32(const float *g32, uint64_t psi, uint32_t 
     if (d_sumsq != nullptr &&
         (!aligned(d_sumsq, 4) || d_partials == nullptr || !aligned(d_partials, 8)))
         return ZERO_EINVAL;
+    if (!check_outputs_ok(g32, 4 * lay.count, d_found_inf, 4, d_sumsq,
+                          d_sumsq != nullptr ? d_partials : nullptr))
+        return ZERO_EINVAL;
     int cus = 0;
     const int rc = device_cus(&cus);
     if (rc != ZERO_OK) return rc;
@@ -217,7 +236,7 @@ extern "C" int zero_adam_step_g32(void *w16, const float *g32, float *master, fl
     uint64_t count = 0;
     zs::AdamScalars s;
     const int rc = step_args(w16, g32, 4, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
-                             weight_decay, &count, &s);
+                             weight_decay, d_found_inf, 4, &count, &s);
     if (rc != ZERO_OK) return rc;
     if (step == 0) return ZERO_EINVAL;
     if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
@@ -308,6 +327,8 @@ extern "C" int zero_overflow_check_dev(const void *g16, zero_dtype dt, uint64_t 
     int rc = check_args(g16, dt, psi, n, rank, &count);
     if (rc != ZERO_OK) return rc;
     if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
+    if (!check_outputs_ok(g16, 2 * count, d_ctl, sizeof(zero_device_ctl), nullptr, nullptr))
+        return ZERO_EINVAL;
     int cus = 0;
     rc = device_cus(&cus);
     if (rc != ZERO_OK) return rc;
@@ -335,7 +356,7 @@ extern "C" int zero_adam_step_dev(void *w16, const void *g16, float *master, flo
     uint64_t count = 0;
     zs::AdamScalars s;
     const int rc = step_args(w16, g16, 2, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
-                             weight_decay, &count, &s);
+                             weight_decay, d_ctl, sizeof(zero_device_ctl), &count, &s);
     if (rc != ZERO_OK) return rc;
     if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
     if (count == 0) return ZERO_OK;
