@@ -477,3 +477,5 @@ def test_flag_control_and_check_outputs_may_not_overlap_the_views():
     # the device control block inside the working weights
     assert zs.lib.zero_adam_step_dev(FAKE, FAKE * 2, FAKE * 4, FAKE * 8, FAKE * 12, 0, 400, 4, 0,
                                      1e-3, 0.9, 0.999, 1e-8, 0.0, FAKE + 64, None) == -1
+    # the bias table over the control block the decision writes
+    assert zs.lib.zero_scaler_update_dev(FAKE * 8, FAKE * 8 + 16, 1, 4, None) == -1

@@ -343,6 +343,7 @@ extern "C" int zero_scaler_update_dev(zero_device_ctl *d_ctl, const float *d_bia
                                       uint64_t t_first, uint32_t len, void *stream) {
     if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
     if (d_bias == nullptr || !aligned(d_bias, 4) || len == 0 || t_first == 0) return ZERO_EINVAL;
+    if (overlap(d_ctl, sizeof(zero_device_ctl), d_bias, 8ull * len)) return ZERO_EINVAL;
     const hipError_t e =
         zs::launch_scaler_decide(d_ctl, d_bias, t_first, len, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_scaler_update_dev launch");
