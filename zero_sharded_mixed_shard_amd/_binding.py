@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -145,7 +146,9 @@ class Layout:
     bytes_z3: int
 
 
+@functools.lru_cache(maxsize=4096)
 def zero_shard_layout(psi: int, n: int, rank: int) -> Layout:
+    """The layout of (psi, n, rank); results are cached (Layout is immutable)."""
     out = _Layout()
     rc = lib.zero_shard_layout(psi, n, rank, ctypes.byref(out))
     if rc != 0:
@@ -153,8 +156,15 @@ def zero_shard_layout(psi: int, n: int, rank: int) -> Layout:
     return Layout(*(getattr(out, f) for f, _ in _Layout._fields_))
 
 
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(stream, device) -> int:
+    """hipStream_t of `stream`, or of torch's current stream on `device`."""
     if stream is None:
+        if _raw_current_stream is not None:
+            return int(_raw_current_stream(device.index if device.index is not None
+                                           else torch.cuda.current_device()))
         stream = torch.cuda.current_stream(device)
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
