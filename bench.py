@@ -404,7 +404,7 @@ def main():
                     help="GPUs (only 1: the step runs on one rank's shard)")
     ap.add_argument("--steps", type=int, default=5, help="timed steps")
     ap.add_argument("--warmup", type=int, default=2, help="untimed steps before them")
-    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5, 6],
                     help="workload id (4 = 1e10 params, N=1; the reported configuration)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle baseline")

@@ -202,6 +202,10 @@ WORKLOADS = {
                 1e-4, 0.9, 0.999, 1e-8, 0.1, 65536.0, 5, 1e-3),
     5: Workload(5, "ragged8.81B_n64_rank63_f16_adam_overflow", 8_810_000_003, 64, (63,), "f16",
                 1e-3, 0.9, 0.999, 1e-8, 0.0, 65536.0, 10, 1e-3, inject_prob=1e-7),
+    # the pages' plain data-parallel example: 1.5e9 parameters, all 16 B/param
+    # of state on one rank (24 GB)
+    6: Workload(6, "flat1.5B_n1_bf16_adamw", 1_500_000_000, 1, (0,), "bf16",
+                3e-4, 0.9, 0.999, 1e-8, 0.01, 1.0, 10, 1e-4),
 }
 
 

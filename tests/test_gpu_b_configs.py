@@ -1,4 +1,4 @@
-"""GPU parity on the five workloads at their real sizes.
+"""GPU parity on the six workloads at their real sizes.
 
 C1 (1M params, rank 3 of 8)    three ZeRO layouts, every element, all agree bitwise
 C2 (GPT-2-small shapes, N=8)  every element of all 8 ranks for 10 steps, and the
@@ -9,6 +9,8 @@ C4 (1e10, N=1, 160 GB)        the whole buffer, 5 steps, windows up to the last 
 C5 (8,810,000,003, N=64)      rank 63's ragged shard (61 padding elements, start = 5 mod 8),
                               10 steps with inf/NaN injection on even steps: every flag,
                               every element, S halving and t bit-exact against the oracle
+C6 (1.5e9, N=1, BF16, 24 GB)  the whole buffer, 10 steps, sampled windows, and at every
+                              element w16 = RNE16(master) and v >= 0
 
 Inputs come from `synth` (seeded); expected values only from `oracle`.
 """
@@ -280,6 +282,52 @@ def test_c4_ten_billion_unsharded_windows():
     g16[far] = keep
     zs.zero_overflow_check(g16, psi, 1, 0, S, flag)
     assert flag.item() == 0
+
+
+def test_c6_one_and_a_half_billion_unsharded_windows():
+    # the pages' plain data-parallel example: 1.5e9 parameters, 16 B each on one rank
+    w = synth.WORKLOADS[6]
+    psi, hp, S = w.psi, hp_of(w), w.loss_scale
+    lay = zs.zero_shard_layout(psi, 1, 0)
+    assert lay.count == psi and lay.bytes_dp == 24_000_000_000
+    log(f"C6 allocating 5 x {psi} elements (24 GB)")
+    master = synth.fill_normal_(torch.empty(psi, device=DEV), w.master_std, synth.seed_of(6, 2))
+    m = torch.zeros(psi, device=DEV)
+    v = torch.zeros(psi, device=DEV)
+    g16 = torch.empty(psi, dtype=torch.bfloat16, device=DEV)
+    w16 = torch.zeros(psi, dtype=torch.bfloat16, device=DEV)
+    wins = windows_of(psi, np.random.default_rng(6))
+    assert wins[-1][1] == psi
+    host = [dict(master=a, m=np.zeros(a.size, np.float32), v=np.zeros(a.size, np.float32),
+                 w16=np.zeros(a.size, np.uint16)) for a in take(master, wins, f32)]
+    flag = flag_buf()
+    steps = list(range(1, w.steps + 1))
+    gsteps = []
+    for t in steps:
+        synth.fill_normal_(g16, w.grad_std, synth.seed_of(6, 1, t))
+        gsteps.append(take(g16, wins, u16))
+        zs.zero_overflow_check(g16, psi, 1, 0, S, flag)
+        zs.zero_adam_step(w16, g16, master, m, v, psi, 1, 0, step=t, loss_scale=S,
+                          found_inf=flag, **hp)
+    torch.cuda.synchronize()
+    assert flag.item() == 0
+    log("C6 GPU steps done; oracle on windows")
+    run_windows_oracle(host, gsteps, "bf16", hp, steps, S)
+    got = [dict(master=a, m=b, v=c, w16=d) for a, b, c, d in
+           zip(take(master, wins, f32), take(m, wins, f32), take(v, wins, f32),
+               take(w16, wins, u16))]
+    cat = lambda lst, k: np.concatenate([x[k] for x in lst])
+    keys = ("master", "m", "v", "w16")
+    log("  C6 windows", assert_close({k: cat(got, k) for k in keys},
+                                     {k: cat(host, k) for k in keys}, "bf16", "C6"))
+    # at every element: the working weights are the master weights rounded to
+    # nearest even in BF16, and v >= 0 (squares only)
+    chunk = 1 << 28
+    for a in range(0, psi, chunk):
+        b = min(psi, a + chunk)
+        rne = master[a:b].to(torch.bfloat16).view(torch.int16)
+        assert torch.equal(rne, w16[a:b].view(torch.int16)), a
+        assert bool((v[a:b] >= 0).all()), a
 
 
 # ---------------------------------------------------------------------------
