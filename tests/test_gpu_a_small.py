@@ -196,8 +196,9 @@ def check_case(bits: np.ndarray, dtype, phase, S, sumsq=True):
     ref_flag, ref_s = oracle.overflow_check(bits, dtype, S)
     assert int(flag.item()) == ref_flag, (count, phase, S)
     if sumsq and ref_flag == 0:
-        assert oracle.ulp_distance32(np.float32(s.item()), np.float32(ref_s)).max() <= 1, \
-            (s.item(), ref_s)
+        with np.errstate(over="ignore"):  # a sum past the FP32 range rounds to inf on both sides
+            want = np.float32(ref_s)
+        assert oracle.ulp_distance32(np.float32(s.item()), want).max() <= 1, (s.item(), ref_s)
     assert gv.guards_intact()
     return int(flag.item()), (s.item() if sumsq else None)
 
