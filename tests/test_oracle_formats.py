@@ -2,8 +2,8 @@
 
 The oracle converts from the IEEE field definitions.  Pins: numpy's float16
 (IEEE binary16, round to nearest even) and torch's CPU bfloat16 (round to
-nearest even) on every 16-bit pattern and on every rounding case class of
-FP32 inputs, plus the format table the first page prints
+nearest even) on every 16-bit pattern, on every rounding case class of FP32
+inputs and on all 2^32 FP32 patterns, plus the format table the first page prints
 (tests/golden/formats.tsv) and its lost-update example
 (tests/golden/lost_update.tsv).
 """
@@ -103,6 +103,48 @@ def test_encode_bf16_rounding_cases_and_random():
     nan = np.isnan(x)
     assert np.array_equal(got[~nan], ref[~nan])
     assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all(got[nan] & 0x0040)
+
+
+def _every_fp32_pattern(fmt, reference):
+    """oracle.encode16 against a reference on all 2^32 FP32 bit patterns.
+
+    Non-NaN inputs must give the reference's bits; NaN inputs a quiet NaN of
+    the same sign.  Chunks run on a thread pool (the conversions release the
+    interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    chunk = 1 << 20
+    exp_field, quiet = (0x7C00, 0x0200) if fmt == "f16" else (0x7F80, 0x0040)
+    offsets = np.arange(chunk, dtype=np.uint32)
+
+    def run(c):
+        bits = offsets + np.uint32(c * chunk)
+        x = bits.view(np.float32)
+        got = oracle.encode16(x, fmt)
+        want = reference(x)
+        nan = np.isnan(x)
+        bad = np.count_nonzero(got[~nan] != want[~nan])
+        bad += np.count_nonzero(((got[nan] & exp_field) != exp_field) | ((got[nan] & quiet) == 0) |
+                                ((got[nan] >> 15) != (bits[nan] >> 31)))
+        return bad
+
+    workers = min(8, os.cpu_count() or 1)
+    with ThreadPoolExecutor(workers) as pool:
+        bad = sum(pool.map(run, range((1 << 32) // chunk)))
+    assert bad == 0
+
+
+def test_encode_f16_every_fp32_pattern():
+    def ref(x):
+        with np.errstate(over="ignore"):
+            return x.astype(np.float16).view(np.uint16)
+    _every_fp32_pattern("f16", ref)
+
+
+def test_encode_bf16_every_fp32_pattern():
+    def ref(x):
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    _every_fp32_pattern("bf16", ref)
 
 
 def test_subnormal_f16_survives():
