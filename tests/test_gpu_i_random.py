@@ -6,7 +6,10 @@ a 16-bit format, hyperparameters (including beta = 0, eps = 0, wd = 0 and
 negative lr), a loss scale (powers of two and not), a gradient spread from
 deep in the FP16 subnormal range to values that overflow after unscaling,
 and sometimes planted inf/NaN.  The flag, the skip-or-apply decision and
-the state after up to three steps must meet the parity bar.
+the state after up to three steps must meet the parity bar.  Further sweeps
+cover the FP32-gradient path, the reduce-scatter and all-gather stand-ins
+(random rank counts, formats, phases, shards in place) and device-controlled
+schedules.
 """
 import numpy as np
 import pytest
@@ -162,6 +165,44 @@ def test_random_fp32_gradients_device_control_and_exchanges():
         assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (case, psi, n, fin, fout)
         assert out.guards_intact()
     log("random FP32-gradient and exchange sweep: 120 cases")
+
+
+def test_random_gathers():
+    # random rank counts, formats and phases; some shards already in place in the
+    # full buffer; the padded tail and every guard must come back untouched
+    rng = np.random.default_rng(9090)
+    tdi = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+    host = lambda t, fmt: f32(t) if fmt == "f32" else u16(t)
+    in_place = 0
+    for case in range(80):
+        psi = int(rng.integers(1, 150_000))
+        n = int(rng.integers(1, 17))
+        fmt = str(rng.choice(["f16", "bf16", "f32"]))
+        lays = [zs.zero_shard_layout(psi, n, k) for k in range(n)]
+        total = lays[0].padded_total
+        full = GuardedView(total, tdi[fmt], int(rng.integers(0, 8)), DEV)
+        full.view.copy_(synth.fill_normal_(torch.empty(total, dtype=tdi[fmt]), 1.0,
+                                           31_000 + case).to(DEV))
+        shards, owners, hshards = [], [], []
+        for k, lay in enumerate(lays):
+            vals = synth.fill_normal_(torch.empty(lay.count, dtype=tdi[fmt]), 1e-2,
+                                      32_000 + 100 * case + k)
+            hshards.append(host(vals, fmt))
+            if lay.count and rng.random() < 0.3:
+                view = full.view[lay.offset:lay.offset + lay.count]
+                in_place += 1
+            else:
+                owners.append(GuardedView(lay.count, tdi[fmt], int(rng.integers(0, 8)), DEV))
+                view = owners[-1].view
+            view.copy_(vals.to(DEV))
+            shards.append(view)
+        want = oracle.gather_shards(hshards, psi, n, host(full.view, fmt))
+        zs.zero_gather_shards(full.view, shards, psi, n)
+        got = host(full.view, fmt)
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (case, psi, n, fmt)
+        assert full.guards_intact() and all(o.guards_intact() for o in owners), case
+    assert in_place > 0
+    log(f"random gathers: 80 cases, {in_place} shards in place")
 
 
 def test_random_device_control_schedules():
