@@ -376,6 +376,25 @@ int zero_adam_step_dev(void *w16, const void *g16, float *master, float *m, floa
                        float beta1, float beta2, float eps, float weight_decay,
                        const zero_device_ctl *d_ctl, void *stream);
 
+/*
+ * zero_overflow_check_g32_dev, zero_adam_step_g32_dev -- the device-resident
+ * sequence over FP32 gradients (an FP32 micro-batch accumulator; "How far
+ * does splitting the batch get you?", "What does gradient accumulation
+ * actually buy?"): zero_overflow_check_g32 with S read from
+ * d_ctl->scaler.loss_scale and the flag written to d_ctl->found_inf (no sum
+ * of squares), and zero_adam_step_g32 with S and the bias corrections read
+ * from d_ctl, writing nothing unless d_ctl->apply is set.  The decision
+ * between them is zero_scaler_update_dev.  Arguments, alignment, overlap
+ * rules and errors are as for the host-controlled forms and
+ * zero_overflow_check_dev / zero_adam_step_dev.
+ */
+int zero_overflow_check_g32_dev(const float *g32, uint64_t psi, uint32_t n, uint32_t rank,
+                                zero_device_ctl *d_ctl, void *stream);
+int zero_adam_step_g32_dev(void *w16, const float *g32, float *master, float *m, float *v,
+                           zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank, float lr,
+                           float beta1, float beta2, float eps, float weight_decay,
+                           const zero_device_ctl *d_ctl, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Sharded checkpoints: each rank writes its own slice of the model states to
  * its own file, in parallel with the others ("Stop Replicating What You Can

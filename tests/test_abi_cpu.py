@@ -270,6 +270,31 @@ def test_device_path_argument_errors():
     assert "table" in zs.zero_strerror(-4)
 
 
+def test_fp32_gradient_device_path_argument_errors():
+    L = zs.lib
+    # check: layout, null or misaligned control block, null or misaligned gradients,
+    # the control block inside the gradients
+    assert L.zero_overflow_check_g32_dev(FAKE, 100, 4, 4, FAKE, None) == -1
+    assert L.zero_overflow_check_g32_dev(FAKE, 100, 4, 0, None, None) == -1
+    assert L.zero_overflow_check_g32_dev(FAKE, 100, 4, 0, FAKE + 4, None) == -1
+    assert L.zero_overflow_check_g32_dev(None, 100, 4, 0, FAKE, None) == -1
+    assert L.zero_overflow_check_g32_dev(FAKE + 2, 100, 4, 0, FAKE * 4, None) == -1
+    assert L.zero_overflow_check_g32_dev(FAKE, 400, 4, 0, FAKE + 64, None) == -1
+    # step: the control block is required, the hyperparameters and views are checked
+    p = (FAKE, FAKE * 2, FAKE * 4, FAKE * 8, FAKE * 12)
+    hp = (1e-3, 0.9, 0.999, 1e-8, 0.0)
+    assert L.zero_adam_step_g32_dev(*p, 0, 100, 4, 0, *hp, None, None) == -1
+    assert L.zero_adam_step_g32_dev(*p, 0, 100, 4, 0, 1e-3, 1.0, 0.999, 1e-8, 0.0, FAKE * 16,
+                                    None) == -1
+    assert L.zero_adam_step_g32_dev(*p, 2, 100, 4, 0, *hp, FAKE * 16, None) == -2
+    assert L.zero_adam_step_g32_dev(FAKE, FAKE + 8, *p[2:], 0, 100, 4, 0, *hp, FAKE * 16,
+                                    None) == -1                    # g32 overlaps w16
+    assert L.zero_adam_step_g32_dev(*p, 0, 400, 4, 0, *hp, FAKE * 2 + 64, None) == -1
+    # empty rank: no launch
+    assert L.zero_adam_step_g32_dev(None, None, None, None, None, 0, 10, 8, 7, *hp, FAKE,
+                                    None) == 0
+
+
 @pytest.mark.parametrize("psi,n", [(8_810_000_000, 8), (8_810_000_000, 64), (10**9, 8),
                                    (12345, 7), (1, 1), (2**56, 4096)])
 def test_comm_volume_matches_oracle(psi, n):

@@ -24,6 +24,8 @@ FP32 gradients (accumulated across micro-batches):
     zero_grad_accumulate(acc32, g16, psi, n, rank, first)
     zero_overflow_check_g32(g32, psi, n, rank, loss_scale, found_inf, sumsq=None, partials=None)
     zero_adam_step_g32(w16, g32, master, m, v, psi, n, rank, *, lr, ..., step, loss_scale)
+    zero_overflow_check_g32_dev(g32, psi, n, rank, ctl)        # device-resident control
+    zero_adam_step_g32_dev(w16, g32, master, m, v, psi, n, rank, lr=..., ..., ctl=ctl)
 
 The exchanges around the step on one GPU, and their accounting:
 
@@ -64,6 +66,7 @@ from ._binding import (  # noqa: F401
     zero_adam_step,
     zero_adam_step_dev,
     zero_adam_step_g32,
+    zero_adam_step_g32_dev,
     zero_bias_corrections,
     zero_ckpt_read,
     zero_ckpt_read_info,
@@ -76,6 +79,7 @@ from ._binding import (  # noqa: F401
     zero_overflow_check,
     zero_overflow_check_dev,
     zero_overflow_check_g32,
+    zero_overflow_check_g32_dev,
     zero_peak_memory,
     zero_reduce_shard,
     zero_reshard_plan,
@@ -105,6 +109,8 @@ __all__ = [
     "zero_grad_accumulate",
     "zero_overflow_check_g32",
     "zero_adam_step_g32",
+    "zero_overflow_check_g32_dev",
+    "zero_adam_step_g32_dev",
     "zero_reduce_shard",
     "zero_gather_shards",
     "zero_comm_volume",

@@ -113,6 +113,11 @@ lib.zero_scaler_update_dev.restype = _i32
 lib.zero_adam_step_dev.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32, _u32, _f32, _f32,
                                    _f32, _f32, _f32, _vp, _vp]
 lib.zero_adam_step_dev.restype = _i32
+lib.zero_overflow_check_g32_dev.argtypes = [_vp, _u64, _u32, _u32, _vp, _vp]
+lib.zero_overflow_check_g32_dev.restype = _i32
+lib.zero_adam_step_g32_dev.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32, _u32, _f32,
+                                       _f32, _f32, _f32, _f32, _vp, _vp]
+lib.zero_adam_step_g32_dev.restype = _i32
 lib.zero_set_grid_cap.argtypes = [_u32]
 lib.zero_set_grid_cap.restype = _i32
 lib.zero_strerror.argtypes = [_i32]
@@ -416,6 +421,41 @@ def zero_adam_step_g32(w16: torch.Tensor, g32: torch.Tensor, master: torch.Tenso
                                     _stream_handle(stream, dev))
     if rc != 0:
         raise ZeroError(rc, "zero_adam_step_g32")
+
+
+def zero_overflow_check_g32_dev(g32: torch.Tensor, psi: int, n: int, rank: int,
+                                ctl: torch.Tensor, stream=None) -> None:
+    """Overflow check of FP32 gradients with S read on the device; writes ctl.found_inf."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g32.device
+    p_g = _view(g32, "g32", (torch.float32,), lay.count, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_overflow_check_g32_dev(p_g, psi, n, rank, _ctl_ptr(ctl, dev),
+                                             _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_overflow_check_g32_dev")
+
+
+def zero_adam_step_g32_dev(w16: torch.Tensor, g32: torch.Tensor, master: torch.Tensor,
+                           m: torch.Tensor, v: torch.Tensor, psi: int, n: int, rank: int, *,
+                           lr: float, beta1: float, beta2: float, eps: float,
+                           weight_decay: float, ctl: torch.Tensor, stream=None) -> None:
+    """Adam step on FP32 gradients with S and the bias corrections read from the control block."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g32.device
+    ptrs = [
+        _view(w16, "w16", _DTYPES, lay.count, dev),
+        _view(g32, "g32", (torch.float32,), lay.count, dev),
+        _view(master, "master", (torch.float32,), lay.count, dev),
+        _view(m, "m", (torch.float32,), lay.count, dev),
+        _view(v, "v", (torch.float32,), lay.count, dev),
+    ]
+    with torch.cuda.device(dev):
+        rc = lib.zero_adam_step_g32_dev(*ptrs, _DTYPES[w16.dtype], psi, n, rank, lr, beta1,
+                                        beta2, eps, weight_decay, _ctl_ptr(ctl, dev),
+                                        _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_adam_step_g32_dev")
 
 
 # ---- exchanges on one GPU and accounting ------------------------------------------

@@ -223,7 +223,7 @@ extern "C" int zero_overflow_check_g32(const float *g32, uint64_t psi, uint32_t 
     const int rc = device_cus(&cus);
     if (rc != ZERO_OK) return rc;
     const hipError_t e =
-        zs::launch_overflow_check_g32(g32, lay.count, loss_scale, d_found_inf, d_sumsq,
+        zs::launch_overflow_check_g32(g32, lay.count, loss_scale, nullptr, d_found_inf, d_sumsq,
                                       d_partials, cus, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check_g32 launch");
 }
@@ -247,7 +247,7 @@ extern "C" int zero_adam_step_g32(void *w16, const float *g32, float *master, fl
     s.bc2 = bias_correction(beta2, step);
     const hipError_t e = zs::launch_adam_step_g32(static_cast<int>(dt),
                                                   static_cast<uint16_t *>(w16), g32, master, m, v,
-                                                  count, s, d_found_inf,
+                                                  count, s, d_found_inf, nullptr,
                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step_g32 launch");
 }
@@ -365,6 +365,42 @@ extern "C" int zero_adam_step_dev(void *w16, const void *g16, float *master, flo
         static_cast<int>(dt), static_cast<uint16_t *>(w16), static_cast<const uint16_t *>(g16),
         master, m, v, count, s, nullptr, d_ctl, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step_dev launch");
+}
+
+extern "C" int zero_overflow_check_g32_dev(const float *g32, uint64_t psi, uint32_t n,
+                                           uint32_t rank, zero_device_ctl *d_ctl, void *stream) {
+    zero_layout lay;
+    if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
+    if (lay.count > 0 && (g32 == nullptr || !aligned(g32, 4))) return ZERO_EINVAL;
+    if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
+    if (!check_outputs_ok(g32, 4 * lay.count, d_ctl, sizeof(zero_device_ctl), nullptr, nullptr))
+        return ZERO_EINVAL;
+    int cus = 0;
+    const int rc = device_cus(&cus);
+    if (rc != ZERO_OK) return rc;
+    const hipError_t e = zs::launch_overflow_check_g32(
+        g32, lay.count, 1.0f, &d_ctl->scaler.loss_scale, &d_ctl->found_inf, nullptr, nullptr, cus,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check_g32_dev launch");
+}
+
+extern "C" int zero_adam_step_g32_dev(void *w16, const float *g32, float *master, float *m,
+                                      float *v, zero_dtype dt, uint64_t psi, uint32_t n,
+                                      uint32_t rank, float lr, float beta1, float beta2,
+                                      float eps, float weight_decay, const zero_device_ctl *d_ctl,
+                                      void *stream) {
+    uint64_t count = 0;
+    zs::AdamScalars s;
+    const int rc = step_args(w16, g32, 4, master, m, v, dt, psi, n, rank, lr, beta1, beta2, eps,
+                             weight_decay, d_ctl, sizeof(zero_device_ctl), &count, &s);
+    if (rc != ZERO_OK) return rc;
+    if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
+    if (count == 0) return ZERO_OK;
+    const hipError_t e = zs::launch_adam_step_g32(static_cast<int>(dt),
+                                                  static_cast<uint16_t *>(w16), g32, master, m, v,
+                                                  count, s, nullptr, d_ctl,
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step_g32_dev launch");
 }
 
 extern "C" const char *zero_strerror(int code) {

@@ -47,19 +47,22 @@ hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count,
                                  const float *loss_scale_dev, int32_t *flag, float *sumsq,
                                  double *partials, int num_cus, hipStream_t stream);
 
-// The step with FP32 gradients (dtype: the working weights' format).
+// The step with FP32 gradients (dtype: the working weights' format); flag and
+// ctl as for launch_adam_step.
 hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, float *master,
                                 float *m, float *v, uint64_t count, const AdamScalars &s,
-                                const int32_t *flag, hipStream_t stream);
+                                const int32_t *flag, const zero_device_ctl *ctl,
+                                hipStream_t stream);
 
 // acc = float(g16) (first) or acc + float(g16), in FP32; count > 0.
 hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, uint64_t count,
                                   bool first, hipStream_t stream);
 
-// The check over FP32 gradients (count may be 0: only the outputs are cleared).
+// The check over FP32 gradients (count may be 0: only the outputs are cleared);
+// loss_scale_dev as for launch_overflow_check.
 hipError_t launch_overflow_check_g32(const float *g32, uint64_t count, float loss_scale,
-                                     int32_t *flag, float *sumsq, double *partials, int num_cus,
-                                     hipStream_t stream);
+                                     const float *loss_scale_dev, int32_t *flag, float *sumsq,
+                                     double *partials, int num_cus, hipStream_t stream);
 
 // Views of up to ZERO_MAX_LOCAL_RANKS replicas or shards, passed by value.
 constexpr uint32_t kMaxLocalRanks = 64;  // == ZERO_MAX_LOCAL_RANKS

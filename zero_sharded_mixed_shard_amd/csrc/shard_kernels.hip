@@ -695,10 +695,10 @@ hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float
 
 hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, float *master,
                                 float *m, float *v, uint64_t count, const AdamScalars &s,
-                                const int32_t *flag, hipStream_t stream) {
-    if (dtype == 0)
-        return adam_dispatch<0>(w16, g32, master, m, v, count, s, flag, nullptr, stream);
-    return adam_dispatch<1>(w16, g32, master, m, v, count, s, flag, nullptr, stream);
+                                const int32_t *flag, const zero_device_ctl *ctl,
+                                hipStream_t stream) {
+    if (dtype == 0) return adam_dispatch<0>(w16, g32, master, m, v, count, s, flag, ctl, stream);
+    return adam_dispatch<1>(w16, g32, master, m, v, count, s, flag, ctl, stream);
 }
 
 hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, uint64_t count,
@@ -724,13 +724,13 @@ hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count,
 }
 
 hipError_t launch_overflow_check_g32(const float *g32, uint64_t count, float loss_scale,
-                                     int32_t *flag, float *sumsq, double *partials, int num_cus,
-                                     hipStream_t stream) {
+                                     const float *loss_scale_dev, int32_t *flag, float *sumsq,
+                                     double *partials, int num_cus, hipStream_t stream) {
     check_init<<<1, 64, 0, stream>>>(flag, sumsq);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess || count == 0) return err;
-    return check_dispatch<float, 0>(g32, count, loss_scale, nullptr, flag, sumsq, partials,
-                                    num_cus, stream);
+    return check_dispatch<float, 0>(g32, count, loss_scale, loss_scale_dev, flag, sumsq,
+                                    partials, num_cus, stream);
 }
 
 hipError_t launch_scaler_decide(zero_device_ctl *ctl, const float *bias, uint64_t t_first,
