@@ -496,6 +496,18 @@ int zero_ckpt_read_resharded(const char *const *paths_old, uint32_t n_old, uint6
 int zero_set_grid_cap(uint32_t blocks);
 
 /*
+ * zero_set_step_occupancy -- resident blocks per compute unit of the step's
+ * vector kernel (both gradient formats, host or device control).  0 (the
+ * default) chooses by shard size: no cap below 2^28 elements, 3 blocks per
+ * CU from 2^28 -- fewer tiles in flight at once streamed faster on MI355X at
+ * those sizes.  1 to 7 caps every shard at that many; 8 or more removes the
+ * cap.  The cap is an LDS reservation the kernel does not use,
+ * so results are bitwise the same under every setting.  Process-wide; set it
+ * while no other thread is launching.  Returns ZERO_OK.
+ */
+int zero_set_step_occupancy(uint32_t blocks_per_cu);
+
+/*
  * zero_strerror -- text for a return code.  For ZERO_EHIP it names the HIP
  * error of the most recent failing call made by this thread.  The pointer
  * stays valid until this thread's next call into the library.

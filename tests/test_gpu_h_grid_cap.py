@@ -6,7 +6,8 @@ not fit in one GPU's memory with the step's five arrays, so these tests lower
 the grid cap with zero_set_grid_cap to 1, 3 and 7 blocks and check every
 kernel against the oracle at sizes of many tiles with ragged heads and tails:
 the step (vector and element-wise paths, 16-bit and FP32 gradients), the
-accumulate, the flag check and both exchanges.
+accumulate, the flag check and both exchanges.  The step's occupancy setting
+(zero_set_step_occupancy) must leave every result bit unchanged.
 """
 import numpy as np
 import pytest
@@ -124,3 +125,54 @@ def test_exchanges_tile_loop(cap):
         assert np.array_equal(got[:psi], want)
         assert np.all(got[psi:] == SENT16) and full.guards_intact()
     log(f"exchanges cap {cap}: bitwise")
+
+
+def test_step_occupancy_settings_change_nothing():
+    # The step's occupancy cap is an LDS reservation the kernel never touches:
+    # under every setting -- by size (0; a cap of 3 per CU at this size), 1, 2,
+    # 3 and no cap (8) -- the same inputs give the same bits, and windows
+    # match the oracle.  2^28 + 12,345 elements at phase 3, both formats.
+    count, phase = (1 << 28) + 12_345, 3
+    for dtype in ("f16", "bf16"):
+        td = TD[dtype]
+        g16 = synth.fill_normal_(torch.empty(count, dtype=td), 1e-3, 71_000)
+        master0 = synth.fill_normal_(torch.empty(count), 0.02, 71_001)
+        V = {k: GuardedView(count, td if k in ("g16", "w16") else torch.float32, phase, DEV)
+             for k in ("g16", "w16", "master", "m", "v")}
+        V["g16"].view.copy_(g16.to(DEV))
+        results = {}
+        try:
+            for occ in (0, 1, 2, 3, 8):
+                zs.zero_set_step_occupancy(occ)
+                V["master"].view.copy_(master0.to(DEV))
+                for k in ("m", "v", "w16"):
+                    V[k].view.zero_()
+                for t in (1, 2):
+                    zs.zero_adam_step(V["w16"].view, V["g16"].view, V["master"].view,
+                                      V["m"].view, V["v"].view, count, 1, 0, step=t,
+                                      loss_scale=1024.0, **HP)
+                torch.cuda.synchronize()
+                results[occ] = {k: V[k].view.clone() for k in ("w16", "master", "m", "v")}
+        finally:
+            torch.cuda.synchronize()
+            zs.zero_set_step_occupancy(0)
+        for occ in (1, 2, 3, 8):
+            for k in results[0]:
+                assert torch.equal(results[occ][k].view(torch.int16 if k == "w16" else
+                                                        torch.int32),
+                                   results[0][k].view(torch.int16 if k == "w16" else
+                                                      torch.int32)), (dtype, occ, k)
+        assert all(v.guards_intact() for v in V.values())
+        wins = [(0, 4096), (count // 2, count // 2 + 4096), (count - 4096, count)]
+        gh = u16(g16)
+        for a, b in wins:
+            ref = dict(master=master0[a:b].numpy().copy(), m=np.zeros(b - a, np.float32),
+                       v=np.zeros(b - a, np.float32), w16=np.zeros(b - a, np.uint16))
+            for t in (1, 2):
+                oracle.adam_step(ref["w16"], gh[a:b], ref["master"], ref["m"], ref["v"], dtype,
+                                 step=t, loss_scale=1024.0, **HP)
+            got = {k: (u16 if k == "w16" else f32)(results[0][k][a:b]) for k in ref}
+            assert_close(got, ref, dtype, f"occupancy window {a}")
+        del results, V
+        torch.cuda.empty_cache()
+    log("step occupancy settings 0/1/2/3/8: bitwise equal, windows match the oracle")

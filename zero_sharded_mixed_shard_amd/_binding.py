@@ -119,6 +119,8 @@ lib.zero_adam_step_g32_dev.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32
                                        _f32, _f32, _f32, _f32, _vp, _vp]
 lib.zero_adam_step_g32_dev.restype = _i32
 lib.zero_set_grid_cap.argtypes = [_u32]
+lib.zero_set_step_occupancy.argtypes = [_u32]
+lib.zero_set_step_occupancy.restype = _i32
 lib.zero_set_grid_cap.restype = _i32
 lib.zero_strerror.argtypes = [_i32]
 lib.zero_strerror.restype = ctypes.c_char_p
@@ -133,6 +135,11 @@ def zero_set_grid_cap(blocks: int) -> None:
     if not 0 <= blocks < 1 << 32:
         raise ValueError("blocks must fit in 32 bits")
     lib.zero_set_grid_cap(blocks)
+
+
+def zero_set_step_occupancy(blocks_per_cu: int) -> None:
+    """Resident step blocks per CU: 0 chooses by shard size, 1-7 cap, 8+ removes the cap."""
+    lib.zero_set_step_occupancy(blocks_per_cu)
 
 
 @dataclass(frozen=True)

@@ -24,26 +24,55 @@ int fail_hip(hipError_t e, const char *what) {
 
 // Compute units per device, queried once per device.
 constexpr int kMaxDevices = 64;
+// Per-device cache of the properties the launchers use; a zero compute-unit
+// count marks an entry not yet filled.  Each field is written once with the
+// same value by whichever thread gets there first, the CU count last.
 std::atomic<int> g_cus[kMaxDevices];
+std::atomic<int> g_lds_cu[kMaxDevices];
+std::atomic<int> g_lds_block[kMaxDevices];
 
-int device_cus(int *cus) {
+// Resident step blocks per CU set by zero_set_step_occupancy (0: by size).
+std::atomic<int> g_step_per_cu{0};
+
+int device_props(zs::DeviceProps *out) {
+    out->step_per_cu = g_step_per_cu.load(std::memory_order_relaxed);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-    if (dev >= 0 && dev < kMaxDevices) {
-        const int cached = g_cus[dev].load(std::memory_order_relaxed);
-        if (cached > 0) {
-            *cus = cached;
+    const bool cacheable = dev >= 0 && dev < kMaxDevices;
+    if (cacheable) {
+        const int cus = g_cus[dev].load(std::memory_order_acquire);
+        if (cus > 0) {
+            out->cus = cus;
+            out->lds_per_cu = g_lds_cu[dev].load(std::memory_order_relaxed);
+            out->lds_per_block = g_lds_block[dev].load(std::memory_order_relaxed);
             return ZERO_OK;
         }
     }
-    int n = 0;
+    int n = 0, lds_cu = 0, lds_block = 0;
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute");
     if (n <= 0) n = 1;
-    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(n, std::memory_order_relaxed);
-    *cus = n;
+    if (cacheable) {
+        g_lds_cu[dev].store(lds_cu, std::memory_order_relaxed);
+        g_lds_block[dev].store(lds_block, std::memory_order_relaxed);
+        g_cus[dev].store(n, std::memory_order_release);
+    }
+    out->cus = n;
+    out->lds_per_cu = lds_cu;
+    out->lds_per_block = lds_block;
     return ZERO_OK;
+}
+
+int device_cus(int *cus) {
+    zs::DeviceProps p;
+    const int rc = device_props(&p);
+    if (rc == ZERO_OK) *cus = p.cus;
+    return rc;
 }
 
 std::atomic<uint64_t> g_grid_cap{zs::kMaxBlocks};
@@ -145,6 +174,12 @@ extern "C" int zero_set_grid_cap(uint32_t blocks) {
     return ZERO_OK;
 }
 
+extern "C" int zero_set_step_occupancy(uint32_t blocks_per_cu) {
+    g_step_per_cu.store(blocks_per_cu >= 8 ? 8 : static_cast<int>(blocks_per_cu),
+                        std::memory_order_relaxed);
+    return ZERO_OK;
+}
+
 extern "C" int zero_overflow_check(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n,
                                    uint32_t rank, float loss_scale, int32_t *d_found_inf,
                                    float *d_sumsq, double *d_partials, void *stream) {
@@ -185,9 +220,12 @@ extern "C" int zero_adam_step(void *w16, const void *g16, float *master, float *
     s.loss_scale = loss_scale;
     s.bc1 = bias_correction(beta1, step);
     s.bc2 = bias_correction(beta2, step);
+    zs::DeviceProps dev;
+    const int prc = device_props(&dev);
+    if (prc != ZERO_OK) return prc;
     const hipError_t e = zs::launch_adam_step(
         static_cast<int>(dt), static_cast<uint16_t *>(w16), static_cast<const uint16_t *>(g16),
-        master, m, v, count, s, d_found_inf, nullptr, static_cast<hipStream_t>(stream));
+        master, m, v, count, s, d_found_inf, nullptr, dev, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step launch");
 }
 
@@ -245,9 +283,12 @@ extern "C" int zero_adam_step_g32(void *w16, const float *g32, float *master, fl
     s.loss_scale = loss_scale;
     s.bc1 = bias_correction(beta1, step);
     s.bc2 = bias_correction(beta2, step);
+    zs::DeviceProps dev;
+    const int prc = device_props(&dev);
+    if (prc != ZERO_OK) return prc;
     const hipError_t e = zs::launch_adam_step_g32(static_cast<int>(dt),
                                                   static_cast<uint16_t *>(w16), g32, master, m, v,
-                                                  count, s, d_found_inf, nullptr,
+                                                  count, s, d_found_inf, nullptr, dev,
                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step_g32 launch");
 }
@@ -361,9 +402,12 @@ extern "C" int zero_adam_step_dev(void *w16, const void *g16, float *master, flo
     if (rc != ZERO_OK) return rc;
     if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
     if (count == 0) return ZERO_OK;
+    zs::DeviceProps dev;
+    const int prc = device_props(&dev);
+    if (prc != ZERO_OK) return prc;
     const hipError_t e = zs::launch_adam_step(
         static_cast<int>(dt), static_cast<uint16_t *>(w16), static_cast<const uint16_t *>(g16),
-        master, m, v, count, s, nullptr, d_ctl, static_cast<hipStream_t>(stream));
+        master, m, v, count, s, nullptr, d_ctl, dev, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step_dev launch");
 }
 
@@ -396,9 +440,12 @@ extern "C" int zero_adam_step_g32_dev(void *w16, const float *g32, float *master
     if (rc != ZERO_OK) return rc;
     if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
     if (count == 0) return ZERO_OK;
+    zs::DeviceProps dev;
+    const int prc = device_props(&dev);
+    if (prc != ZERO_OK) return prc;
     const hipError_t e = zs::launch_adam_step_g32(static_cast<int>(dt),
                                                   static_cast<uint16_t *>(w16), g32, master, m, v,
-                                                  count, s, nullptr, d_ctl,
+                                                  count, s, nullptr, d_ctl, dev,
                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step_g32_dev launch");
 }

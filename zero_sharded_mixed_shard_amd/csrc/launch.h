@@ -32,12 +32,22 @@ constexpr uint64_t kMaxBlocks = 1ull << 23;
 // zero_set_grid_cap (tests use it to run the tile loops at small sizes).
 uint64_t max_blocks();
 
+// What the launchers need to know of the current device, and the step's
+// occupancy setting in force.
+struct DeviceProps {
+    int cus;              // compute units
+    int lds_per_cu;       // LDS bytes of one compute unit
+    int lds_per_block;    // largest LDS allocation of one workgroup
+    int step_per_cu;      // resident step blocks per CU: 0 = by shard size, else this cap
+};
+
 // Enqueue the Adam step over `count` elements of five shard views.  The
 // caller has validated every argument; count > 0.  flag (nullable): skip if
 // set.  ctl (nullable): skip unless ctl->apply, and take S, bc1, bc2 from it.
 hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float *master, float *m,
                             float *v, uint64_t count, const AdamScalars &s, const int32_t *flag,
-                            const zero_device_ctl *ctl, hipStream_t stream);
+                            const zero_device_ctl *ctl, const DeviceProps &dev,
+                            hipStream_t stream);
 
 // Enqueue the unscale + overflow check of `count` gradients (count may be 0:
 // then only the outputs are cleared).  partials holds ZERO_SUMSQ_PARTIALS
@@ -52,7 +62,7 @@ hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count,
 hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, float *master,
                                 float *m, float *v, uint64_t count, const AdamScalars &s,
                                 const int32_t *flag, const zero_device_ctl *ctl,
-                                hipStream_t stream);
+                                const DeviceProps &dev, hipStream_t stream);
 
 // acc = float(g16) (first) or acc + float(g16), in FP32; count > 0.
 hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, uint64_t count,

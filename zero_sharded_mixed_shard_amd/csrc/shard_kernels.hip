@@ -593,6 +593,26 @@ bool common_phase(const float *ref, const float *a, const float *b, const GT *g,
            g_ok && (h16 == nullptr || (addr(h16) + 2u * *head) % 8 == 0);
 }
 
+// Resident step blocks per CU.  One tile per block keeps the hardware
+// dispatcher feeding CUs in tile order; how many tiles are in flight at once
+// is set by reserving LDS the kernel does not use.  Measured on MI355X, the
+// same arrays in one process (TB/s, no cap / 3 per CU / 2 per CU): the
+// 937.5M-element BF16 rank 5.55-5.60 / 6.02-6.05 / 5.67; 1.5e9 elements
+// 5.46 / 5.77 / 5.60; 1e10 6.30-6.40 / 6.33-6.46 / 6.18-6.24.  Below 2^28
+// elements the cap gains nothing reliably (a 137.7M ragged rank: 5.85-5.93 /
+// 5.67 / 5.94; a 15.5M rank: 5.60-5.65 / 5.58 / 5.16-5.39).
+constexpr uint64_t kStepCapFrom = 1ull << 28;
+constexpr int kStepCapPerCU = 3;
+
+inline size_t step_lds_bytes(uint64_t count, const DeviceProps &dev) {
+    int per_cu = dev.step_per_cu;
+    if (per_cu == 0) per_cu = count >= kStepCapFrom ? kStepCapPerCU : 8;
+    if (per_cu <= 0 || per_cu >= 8 || dev.lds_per_cu <= 0) return 0;  // 8: the kernel's own limit
+    // one more block than per_cu would not fit
+    const size_t bytes = static_cast<size_t>(dev.lds_per_cu) / (per_cu + 1) + 256;
+    return bytes <= static_cast<size_t>(dev.lds_per_block) ? bytes : 0;
+}
+
 inline uint32_t grid_for(uint64_t need) {
     if (need == 0) need = 1;
     const uint64_t cap = max_blocks();
@@ -602,7 +622,8 @@ inline uint32_t grid_for(uint64_t need) {
 template <int DT, typename GT>
 hipError_t adam_dispatch(uint16_t *w16, const GT *g, float *master, float *m, float *v,
                          uint64_t count, const AdamScalars &s, const int32_t *flag,
-                         const zero_device_ctl *ctl, hipStream_t stream) {
+                         const zero_device_ctl *ctl, const DeviceProps &dev,
+                         hipStream_t stream) {
     uint32_t head = 0;
     if (!common_phase<GT>(master, m, v, g, w16, &head)) {
         adam_step_elem<DT, GT><<<grid_for((count + kThreads - 1) / kThreads), kThreads, 0,
@@ -614,8 +635,9 @@ hipError_t adam_dispatch(uint16_t *w16, const GT *g, float *master, float *m, fl
     const uint64_t n_tiles = (count - head) / kTile;
     const uint64_t rest = count - head - n_tiles * kTile;
     const uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
-    adam_step_vec<DT, GT, kAdamU><<<grid_for(need), kThreads, 0, stream>>>(
-        w16, g, master, m, v, count, head, n_tiles, s, flag, ctl);
+    adam_step_vec<DT, GT, kAdamU><<<grid_for(need), kThreads, step_lds_bytes(count, dev),
+                                    stream>>>(w16, g, master, m, v, count, head, n_tiles, s,
+                                              flag, ctl);
     return hipGetLastError();
 }
 
@@ -688,17 +710,20 @@ hipError_t check_dispatch(const GT *g, uint64_t count, float loss_scale,
 
 hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float *master, float *m,
                             float *v, uint64_t count, const AdamScalars &s, const int32_t *flag,
-                            const zero_device_ctl *ctl, hipStream_t stream) {
-    if (dtype == 0) return adam_dispatch<0>(w16, g16, master, m, v, count, s, flag, ctl, stream);
-    return adam_dispatch<1>(w16, g16, master, m, v, count, s, flag, ctl, stream);
+                            const zero_device_ctl *ctl, const DeviceProps &dev,
+                            hipStream_t stream) {
+    if (dtype == 0)
+        return adam_dispatch<0>(w16, g16, master, m, v, count, s, flag, ctl, dev, stream);
+    return adam_dispatch<1>(w16, g16, master, m, v, count, s, flag, ctl, dev, stream);
 }
 
 hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, float *master,
                                 float *m, float *v, uint64_t count, const AdamScalars &s,
                                 const int32_t *flag, const zero_device_ctl *ctl,
-                                hipStream_t stream) {
-    if (dtype == 0) return adam_dispatch<0>(w16, g32, master, m, v, count, s, flag, ctl, stream);
-    return adam_dispatch<1>(w16, g32, master, m, v, count, s, flag, ctl, stream);
+                                const DeviceProps &dev, hipStream_t stream) {
+    if (dtype == 0)
+        return adam_dispatch<0>(w16, g32, master, m, v, count, s, flag, ctl, dev, stream);
+    return adam_dispatch<1>(w16, g32, master, m, v, count, s, flag, ctl, dev, stream);
 }
 
 hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, uint64_t count,
