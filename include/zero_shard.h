@@ -498,10 +498,11 @@ int zero_set_grid_cap(uint32_t blocks);
 /*
  * zero_set_step_occupancy -- resident blocks per compute unit of the step's
  * vector kernel (both gradient formats, host or device control).  0 (the
- * default) chooses by shard size: no cap below 2^28 elements, 3 blocks per
- * CU from 2^28 -- fewer tiles in flight at once streamed faster on MI355X at
- * those sizes.  1 to 7 caps every shard at that many; 8 or more removes the
- * cap.  The cap is an LDS reservation the kernel does not use,
+ * default) chooses what measured fastest on MI355X: no cap below 2^28
+ * elements; from 2^28, 3 blocks per CU with BF16 working weights and 16-bit
+ * gradients, 2 with FP16 working weights (3 from 2^33 elements) and 2 with
+ * FP32 gradients.  1 to 7 caps every shard at that many; 8 or more removes
+ * the cap.  The cap is an LDS reservation the kernel does not use,
  * so results are bitwise the same under every setting.  Process-wide; set it
  * while no other thread is launching.  Returns ZERO_OK.
  */

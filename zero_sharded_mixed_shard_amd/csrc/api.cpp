@@ -237,9 +237,12 @@ extern "C" int zero_grad_accumulate(float *acc, const void *g16, zero_dtype dt, 
     if (count == 0) return ZERO_OK;
     if (acc == nullptr || !aligned(acc, 4)) return ZERO_EINVAL;
     if (overlap(acc, 4 * count, g16, 2 * count)) return ZERO_EINVAL;
+    zs::DeviceProps dev;
+    const int prc = device_props(&dev);
+    if (prc != ZERO_OK) return prc;
     const hipError_t e =
         zs::launch_grad_accumulate(static_cast<int>(dt), acc, static_cast<const uint16_t *>(g16),
-                                   count, first != 0, static_cast<hipStream_t>(stream));
+                                   count, first != 0, dev, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_grad_accumulate launch");
 }
 

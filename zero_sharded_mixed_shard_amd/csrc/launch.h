@@ -66,7 +66,7 @@ hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, floa
 
 // acc = float(g16) (first) or acc + float(g16), in FP32; count > 0.
 hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, uint64_t count,
-                                  bool first, hipStream_t stream);
+                                  bool first, const DeviceProps &dev, hipStream_t stream);
 
 // The check over FP32 gradients (count may be 0: only the outputs are cleared);
 // loss_scale_dev as for launch_overflow_check.

@@ -595,22 +595,60 @@ bool common_phase(const float *ref, const float *a, const float *b, const GT *g,
 
 // Resident step blocks per CU.  One tile per block keeps the hardware
 // dispatcher feeding CUs in tile order; how many tiles are in flight at once
-// is set by reserving LDS the kernel does not use.  Measured on MI355X, the
-// same arrays in one process (TB/s, no cap / 3 per CU / 2 per CU): the
-// 937.5M-element BF16 rank 5.55-5.60 / 6.02-6.05 / 5.67; 1.5e9 elements
-// 5.46 / 5.77 / 5.60; 1e10 6.30-6.40 / 6.33-6.46 / 6.18-6.24.  Below 2^28
-// elements the cap gains nothing reliably (a 137.7M ragged rank: 5.85-5.93 /
-// 5.67 / 5.94; a 15.5M rank: 5.60-5.65 / 5.58 / 5.16-5.39).
+// is set by reserving LDS the kernel does not use (the code and the bytes
+// moved are the same).  Fewer tiles in flight stream faster from 2^28
+// elements on; the best number differs between the kernels, not with the
+// size.  Measured on MI355X, the same arrays in one process, means of two
+// processes (TB/s; uncapped / 3 per CU / 2 per CU):
+//   FP16 weights, 16-bit gradients: 2^28 5.77 / 5.85 / 6.12; 2^30 5.87 /
+//     5.88 / 6.05; 2^32 5.80 / 5.88 / 6.08.  At 1e10, where the driver
+//     places 160 GB well, 3 per CU is best (6.30-6.40 / 6.33-6.46 /
+//     6.18-6.24; elsewhere 6.01 / 6.01 / 6.09).
+//   BF16 weights, 16-bit gradients: 2^28 5.65 / 6.24 / 5.72; 2^30 5.88 /
+//     6.05 / 5.77; 2^32 5.81 / 6.05 / 5.71; 1e10 5.98 / 6.06 / 5.75.
+//   FP32 gradients (either format): 2^28 5.69 / 5.85 / 6.19; 2^30 5.51 /
+//     5.69 / 6.07; 2^32 6.21 / 6.24 / 6.29.
+// Below 2^28 no cap helps reliably (a 137.7M ragged FP16 rank: 5.85-5.93
+// uncapped, 5.67 at 3, 5.94 at 2; a 15.5M rank: 5.60-5.65 / 5.58 /
+// 5.16-5.39).
 constexpr uint64_t kStepCapFrom = 1ull << 28;
-constexpr int kStepCapPerCU = 3;
+constexpr uint64_t kStepF16ThreeFrom = 1ull << 33;
 
-inline size_t step_lds_bytes(uint64_t count, const DeviceProps &dev) {
-    int per_cu = dev.step_per_cu;
-    if (per_cu == 0) per_cu = count >= kStepCapFrom ? kStepCapPerCU : 8;
-    if (per_cu <= 0 || per_cu >= 8 || dev.lds_per_cu <= 0) return 0;  // 8: the kernel's own limit
+template <int DT, typename GT>
+int step_blocks_per_cu(uint64_t count) {
+    if (count < kStepCapFrom) return 8;
+    if constexpr (sizeof(GT) == 4) return 2;  // FP32 gradients
+    if constexpr (DT == 1) return 3;          // BF16 weights
+    return count < kStepF16ThreeFrom ? 2 : 3;
+}
+// The accumulate (three streams, the same tiles) gains more from fewer blocks:
+// 2 per CU run 2^28 elements at 6.35-6.44 TB/s against 6.07-6.17 uncapped,
+// 2^30 at 6.37-6.40 against 5.84-5.91 and 2^32 at 6.33-6.39 against
+// 5.78-5.85; at 15.5M the cap loses (6.07-6.33 against 6.47-6.63).  The first
+// micro-batch (a 16-bit read and an FP32 write, nothing read back) wants 4:
+// 6.48-6.53 TB/s against 5.97-6.10 uncapped and 4.96-4.99 at 2 per CU, from
+// 2^28 to 2^32 elements.
+constexpr uint64_t kAccCapFrom = 1ull << 28;
+constexpr int kAccCapPerCU = 2;
+constexpr int kAccFirstCapPerCU = 4;
+
+// LDS to reserve so that at most per_cu blocks are resident on a CU (0: none).
+inline size_t cap_lds_bytes(int per_cu, const DeviceProps &dev) {
+    if (per_cu <= 0 || per_cu >= 8 || dev.lds_per_cu <= 0) return 0;  // 8: the kernels' own limit
     // one more block than per_cu would not fit
     const size_t bytes = static_cast<size_t>(dev.lds_per_cu) / (per_cu + 1) + 256;
     return bytes <= static_cast<size_t>(dev.lds_per_block) ? bytes : 0;
+}
+
+template <int DT, typename GT>
+size_t step_lds_bytes(uint64_t count, const DeviceProps &dev) {
+    const int per_cu = dev.step_per_cu != 0 ? dev.step_per_cu : step_blocks_per_cu<DT, GT>(count);
+    return cap_lds_bytes(per_cu, dev);
+}
+
+inline size_t accumulate_lds_bytes(uint64_t count, bool first, const DeviceProps &dev) {
+    if (count < kAccCapFrom) return 0;
+    return cap_lds_bytes(first ? kAccFirstCapPerCU : kAccCapPerCU, dev);
 }
 
 inline uint32_t grid_for(uint64_t need) {
@@ -635,7 +673,7 @@ hipError_t adam_dispatch(uint16_t *w16, const GT *g, float *master, float *m, fl
     const uint64_t n_tiles = (count - head) / kTile;
     const uint64_t rest = count - head - n_tiles * kTile;
     const uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
-    adam_step_vec<DT, GT, kAdamU><<<grid_for(need), kThreads, step_lds_bytes(count, dev),
+    adam_step_vec<DT, GT, kAdamU><<<grid_for(need), kThreads, step_lds_bytes<DT, GT>(count, dev),
                                     stream>>>(w16, g, master, m, v, count, head, n_tiles, s,
                                               flag, ctl);
     return hipGetLastError();
@@ -643,7 +681,7 @@ hipError_t adam_dispatch(uint16_t *w16, const GT *g, float *master, float *m, fl
 
 template <int DT, bool FIRST>
 hipError_t accumulate_dispatch(float *acc, const uint16_t *g16, uint64_t count,
-                               hipStream_t stream) {
+                               const DeviceProps &dev, hipStream_t stream) {
     uint32_t head = 0;
     if (!common_phase<uint16_t>(acc, acc, nullptr, g16, nullptr, &head)) {
         accumulate_elem<DT, FIRST><<<grid_for((count + kThreads - 1) / kThreads), kThreads, 0,
@@ -655,8 +693,9 @@ hipError_t accumulate_dispatch(float *acc, const uint16_t *g16, uint64_t count,
     const uint64_t n_tiles = (count - head) / kTile;
     const uint64_t rest = count - head - n_tiles * kTile;
     const uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
-    accumulate_vec<DT, FIRST, kAccU><<<grid_for(need), kThreads, 0, stream>>>(acc, g16, count,
-                                                                             head, n_tiles);
+    accumulate_vec<DT, FIRST, kAccU><<<grid_for(need), kThreads,
+                                       accumulate_lds_bytes(count, FIRST, dev), stream>>>(
+        acc, g16, count, head, n_tiles);
     return hipGetLastError();
 }
 
@@ -727,12 +766,12 @@ hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, floa
 }
 
 hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, uint64_t count,
-                                  bool first, hipStream_t stream) {
+                                  bool first, const DeviceProps &dev, hipStream_t stream) {
     if (dtype == 0)
-        return first ? accumulate_dispatch<0, true>(acc, g16, count, stream)
-                     : accumulate_dispatch<0, false>(acc, g16, count, stream);
-    return first ? accumulate_dispatch<1, true>(acc, g16, count, stream)
-                 : accumulate_dispatch<1, false>(acc, g16, count, stream);
+        return first ? accumulate_dispatch<0, true>(acc, g16, count, dev, stream)
+                     : accumulate_dispatch<0, false>(acc, g16, count, dev, stream);
+    return first ? accumulate_dispatch<1, true>(acc, g16, count, dev, stream)
+                 : accumulate_dispatch<1, false>(acc, g16, count, dev, stream);
 }
 
 hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
