@@ -498,8 +498,8 @@ int zero_set_grid_cap(uint32_t blocks);
 /*
  * zero_set_step_occupancy -- resident blocks per compute unit of the step's
  * vector kernel (both gradient formats, host or device control).  0 (the
- * default) chooses what measured fastest on MI355X: no cap below 2^28
- * elements; from 2^28, 3 blocks per CU with BF16 working weights and 16-bit
+ * default) chooses what measured fastest on MI355X: no cap below 2^26
+ * elements; from 2^26, 3 blocks per CU with BF16 working weights and 16-bit
  * gradients, 2 with FP16 working weights (3 from 2^33 elements) and 2 with
  * FP32 gradients.  1 to 7 caps every shard at that many; 8 or more removes
  * the cap.  The cap is an LDS reservation the kernel does not use,

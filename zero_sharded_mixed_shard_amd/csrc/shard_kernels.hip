@@ -596,22 +596,24 @@ bool common_phase(const float *ref, const float *a, const float *b, const GT *g,
 // Resident step blocks per CU.  One tile per block keeps the hardware
 // dispatcher feeding CUs in tile order; how many tiles are in flight at once
 // is set by reserving LDS the kernel does not use (the code and the bytes
-// moved are the same).  Fewer tiles in flight stream faster from 2^28
+// moved are the same).  Fewer tiles in flight stream faster from 2^26
 // elements on; the best number differs between the kernels, not with the
 // size.  Measured on MI355X, the same arrays in one process, means of two
 // processes (TB/s; uncapped / 3 per CU / 2 per CU):
-//   FP16 weights, 16-bit gradients: 2^28 5.77 / 5.85 / 6.12; 2^30 5.87 /
-//     5.88 / 6.05; 2^32 5.80 / 5.88 / 6.08.  At 1e10, where the driver
-//     places 160 GB well, 3 per CU is best (6.30-6.40 / 6.33-6.46 /
-//     6.18-6.24; elsewhere 6.01 / 6.01 / 6.09).
-//   BF16 weights, 16-bit gradients: 2^28 5.65 / 6.24 / 5.72; 2^30 5.88 /
-//     6.05 / 5.77; 2^32 5.81 / 6.05 / 5.71; 1e10 5.98 / 6.06 / 5.75.
-//   FP32 gradients (either format): 2^28 5.69 / 5.85 / 6.19; 2^30 5.51 /
-//     5.69 / 6.07; 2^32 6.21 / 6.24 / 6.29.
-// Below 2^28 no cap helps reliably (a 137.7M ragged FP16 rank: 5.85-5.93
-// uncapped, 5.67 at 3, 5.94 at 2; a 15.5M rank: 5.60-5.65 / 5.58 /
-// 5.16-5.39).
-constexpr uint64_t kStepCapFrom = 1ull << 28;
+//   FP16 weights, 16-bit gradients: 67M 5.84 / 5.88 / 5.95; 137.7M 5.69 /
+//     5.64 / 5.90; 2^28 5.77 / 5.85 / 6.12; 2^30 5.87 / 5.88 / 6.05; 2^32
+//     5.80 / 5.88 / 6.08.  At 1e10, where the driver places 160 GB well,
+//     3 per CU is best (6.30-6.40 / 6.33-6.46 / 6.18-6.24; elsewhere
+//     6.01 / 6.01 / 6.09).
+//   BF16 weights, 16-bit gradients: 67M 5.71 / 6.08 / 5.64; 137.7M 5.57 /
+//     5.92 / 5.60; 2^28 5.65 / 6.24 / 5.72; 2^30 5.88 / 6.05 / 5.77; 2^32
+//     5.81 / 6.05 / 5.71; 1e10 5.98 / 6.06 / 5.75.
+//   FP32 gradients (either format): 137.7M 5.62 / 5.72-5.79 / 6.01-6.08;
+//     2^28 5.69 / 5.85 / 6.19; 2^30 5.51 / 5.69 / 6.07; 2^32 6.21 / 6.24 /
+//     6.29.
+// At 15.5M elements a cap gains nothing (FP16: 5.60-5.65 uncapped, 5.58
+// at 3, 5.16-5.39 at 2).
+constexpr uint64_t kStepCapFrom = 1ull << 26;
 constexpr uint64_t kStepF16ThreeFrom = 1ull << 33;
 
 template <int DT, typename GT>
