@@ -188,7 +188,8 @@ def measure_extras(dev, n_elem: int = 1 << 30, reps: int = 5) -> dict:
     """Bandwidth of the path's other kernels on n_elem-element shards (HIP events).
 
     Algorithmic bytes per element: accumulate 10 (read 2 + 4, write 4), FP32
-    check 4, 16-bit check with the sum of squares 2 (S a power of two, and S = 3),
+    check 4, accumulate with the FP32 check fused 10, 16-bit check with the sum
+    of squares 2 (S a power of two, and S = 3),
     FP32-gradient step 30, reduce of 8 FP16 replicas into FP16 18 (read
     8 x 2, write 2), gather of 8 FP16 shards 4 (read 2, write 2), and the
     device-controlled check + decision + step 30 (2 + 28)."""
@@ -226,6 +227,10 @@ def measure_extras(dev, n_elem: int = 1 << 30, reps: int = 5) -> dict:
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     record("overflow_check_g32", timed(lambda: zs.zero_overflow_check_g32(acc, n, 1, 0, 65536.0,
                                                                           flag)), n, 4)
+    # the last micro-batch with the FP32 check fused in: the accumulate's 10 B
+    # per element, in place of 10 + 4 for the accumulate followed by the check
+    record("grad_accumulate_check", timed(lambda: zs.zero_grad_accumulate_check(
+        acc, g16, n, 1, 0, first=False, loss_scale=65536.0, found_inf=flag)), n, 10)
     sumsq = torch.zeros(1, device=dev)
     parts = torch.empty(zs.SUMSQ_PARTIALS, dtype=torch.float64, device=dev)
     record("overflow_check_sumsq_f16", timed(lambda: zs.zero_overflow_check(

@@ -221,6 +221,22 @@ int zero_grad_accumulate(float *acc, const void *g16, zero_dtype dt, uint64_t ps
                          uint32_t rank, int32_t first, void *stream);
 
 /*
+ * zero_grad_accumulate_check -- zero_grad_accumulate for the last
+ * micro-batch of a step, with the overflow check over the FP32 gradients it
+ * writes fused in: *d_found_inf becomes 1 iff some written acc[i] / S is
+ * not finite (the flag zero_overflow_check_g32 would give on the result, no
+ * sum of squares), without reading the accumulator again.
+ *   loss_scale   S > 0 and finite.
+ *   d_found_inf  device int32, cleared on `stream` first (also for an empty
+ *                rank), may not overlap acc or g16.
+ *   Other arguments and errors as for zero_grad_accumulate; ZERO_EINVAL also
+ *   for a NULL or misaligned d_found_inf or a bad S.
+ */
+int zero_grad_accumulate_check(float *acc, const void *g16, zero_dtype dt, uint64_t psi,
+                               uint32_t n, uint32_t rank, int32_t first, float loss_scale,
+                               int32_t *d_found_inf, void *stream);
+
+/*
  * zero_overflow_check_g32 -- zero_overflow_check over FP32 gradients
  * (4 bytes per element); same outputs, scratch and errors.
  */
@@ -394,6 +410,16 @@ int zero_adam_step_g32_dev(void *w16, const float *g32, float *master, float *m,
                            zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank, float lr,
                            float beta1, float beta2, float eps, float weight_decay,
                            const zero_device_ctl *d_ctl, void *stream);
+
+/*
+ * zero_grad_accumulate_check_dev -- zero_grad_accumulate_check with S read from
+ * d_ctl->scaler.loss_scale and the flag written to d_ctl->found_inf, for the
+ * device-resident sequence (zero_scaler_update_dev and zero_adam_step_g32_dev
+ * follow).  d_ctl may not overlap acc or g16.
+ */
+int zero_grad_accumulate_check_dev(float *acc, const void *g16, zero_dtype dt, uint64_t psi,
+                                   uint32_t n, uint32_t rank, int32_t first,
+                                   zero_device_ctl *d_ctl, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Sharded checkpoints: each rank writes its own slice of the model states to

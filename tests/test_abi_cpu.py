@@ -270,6 +270,38 @@ def test_device_path_argument_errors():
     assert "table" in zs.zero_strerror(-4)
 
 
+def test_fused_accumulate_check_argument_errors():
+    L = zs.lib
+    # dtype, layout, null or misaligned views and flag, bad S, overlaps -- all before any device call
+    assert L.zero_grad_accumulate_check(FAKE * 4, FAKE, 3, 100, 4, 0, 1, 1.0, FAKE * 8, None) == -2
+    assert L.zero_grad_accumulate_check(FAKE * 4, FAKE, 0, 100, 4, 4, 1, 1.0, FAKE * 8, None) == -1
+    assert L.zero_grad_accumulate_check(None, FAKE, 0, 100, 4, 0, 1, 1.0, FAKE * 8, None) == -1
+    assert L.zero_grad_accumulate_check(FAKE * 4, None, 0, 100, 4, 0, 1, 1.0, FAKE * 8, None) == -1
+    assert L.zero_grad_accumulate_check(FAKE * 4 + 2, FAKE, 0, 100, 4, 0, 1, 1.0, FAKE * 8,
+                                        None) == -1
+    assert L.zero_grad_accumulate_check(FAKE * 4, FAKE, 0, 100, 4, 0, 1, 1.0, None, None) == -1
+    assert L.zero_grad_accumulate_check(FAKE * 4, FAKE, 0, 100, 4, 0, 1, 1.0, FAKE * 8 + 2,
+                                        None) == -1
+    for S in (0.0, -1.0, float("inf"), float("nan")):
+        assert L.zero_grad_accumulate_check(FAKE * 4, FAKE, 0, 100, 4, 0, 1, S, FAKE * 8,
+                                            None) == -1
+    # psi = 400 over 4 ranks: count 100; the flag inside acc, inside g16; acc over g16
+    assert L.zero_grad_accumulate_check(FAKE * 4, FAKE, 0, 400, 4, 0, 0, 1.0, FAKE * 4 + 96,
+                                        None) == -1
+    assert L.zero_grad_accumulate_check(FAKE * 4, FAKE, 0, 400, 4, 0, 0, 1.0, FAKE + 100,
+                                        None) == -1
+    assert L.zero_grad_accumulate_check(FAKE + 100, FAKE, 0, 400, 4, 0, 0, 1.0, FAKE * 8,
+                                        None) == -1
+    # the device form: null or misaligned control block, or one inside a view
+    assert L.zero_grad_accumulate_check_dev(FAKE * 4, FAKE, 0, 100, 4, 0, 1, None, None) == -1
+    assert L.zero_grad_accumulate_check_dev(FAKE * 4, FAKE, 0, 100, 4, 0, 1, FAKE * 8 + 4,
+                                            None) == -1
+    assert L.zero_grad_accumulate_check_dev(FAKE * 4, FAKE, 0, 400, 4, 0, 1, FAKE * 4 + 64,
+                                            None) == -1
+    assert L.zero_grad_accumulate_check_dev(FAKE * 4, FAKE, 2, 100, 4, 0, 1, FAKE * 8,
+                                            None) == -2
+
+
 def test_fp32_gradient_device_path_argument_errors():
     L = zs.lib
     # check: layout, null or misaligned control block, null or misaligned gradients,

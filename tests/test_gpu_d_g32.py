@@ -44,6 +44,72 @@ def test_accumulate_matches_oracle(dtype, phases):
     log(f"accumulate {dtype} phases {phases}: bitwise")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("phases", [(0, 0), (1, 1), (3, 3), (0, 1)])
+def test_fused_accumulate_check_matches_oracle(dtype, phases):
+    # the last micro-batch accumulated with the FP32 check of the result fused
+    # in: the accumulator bit for bit and the flag equal to the check's flag on
+    # the result -- clean, with an inf in the last micro-batch, with a NaN from
+    # an earlier one, for S a power of two and not
+    pa, pg = phases
+    rng = np.random.default_rng(17 + pa + 4 * pg)
+    for count in COUNTS:
+        for case in ("clean", "inf_last", "nan_first"):
+            for S in (1024.0, 3.0):
+                mbs = micro_batches(count, 3, dtype, 950 + count % 97)
+                pos = int(rng.integers(count))
+                if case == "inf_last":
+                    mbs[-1][pos] = float("-inf")
+                elif case == "nan_first":
+                    mbs[0][pos] = float("nan")
+                acc = GuardedView(count, torch.float32, pa, DEV)
+                gv = GuardedView(count, TD[dtype], pg, DEV)
+                flag = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+                ref = np.zeros(count, np.float32)
+                for j, g in enumerate(mbs):
+                    gv.view.copy_(g.to(DEV))
+                    if j == len(mbs) - 1:
+                        zs.zero_grad_accumulate_check(acc.view, gv.view, count, 1, 0,
+                                                      first=(j == 0), loss_scale=S,
+                                                      found_inf=flag)
+                    else:
+                        zs.zero_grad_accumulate(acc.view, gv.view, count, 1, 0, first=(j == 0))
+                    oracle.grad_accumulate(ref, u16(g), dtype, first=(j == 0))
+                torch.cuda.synchronize()
+                rf, _ = oracle.overflow_check_g32(ref, S)
+                assert rf == (case != "clean")
+                assert flag.item() == rf, (count, case, S, phases)
+                got = f32(acc.view)
+                same = (got.view(np.uint32) == ref.view(np.uint32)) | (np.isnan(got) & np.isnan(ref))
+                assert same.all(), (count, case, S, phases)
+                assert acc.guards_intact() and gv.guards_intact()
+    log(f"fused accumulate + check {dtype} phases {phases}: bitwise, flags equal")
+
+
+def test_fused_accumulate_check_overflow_by_division_and_empty_rank():
+    # BF16 gradients near the top of the FP32 range: the FP32 sum overflows in
+    # one case and only the division by S < 1 overflows in the other
+    count = 70_001
+    big = torch.full((count,), 1.0, dtype=torch.bfloat16)
+    big[12_345] = 1.7e38
+    g = big.to(DEV)
+    acc = torch.empty(count, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for first, S, want in ((True, 1.0, 0), (True, 0.25, 1), (False, 1.0, 1)):
+        zs.zero_grad_accumulate_check(acc, g, count, 1, 0, first=first, loss_scale=S,
+                                      found_inf=flag)
+        torch.cuda.synchronize()
+        assert flag.item() == want, (first, S)
+    # second pass (not first): 1.7e38 + 1.7e38 overflows FP32 to inf
+    assert np.isinf(f32(acc)[12_345])
+    # an empty rank still clears the flag
+    flag.fill_(7)
+    zs.zero_grad_accumulate_check(acc[:0], g[:0], 10, 8, 7, first=True, loss_scale=1.0,
+                                  found_inf=flag)
+    torch.cuda.synchronize()
+    assert flag.item() == 0
+
+
 @pytest.mark.parametrize("phase", [0, 1, 2, 3])
 def test_check_g32_matches_oracle(phase):
     rng = np.random.default_rng(40 + phase)

@@ -53,12 +53,19 @@ def test_step_g32_and_accumulate_tile_loop(cap):
             acc = GuardedView(count, torch.float32, 1, DEV)
             gv = GuardedView(count, TD[dtype], 1, DEV)
             ref_acc = np.zeros(count, np.float32)
-            for j, g in enumerate(micro_batches(count, 3, dtype, 70 + cap)):
+            flag = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+            mbs = micro_batches(count, 3, dtype, 70 + cap)
+            for j, g in enumerate(mbs):
                 gv.view.copy_(g.to(DEV))
-                zs.zero_grad_accumulate(acc.view, gv.view, count, 1, 0, first=(j == 0))
+                if j == len(mbs) - 1:      # the last one with the fused FP32 check
+                    zs.zero_grad_accumulate_check(acc.view, gv.view, count, 1, 0, first=(j == 0),
+                                                  loss_scale=3.0, found_inf=flag)
+                else:
+                    zs.zero_grad_accumulate(acc.view, gv.view, count, 1, 0, first=(j == 0))
                 oracle.grad_accumulate(ref_acc, u16(g), dtype, first=(j == 0))
             torch.cuda.synchronize()
             assert np.array_equal(f32(acc.view).view(np.uint32), ref_acc.view(np.uint32))
+            assert flag.item() == oracle.overflow_check_g32(ref_acc, 3.0)[0] == 0
             assert acc.guards_intact() and gv.guards_intact()
 
             V = {k: GuardedView(count, torch.float32, 2, DEV) for k in ("master", "m", "v")}

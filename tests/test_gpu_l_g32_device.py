@@ -7,7 +7,8 @@ inside the loop.  The same training step -- k accumulations, the check, the
 decision and the step -- is then captured once into a HIP graph and replayed
 per step, each replay checked bit for bit against the same step run eagerly on
 a second copy of the state (with eager work and synchronisation between
-replays), and the final state against the oracle.
+replays), and the final state against the oracle.  Both run with the check as
+its own pass and fused into the last micro-batch's accumulate.
 """
 import numpy as np
 import pytest
@@ -52,11 +53,17 @@ class State:
         return all(v.guards_intact() for v in self.V.values())
 
 
-def enqueue_training_step(st, mb_views, count, ctl, bias):
+def enqueue_training_step(st, mb_views, count, ctl, bias, fused=False):
+    # fused: the last micro-batch's accumulate carries the check of the result
     V = st.V
     for j, g in enumerate(mb_views):
-        zs.zero_grad_accumulate(V["acc"].view, g, count, 1, 0, first=(j == 0))
-    zs.zero_overflow_check_g32_dev(V["acc"].view, count, 1, 0, ctl)
+        if fused and j == len(mb_views) - 1:
+            zs.zero_grad_accumulate_check_dev(V["acc"].view, g, count, 1, 0, first=(j == 0),
+                                              ctl=ctl)
+        else:
+            zs.zero_grad_accumulate(V["acc"].view, g, count, 1, 0, first=(j == 0))
+    if not fused:
+        zs.zero_overflow_check_g32_dev(V["acc"].view, count, 1, 0, ctl)
     zs.zero_scaler_update_dev(ctl, bias, 1)
     zs.zero_adam_step_g32_dev(V["w16"].view, V["acc"].view, V["master"].view, V["m"].view,
                               V["v"].view, count, 1, 0, ctl=ctl, **HP)
@@ -82,8 +89,9 @@ def run_oracle(master0, batches, dtype, S0, growth):
     return ref, sc, trace
 
 
-@pytest.mark.parametrize("dtype,phase", [("f16", 0), ("bf16", 3)])
-def test_device_controlled_fp32_gradient_schedule(dtype, phase):
+@pytest.mark.parametrize("dtype,phase,fused", [("f16", 0, False), ("bf16", 3, False),
+                                               ("f16", 1, True), ("bf16", 0, True)])
+def test_device_controlled_fp32_gradient_schedule(dtype, phase, fused):
     count, steps, k, S0, growth = 300_007, 8, 3, 1024.0, 2
     batches = micro_batches(count, steps, k, dtype, 61_000, bad_steps=(3, 6))
     master0 = synth.fill_normal_(torch.empty(count), 0.02, 61_900)
@@ -96,7 +104,7 @@ def test_device_controlled_fp32_gradient_schedule(dtype, phase):
     for mbs in dev_batches:            # no host read-back inside this loop
         for view, g in zip(mb, mbs):
             view.view.copy_(g)
-        enqueue_training_step(st, [m.view for m in mb], count, ctl, bias)
+        enqueue_training_step(st, [m.view for m in mb], count, ctl, bias, fused=fused)
     torch.cuda.synchronize()
     ref, sc, trace = run_oracle(master0, batches, dtype, S0, growth)
     assert [a for _, a in trace] == [True, True, False, True, True, False, True, True]
@@ -104,12 +112,14 @@ def test_device_controlled_fp32_gradient_schedule(dtype, phase):
     assert (c.scaler.step, c.scaler.loss_scale, c.scaler.clean_steps) == \
         (sc.step, sc.loss_scale, sc.clean_steps)
     assert c.status == 0 and c.apply == 1
-    log(f"  FP32-gradient device schedule {dtype}: t {c.scaler.step}, S {c.scaler.loss_scale}",
+    log(f"  FP32-gradient device schedule {dtype} fused={fused}: t {c.scaler.step}, "
+        f"S {c.scaler.loss_scale}",
         assert_close(st.host(), ref, dtype, "g32 device schedule"))
     assert st.intact() and all(m.guards_intact() for m in mb)
 
 
-def test_fp32_gradient_training_step_graph_replays():
+@pytest.mark.parametrize("fused", [False, True])
+def test_fp32_gradient_training_step_graph_replays(fused):
     dtype, count, steps, k, S0, growth = "f16", 1_000_003, 6, 2, 65536.0, 2
     batches = micro_batches(count, steps, k, dtype, 62_000, bad_steps=(4,))
     master0 = synth.fill_normal_(torch.empty(count), 0.02, 62_900)
@@ -122,7 +132,7 @@ def test_fp32_gradient_training_step_graph_replays():
 
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        enqueue_training_step(G, mb, count, ctl_g, bias)
+        enqueue_training_step(G, mb, count, ctl_g, bias, fused=fused)
     torch.cuda.synchronize()
     assert zs.device_ctl_read(ctl_g).scaler.step == 0          # capture ran nothing
 
@@ -131,7 +141,7 @@ def test_fp32_gradient_training_step_graph_replays():
             view.copy_(g.to(DEV))
         graph.replay()
         torch.cuda.synchronize()
-        enqueue_training_step(E, mb, count, ctl_e, bias)
+        enqueue_training_step(E, mb, count, ctl_e, bias, fused=fused)
         torch.cuda.synchronize()
         he, hg = E.host(), G.host()
         for key in he:
@@ -144,7 +154,7 @@ def test_fp32_gradient_training_step_graph_replays():
     assert [a for _, a in trace] == [True, True, True, False, True, True]
     c = zs.device_ctl_read(ctl_g)
     assert (c.scaler.step, c.scaler.loss_scale) == (sc.step, sc.loss_scale)
-    log(f"  FP32-gradient training step, graph x{steps}",
+    log(f"  FP32-gradient training step, graph x{steps}, fused={fused}",
         assert_close(G.host(), ref, dtype, "g32 graph"))
     assert G.intact()
     del graph

@@ -74,10 +74,12 @@ def test_vector_step_uses_16_byte_accesses(asm):
         if not g32:
             assert count(body, "global_load_dwordx2") >= 2  # 4 gradients per lane per group
         assert count(body, "global_store_dwordx2") >= 2     # 4 working weights
-    acc = [b for k, b in kernels.items() if "accumulate_vec" in k]
-    assert len(acc) == 4
-    for body in acc:
+    acc = {k: b for k, b in kernels.items() if "accumulate_vec" in k}
+    assert len(acc) == 8       # FP16 / BF16 x first / not x with / without the fused check
+    for name, body in acc.items():
         assert count(body, "global_store_dwordx4") >= 2
+        if "Lb0ELi2ELb0E" in name or "Lb0ELi2ELb1E" in name:   # not the first micro-batch
+            assert count(body, "global_load_dwordx4") >= 2
 
 
 def test_sum_of_squares_visits_every_vector_lane(asm):

@@ -22,6 +22,7 @@ weight_decay, step, loss_scale, found_inf=None).
 FP32 gradients (accumulated across micro-batches):
 
     zero_grad_accumulate(acc32, g16, psi, n, rank, first)
+    zero_grad_accumulate_check(acc32, g16, psi, n, rank, first, loss_scale, found_inf)  # last one
     zero_overflow_check_g32(g32, psi, n, rank, loss_scale, found_inf, sumsq=None, partials=None)
     zero_adam_step_g32(w16, g32, master, m, v, psi, n, rank, *, lr, ..., step, loss_scale)
     zero_overflow_check_g32_dev(g32, psi, n, rank, ctl)        # device-resident control
@@ -76,6 +77,8 @@ from ._binding import (  # noqa: F401
     zero_comm_volume,
     zero_gather_shards,
     zero_grad_accumulate,
+    zero_grad_accumulate_check,
+    zero_grad_accumulate_check_dev,
     zero_overflow_check,
     zero_overflow_check_dev,
     zero_overflow_check_g32,
@@ -108,6 +111,8 @@ __all__ = [
     "zero_scaler_update_dev",
     "zero_adam_step_dev",
     "zero_grad_accumulate",
+    "zero_grad_accumulate_check",
+    "zero_grad_accumulate_check_dev",
     "zero_overflow_check_g32",
     "zero_adam_step_g32",
     "zero_overflow_check_g32_dev",

@@ -82,6 +82,12 @@ class DeviceCtl(ctypes.Structure):
 
 
 lib.zero_grad_accumulate.argtypes = [_vp, _vp, _i32, _u64, _u32, _u32, ctypes.c_int32, _vp]
+lib.zero_grad_accumulate_check.argtypes = [_vp, _vp, _i32, _u64, _u32, _u32, ctypes.c_int32,
+                                           _f32, _vp, _vp]
+lib.zero_grad_accumulate_check.restype = _i32
+lib.zero_grad_accumulate_check_dev.argtypes = [_vp, _vp, _i32, _u64, _u32, _u32, ctypes.c_int32,
+                                               _vp, _vp]
+lib.zero_grad_accumulate_check_dev.restype = _i32
 lib.zero_grad_accumulate.restype = _i32
 lib.zero_overflow_check_g32.argtypes = [_vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _vp]
 lib.zero_overflow_check_g32.restype = _i32
@@ -383,6 +389,39 @@ def zero_grad_accumulate(acc: torch.Tensor, g16: torch.Tensor, psi: int, n: int,
                                       _stream_handle(stream, dev))
     if rc != 0:
         raise ZeroError(rc, "zero_grad_accumulate")
+
+
+def zero_grad_accumulate_check(acc: torch.Tensor, g16: torch.Tensor, psi: int, n: int,
+                               rank: int, first: bool, loss_scale: float, found_inf: torch.Tensor,
+                               stream=None) -> None:
+    """The last micro-batch's accumulate with the FP32 overflow check of the result fused in."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g16.device
+    p_g = _view(g16, "g16", _DTYPES, lay.count, dev)
+    p_a = _view(acc, "acc", (torch.float32,), lay.count, dev)
+    p_f = _view(found_inf, "found_inf", (torch.int32,), 1, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_grad_accumulate_check(p_a, p_g, _DTYPES[g16.dtype], psi, n, rank,
+                                            int(bool(first)), loss_scale, p_f,
+                                            _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_grad_accumulate_check")
+
+
+def zero_grad_accumulate_check_dev(acc: torch.Tensor, g16: torch.Tensor, psi: int, n: int,
+                                   rank: int, first: bool, ctl: torch.Tensor,
+                                   stream=None) -> None:
+    """zero_grad_accumulate_check with S read from, and the flag written to, the control block."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g16.device
+    p_g = _view(g16, "g16", _DTYPES, lay.count, dev)
+    p_a = _view(acc, "acc", (torch.float32,), lay.count, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_grad_accumulate_check_dev(p_a, p_g, _DTYPES[g16.dtype], psi, n, rank,
+                                                int(bool(first)), _ctl_ptr(ctl, dev),
+                                                _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_grad_accumulate_check_dev")
 
 
 def zero_overflow_check_g32(g32: torch.Tensor, psi: int, n: int, rank: int, loss_scale: float,

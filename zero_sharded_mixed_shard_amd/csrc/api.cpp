@@ -246,6 +246,54 @@ extern "C" int zero_grad_accumulate(float *acc, const void *g16, zero_dtype dt, 
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_grad_accumulate launch");
 }
 
+// Shared by both forms of the fused accumulate-and-check: arguments of the
+// accumulate, and the flag (or control block) apart from both views.
+int accumulate_check_args(float *acc, const void *g16, zero_dtype dt, uint64_t psi, uint32_t n,
+                          uint32_t rank, const void *flag, uint64_t flag_bytes, uint64_t *count) {
+    const int rc = check_args(g16, dt, psi, n, rank, count);
+    if (rc != ZERO_OK) return rc;
+    if (*count > 0 && (acc == nullptr || !aligned(acc, 4))) return ZERO_EINVAL;
+    if (overlap(acc, 4 * *count, g16, 2 * *count)) return ZERO_EINVAL;
+    if (flag == nullptr || !aligned(flag, 4)) return ZERO_EINVAL;
+    if (overlap(flag, flag_bytes, acc, 4 * *count) || overlap(flag, flag_bytes, g16, 2 * *count))
+        return ZERO_EINVAL;
+    return ZERO_OK;
+}
+
+extern "C" int zero_grad_accumulate_check(float *acc, const void *g16, zero_dtype dt,
+                                          uint64_t psi, uint32_t n, uint32_t rank, int32_t first,
+                                          float loss_scale, int32_t *d_found_inf, void *stream) {
+    uint64_t count = 0;
+    int rc = accumulate_check_args(acc, g16, dt, psi, n, rank, d_found_inf, 4, &count);
+    if (rc != ZERO_OK) return rc;
+    if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
+    zs::DeviceProps dev;
+    rc = device_props(&dev);
+    if (rc != ZERO_OK) return rc;
+    const hipError_t e = zs::launch_grad_accumulate_check(
+        static_cast<int>(dt), acc, static_cast<const uint16_t *>(g16), count, first != 0,
+        loss_scale, nullptr, d_found_inf, dev, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_grad_accumulate_check launch");
+}
+
+extern "C" int zero_grad_accumulate_check_dev(float *acc, const void *g16, zero_dtype dt,
+                                              uint64_t psi, uint32_t n, uint32_t rank,
+                                              int32_t first, zero_device_ctl *d_ctl,
+                                              void *stream) {
+    uint64_t count = 0;
+    if (d_ctl != nullptr && !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
+    int rc = accumulate_check_args(acc, g16, dt, psi, n, rank, d_ctl, sizeof(zero_device_ctl),
+                                   &count);
+    if (rc != ZERO_OK) return rc;
+    zs::DeviceProps dev;
+    rc = device_props(&dev);
+    if (rc != ZERO_OK) return rc;
+    const hipError_t e = zs::launch_grad_accumulate_check(
+        static_cast<int>(dt), acc, static_cast<const uint16_t *>(g16), count, first != 0, 1.0f,
+        &d_ctl->scaler.loss_scale, &d_ctl->found_inf, dev, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_grad_accumulate_check_dev launch");
+}
+
 extern "C" int zero_overflow_check_g32(const float *g32, uint64_t psi, uint32_t n, uint32_t rank,
                                        float loss_scale, int32_t *d_found_inf, float *d_sumsq,
                                        double *d_partials, void *stream) {

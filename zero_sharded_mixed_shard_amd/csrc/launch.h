@@ -68,6 +68,15 @@ hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, floa
 hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, uint64_t count,
                                   bool first, const DeviceProps &dev, hipStream_t stream);
 
+// The same accumulate, raising *flag (cleared first, also when count == 0)
+// iff some written acc[i] / S is not finite -- the check over FP32 gradients
+// of the result, fused into the pass that writes it.  loss_scale_dev
+// (nullable) replaces loss_scale with a value read on the device.
+hipError_t launch_grad_accumulate_check(int dtype, float *acc, const uint16_t *g16,
+                                        uint64_t count, bool first, float loss_scale,
+                                        const float *loss_scale_dev, int32_t *flag,
+                                        const DeviceProps &dev, hipStream_t stream);
+
 // The check over FP32 gradients (count may be 0: only the outputs are cleared);
 // loss_scale_dev as for launch_overflow_check.
 hipError_t launch_overflow_check_g32(const float *g32, uint64_t count, float loss_scale,

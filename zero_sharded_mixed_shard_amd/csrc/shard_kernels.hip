@@ -225,21 +225,57 @@ __global__ __launch_bounds__(kThreads) void adam_step_elem(
 // acc = float(g16) on the first micro-batch, acc + float(g16) after it: one
 // FP32 addition per element per micro-batch (10 B of traffic; 6 B for the
 // first).  Same head / tile / tail split and alignment rule as the step.
+//
+// With CHECK the kernel also raises the overflow flag of the values it
+// writes, as the check over FP32 gradients would on the result (some
+// acc/S not finite): each lane keeps the largest magnitude bits it wrote and
+// divides once at the end (correctly rounded division by S > 0 is monotone
+// in |acc|), so the last micro-batch needs no separate 4-B/element check
+// pass.  The flag is cleared by a kernel launched before this one.
+
+struct AccCheck {
+    float loss_scale;             // S, unless loss_scale_dev is set
+    const float *loss_scale_dev;  // S read on the device, or null
+    int32_t *flag;                // set to 1 by each wave that wrote a value with acc/S not finite
+};
 
 template <int DT, bool FIRST>
-__device__ __forceinline__ void accumulate_one(float *__restrict__ acc,
-                                               const uint16_t *__restrict__ g16, uint64_t i) {
+__device__ __forceinline__ float accumulate_one(float *__restrict__ acc,
+                                                const uint16_t *__restrict__ g16, uint64_t i) {
     const float g = widen<DT>(g16[i]);
-    acc[i] = FIRST ? g : acc[i] + g;
+    const float r = FIRST ? g : acc[i] + g;
+    acc[i] = r;
+    return r;
 }
 
-template <int DT, bool FIRST, int U>
+__device__ __forceinline__ uint32_t magnitude_bits(float x) {
+    return __builtin_bit_cast(uint32_t, x) & 0x7fffffffu;
+}
+
+// The flag from a lane's largest magnitude bits; every lane of the wave calls it.
+__device__ __forceinline__ void accumulate_flag(uint32_t mx, const AccCheck &chk) {
+    const float S = chk.loss_scale_dev != nullptr ? *chk.loss_scale_dev : chk.loss_scale;
+    const uint32_t bad = mx >= 0x7f800000u || not_finite(__builtin_bit_cast(float, mx) / S) ||
+                         !(S > 0.0f) || not_finite(S);
+    if (__any(bad)) {
+        if ((threadIdx.x & 63u) == 0) *chk.flag = 1;
+    }
+}
+
+template <int DT, bool FIRST, int U, bool CHECK>
 __global__ __launch_bounds__(kThreads) void accumulate_vec(float *__restrict__ acc,
                                                            const uint16_t *__restrict__ g16,
                                                            uint64_t count, uint32_t head,
-                                                           uint64_t n_tiles) {
+                                                           uint64_t n_tiles, AccCheck chk) {
     const uint32_t tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid < head) accumulate_one<DT, FIRST>(acc, g16, tid);
+    uint32_t mx = 0;
+    auto note = [&](float r) {
+        if constexpr (CHECK) {
+            const uint32_t a = magnitude_bits(r);
+            mx = a > mx ? a : mx;
+        }
+    };
+    if (blockIdx.x == 0 && tid < head) note(accumulate_one<DT, FIRST>(acc, g16, tid));
     constexpr uint64_t kTile = static_cast<uint64_t>(U) * kGroup;
     for (uint64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
         const uint64_t base = head + t * kTile + static_cast<uint64_t>(tid) * kVec;
@@ -258,22 +294,34 @@ __global__ __launch_bounds__(kThreads) void accumulate_vec(float *__restrict__ a
                                   : f32x4{A[u].x + G[u][0], A[u].y + G[u][1], A[u].z + G[u][2],
                                           A[u].w + G[u][3]};
             store_nt(reinterpret_cast<f32x4 *>(acc + e), r);
+            note(r.x);
+            note(r.y);
+            note(r.z);
+            note(r.w);
         }
     }
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     for (uint64_t i = head + n_tiles * kTile + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
          i < count; i += stride)
-        accumulate_one<DT, FIRST>(acc, g16, i);
+        note(accumulate_one<DT, FIRST>(acc, g16, i));
+    if constexpr (CHECK) accumulate_flag(mx, chk);
 }
 
-template <int DT, bool FIRST>
+template <int DT, bool FIRST, bool CHECK>
 __global__ __launch_bounds__(kThreads) void accumulate_elem(float *__restrict__ acc,
                                                             const uint16_t *__restrict__ g16,
-                                                            uint64_t count) {
+                                                            uint64_t count, AccCheck chk) {
+    uint32_t mx = 0;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < count;
-         i += stride)
-        accumulate_one<DT, FIRST>(acc, g16, i);
+         i += stride) {
+        const float r = accumulate_one<DT, FIRST>(acc, g16, i);
+        if constexpr (CHECK) {
+            const uint32_t a = magnitude_bits(r);
+            mx = a > mx ? a : mx;
+        }
+    }
+    if constexpr (CHECK) accumulate_flag(mx, chk);
 }
 
 // ---- unscale + overflow check ----------------------------------------------
@@ -681,13 +729,13 @@ hipError_t adam_dispatch(uint16_t *w16, const GT *g, float *master, float *m, fl
     return hipGetLastError();
 }
 
-template <int DT, bool FIRST>
+template <int DT, bool FIRST, bool CHECK>
 hipError_t accumulate_dispatch(float *acc, const uint16_t *g16, uint64_t count,
-                               const DeviceProps &dev, hipStream_t stream) {
+                               const AccCheck &chk, const DeviceProps &dev, hipStream_t stream) {
     uint32_t head = 0;
     if (!common_phase<uint16_t>(acc, acc, nullptr, g16, nullptr, &head)) {
-        accumulate_elem<DT, FIRST><<<grid_for((count + kThreads - 1) / kThreads), kThreads, 0,
-                                     stream>>>(acc, g16, count);
+        accumulate_elem<DT, FIRST, CHECK><<<grid_for((count + kThreads - 1) / kThreads), kThreads,
+                                            0, stream>>>(acc, g16, count, chk);
         return hipGetLastError();
     }
     if (head > count) head = static_cast<uint32_t>(count);
@@ -695,9 +743,9 @@ hipError_t accumulate_dispatch(float *acc, const uint16_t *g16, uint64_t count,
     const uint64_t n_tiles = (count - head) / kTile;
     const uint64_t rest = count - head - n_tiles * kTile;
     const uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
-    accumulate_vec<DT, FIRST, kAccU><<<grid_for(need), kThreads,
-                                       accumulate_lds_bytes(count, FIRST, dev), stream>>>(
-        acc, g16, count, head, n_tiles);
+    accumulate_vec<DT, FIRST, kAccU, CHECK><<<grid_for(need), kThreads,
+                                              accumulate_lds_bytes(count, FIRST, dev), stream>>>(
+        acc, g16, count, head, n_tiles, chk);
     return hipGetLastError();
 }
 
@@ -769,11 +817,27 @@ hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, floa
 
 hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, uint64_t count,
                                   bool first, const DeviceProps &dev, hipStream_t stream) {
+    const AccCheck none{1.0f, nullptr, nullptr};
     if (dtype == 0)
-        return first ? accumulate_dispatch<0, true>(acc, g16, count, dev, stream)
-                     : accumulate_dispatch<0, false>(acc, g16, count, dev, stream);
-    return first ? accumulate_dispatch<1, true>(acc, g16, count, dev, stream)
-                 : accumulate_dispatch<1, false>(acc, g16, count, dev, stream);
+        return first ? accumulate_dispatch<0, true, false>(acc, g16, count, none, dev, stream)
+                     : accumulate_dispatch<0, false, false>(acc, g16, count, none, dev, stream);
+    return first ? accumulate_dispatch<1, true, false>(acc, g16, count, none, dev, stream)
+                 : accumulate_dispatch<1, false, false>(acc, g16, count, none, dev, stream);
+}
+
+hipError_t launch_grad_accumulate_check(int dtype, float *acc, const uint16_t *g16,
+                                        uint64_t count, bool first, float loss_scale,
+                                        const float *loss_scale_dev, int32_t *flag,
+                                        const DeviceProps &dev, hipStream_t stream) {
+    check_init<<<1, 64, 0, stream>>>(flag, nullptr);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess || count == 0) return err;
+    const AccCheck chk{loss_scale, loss_scale_dev, flag};
+    if (dtype == 0)
+        return first ? accumulate_dispatch<0, true, true>(acc, g16, count, chk, dev, stream)
+                     : accumulate_dispatch<0, false, true>(acc, g16, count, chk, dev, stream);
+    return first ? accumulate_dispatch<1, true, true>(acc, g16, count, chk, dev, stream)
+                 : accumulate_dispatch<1, false, true>(acc, g16, count, chk, dev, stream);
 }
 
 hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
