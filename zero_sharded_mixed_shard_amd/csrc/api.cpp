@@ -22,7 +22,6 @@ int fail_hip(hipError_t e, const char *what) {
     return ZERO_EHIP;
 }
 
-// Compute units per device, queried once per device.
 constexpr int kMaxDevices = 64;
 // Per-device cache of the properties the launchers use; a zero compute-unit
 // count marks an entry not yet filled.  Each field is written once with the
@@ -113,7 +112,8 @@ float bias_correction(float beta, uint64_t t) {
     return static_cast<float>(1.0 - std::pow(static_cast<double>(beta), static_cast<double>(t)));
 }
 
-// Checks shared by both forms of the check; returns the layout's count.
+// Checks of a 16-bit gradient view and its layout, shared by the checks and the
+// accumulates; returns the layout's count.
 int check_args(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank,
                uint64_t *count) {
     if (dt != ZERO_F16 && dt != ZERO_BF16) return ZERO_EDTYPE;
