@@ -298,6 +298,40 @@ def test_sumsq_power_of_two_scales_and_their_edges():
                 check_case(bits, dtype, phase, S)    # flag bit-exact; sum within 1 ulp
 
 
+def test_sumsq_single_quotients_bit_exact():
+    # One gradient per call: the sum of squares is then q*q rounded once to
+    # FP32, so a single quotient q = g / S off by one unit would show.  Every
+    # S path (power of two: multiply; others: the FP64 reciprocal product, and
+    # the division where the quotient is subnormal) against the oracle's
+    # correctly rounded FP32 division, bit for bit.
+    rng = np.random.default_rng(11)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    s = torch.zeros(1, device=DEV)
+    parts = torch.empty(zs.SUMSQ_PARTIALS, dtype=torch.float64, device=DEV)
+    scales = [3.0, 7.0, 1000.0, 0.3, 1.0 + 2.0 ** -23, 2.0 - 2.0 ** -23, 65535.0, 2.0 ** 20 * 3.0,
+              float(np.float32(1e30)), float(np.float32(3e-30)), 1024.0, 0.5]
+    scales += [float(v) for v in (np.exp(rng.uniform(-40, 40, 24))).astype(np.float32)]
+    n = 0
+    for dtype, td in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        pats = rng.integers(0, 1 << 16, 48).astype(np.uint16)
+        pats[:4] = [0x0001, 0x8003, 0x03ff, 0x3c01]       # subnormals and 1 + 1 ulp (FP16 bits)
+        for h in pats:
+            bits = np.array([h], np.uint16)
+            g = torch.from_numpy(bits.view(np.int16).copy()).view(td).to(DEV)
+            for S in scales:
+                zs.zero_overflow_check(g, 1, 1, 0, S, flag, s, parts)
+                rf, rs = oracle.overflow_check(bits, dtype, S)
+                got_f, got_s = int(flag.item()), s.item()
+                assert got_f == rf, (dtype, hex(int(h)), S)
+                if rf == 0:
+                    with np.errstate(over="ignore"):
+                        want = np.float32(rs)
+                    assert np.float32(got_s).view(np.uint32) == want.view(np.uint32), \
+                        (dtype, hex(int(h)), S, got_s, rs)
+                n += 1
+    log(f"single-gradient sums of squares: {n} cases bit-exact")
+
+
 def test_calls_return_without_synchronising():
     # A bounded spin kernel ahead of them on the stream: the check and the step
     # are enqueued behind it and the calls return while it still runs.

@@ -83,19 +83,24 @@ def test_vector_step_uses_16_byte_accesses(asm):
 
 
 def test_sum_of_squares_visits_every_vector_lane(asm):
-    # each lane's 16-B vectors hold 8 (16-bit) or 4 (FP32) gradients; every one
-    # is widened to FP64 and its square added by one FP64 FMA: 4 vectors in
-    # flight + 1 remainder vector + the scalar head and tail, in each of two
-    # paths (S a power of two: multiply by 1/S; any other S: divide)
+    # each lane's 16-B vectors hold 8 (16-bit) or 4 (FP32) gradients; each is
+    # visited once in each of two paths (4 vectors in flight + 1 remainder
+    # vector + the scalar head and tail = n visits per path).  S a power of
+    # two: multiply by 1/S in FP32, widen, one FP64 FMA.  Any other S: widen,
+    # one FP64 multiply by RN64(1/S), one rounding to FP32, widen again, one
+    # FP64 FMA -- and, only in the branch for subnormal quotients, the FP32
+    # divide.  Plus the two reciprocals (FP32 and FP64) once per lane.
     _, kernels = asm
     sumsq = {k: b for k, b in kernels.items() if "overflow_sumsq_kernel" in k}
     assert len(sumsq) == 3
     for name, body in sumsq.items():
         per_vec = 4 if "IfLi" in name else 8
         n = 5 * per_vec + 2
-        assert count(body, "v_cvt_f64_f32_e32") == 2 * n, name
-        assert count(body, "v_fmac_f64_e32") + count(body, "v_fma_f64") == 2 * n, name
-        assert count(body, "v_mul_f64") == 0, name
-        assert count(body, "v_div_fixup_f32") == n + 1, name   # the divide path, and 1/S
+        assert count(body, "v_cvt_f64_f32_e32") == 3 * n + 1, name
+        assert count(body, "v_cvt_f32_f64_e32") == n, name
+        assert count(body, "v_mul_f64") == n + 1, name          # + one inside 1/S in FP64
+        assert count(body, "v_fmac_f64_e32") == 2 * n, name     # the squares, both paths
+        assert count(body, "v_div_fixup_f64") == 1, name        # RN64(1/S), once
+        assert count(body, "v_div_fixup_f32") == n + 1, name    # the fallback divides, and 1/S
         assert count(body, "global_load_dwordx4") == 10, name
         assert count(body, "v_mov_b32_dpp") == 12, name        # wave sum: 6 DPP steps x 2 halves

@@ -441,14 +441,25 @@ __device__ __forceinline__ double wave_sum_to_lane63(double x) {
 }
 
 // Flag and sum of squares.  Every gradient is unscaled and squared as its
-// definition says, with three exact shortcuts: when S is a power of two whose
-// reciprocal is a normal number, g * (1/S) is the same correctly rounded
-// value as g / S; q*q is exact in FP64 (a 24-bit significand squared), so one
-// FP64 fma equals the square followed by the addition; and a lane's FP64 sum
-// is not finite iff one of its q is (finite squares of FP32 values cannot
-// overflow an FP64 sum of fewer than 2^60 terms), so the flag is read off the
-// sums.  Lanes accumulate in FP64, waves reduce by DPP, and block b writes
-// its partial sum to partials[b].  Same element split as the flag kernel.
+// definition says, with exact shortcuts for the unscaling and the sum:
+//  - S a power of two whose reciprocal is a normal number: g * (1/S) is the
+//    same correctly rounded value as g / S.
+//  - Any other S: q = (float)((double)g * RN64(1/S)).  The FP64 product is
+//    within 2^-52 (relative) of g/S, and g/S is never within 2^-49 of a
+//    point where rounding to FP32 changes: such a midpoint has a 25-bit odd
+//    significand, which the product of S's odd significand (> 1) and a
+//    16-bit or FP32 gradient's cannot equal, and two unequal multiples of a
+//    power of two differ by at least that power.  So the one rounding to
+//    FP32 gives exactly g / S -- wherever the quotient is a normal number; a
+//    vector with a quotient below 2^-125 in magnitude is divided as written.
+//  - q*q is exact in FP64 (a 24-bit significand squared), so one FP64 fma
+//    equals the square followed by the addition.
+//  - A lane's FP64 sum is not finite iff one of its q is (finite squares of
+//    FP32 values cannot overflow an FP64 sum of fewer than 2^60 terms), so
+//    the flag is read off the sums.
+// Lanes accumulate in FP64 in element order, waves reduce by DPP, and block b
+// writes its partial sum to partials[b].  Same element split as the flag
+// kernel.
 template <typename GT, int DT, int U>
 __global__ __launch_bounds__(kThreads) void overflow_sumsq_kernel(
     const GT *__restrict__ g, uint64_t count, uint32_t head, uint64_t n_vec, float loss_scale,
@@ -461,30 +472,61 @@ __global__ __launch_bounds__(kThreads) void overflow_sumsq_kernel(
     const uint32_t sbits = __builtin_bit_cast(uint32_t, loss_scale);
     const uint32_t sexp = (sbits >> 23) & 0xffu;
     const bool pow2 = scale_ok && (sbits & 0x7fffffu) == 0 && sexp >= 1 && sexp <= 253;
-    const float inv = 1.0f / loss_scale;  // exact when pow2
+    const float inv = 1.0f / loss_scale;                              // exact when pow2
+    const double rcp = 1.0 / static_cast<double>(loss_scale);          // RN64(1/S)
     double acc = 0.0;
 
     auto run = [&](auto pow2_tag) {
         constexpr bool kPow2 = decltype(pow2_tag)::value;
-        auto visit = [&](float graw) {
-            const float q = kPow2 ? graw * inv : graw / loss_scale;
-            const double qd = static_cast<double>(q);
-            acc = __builtin_fma(qd, qd, acc);
-        };
-        auto visit_vec = [&](const u32x4 &x) {
+        // K gradients: unscale all, redo them by division if one quotient is
+        // subnormal (never with the power-of-two multiply), then add the
+        // squares in order
+        auto visit_n = [&](auto k_tag, const float *gr) {
+            constexpr int K = decltype(k_tag)::value;
+            float q[K];
+            bool tiny = false;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (sizeof(GT) == 2) {
-                    visit(widen<DT>(x[j] & 0xffffu));
-                    visit(widen<DT>(x[j] >> 16));
+            for (int j = 0; j < K; ++j) {
+                if constexpr (kPow2) {
+                    q[j] = gr[j] * inv;
                 } else {
-                    // copy the lane out first: bit-casting the vector element in
-                    // place made the compiler reuse one element for all four
-                    const uint32_t bits = x[j];
-                    visit(__builtin_bit_cast(float, bits));
+                    const double qq = static_cast<double>(gr[j]) * rcp;
+                    q[j] = static_cast<float>(qq);
+                    tiny |= __builtin_fabs(qq) < 0x1p-125;
                 }
             }
+            if (!kPow2 && tiny) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) q[j] = gr[j] / loss_scale;
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const double qd = static_cast<double>(q[j]);
+                acc = __builtin_fma(qd, qd, acc);
+            }
         };
+        auto visit_vec = [&](const u32x4 &x) {
+            if constexpr (sizeof(GT) == 2) {
+                float gr[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    gr[2 * j] = widen<DT>(x[j] & 0xffffu);
+                    gr[2 * j + 1] = widen<DT>(x[j] >> 16);
+                }
+                visit_n(std::integral_constant<int, 8>{}, gr);
+            } else {
+                // copy each lane out first: bit-casting the vector element in
+                // place made the compiler reuse one element for all four
+                float gr[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t bits = x[j];
+                    gr[j] = __builtin_bit_cast(float, bits);
+                }
+                visit_n(std::integral_constant<int, 4>{}, gr);
+            }
+        };
+        auto visit = [&](float graw) { visit_n(std::integral_constant<int, 1>{}, &graw); };
         if (blockIdx.x == 0 && tid < head) visit(grad_at<GT, DT>(g, tid));
         const u32x4 *vec = reinterpret_cast<const u32x4 *>(g + head);
         const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
