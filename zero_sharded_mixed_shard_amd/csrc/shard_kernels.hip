@@ -719,10 +719,13 @@ int step_blocks_per_cu(uint64_t count) {
 // 5.78-5.85; at 15.5M the cap loses (6.07-6.33 against 6.47-6.63).  The first
 // micro-batch (a 16-bit read and an FP32 write, nothing read back) wants 4:
 // 6.48-6.53 TB/s against 5.97-6.10 uncapped and 4.96-4.99 at 2 per CU, from
-// 2^28 to 2^32 elements.
+// 2^28 to 2^32 elements.  So does the accumulate with the check fused in,
+// whose blocks end with the divide: at 2^30 elements 1.704-1.730 ms at 4 per
+// CU against 1.772-1.782 at 2 and 1.799-1.828 uncapped.
 constexpr uint64_t kAccCapFrom = 1ull << 28;
 constexpr int kAccCapPerCU = 2;
 constexpr int kAccFirstCapPerCU = 4;
+constexpr int kAccCheckCapPerCU = 4;
 
 // LDS to reserve so that at most per_cu blocks are resident on a CU (0: none).
 inline size_t cap_lds_bytes(int per_cu, const DeviceProps &dev) {
@@ -738,9 +741,11 @@ size_t step_lds_bytes(uint64_t count, const DeviceProps &dev) {
     return cap_lds_bytes(per_cu, dev);
 }
 
-inline size_t accumulate_lds_bytes(uint64_t count, bool first, const DeviceProps &dev) {
+inline size_t accumulate_lds_bytes(uint64_t count, bool first, bool check,
+                                   const DeviceProps &dev) {
     if (count < kAccCapFrom) return 0;
-    return cap_lds_bytes(first ? kAccFirstCapPerCU : kAccCapPerCU, dev);
+    return cap_lds_bytes(first ? kAccFirstCapPerCU : check ? kAccCheckCapPerCU : kAccCapPerCU,
+                         dev);
 }
 
 inline uint32_t grid_for(uint64_t need) {
@@ -786,7 +791,7 @@ hipError_t accumulate_dispatch(float *acc, const uint16_t *g16, uint64_t count,
     const uint64_t rest = count - head - n_tiles * kTile;
     const uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
     accumulate_vec<DT, FIRST, kAccU, CHECK><<<grid_for(need), kThreads,
-                                              accumulate_lds_bytes(count, FIRST, dev), stream>>>(
+                                              accumulate_lds_bytes(count, FIRST, CHECK, dev), stream>>>(
         acc, g16, count, head, n_tiles, chk);
     return hipGetLastError();
 }
