@@ -332,6 +332,76 @@ def test_sumsq_single_quotients_bit_exact():
     log(f"single-gradient sums of squares: {n} cases bit-exact")
 
 
+def test_sumsq_quotients_inside_vectors_bit_exact():
+    # Quotients at every place a gradient can sit (head, each lane of a 16-B
+    # vector, the vectors in flight and the remainder, the tail) in shards of
+    # zeros, for scales that are not powers of two: a quotient below the
+    # normal range (divided), one near 2^-125 (either side of the test), and
+    # a normal quotient in a vector whose zeros send it down the per-element
+    # branch (the product kept).  With at most two nonzero squares every
+    # summation order gives the same FP64 value, so the FP64 partial sums
+    # (the kernel's scratch, zero-filled first; white-box) must add up to the
+    # oracle's FP64 sum bit for bit, and the FP32 result must match too.
+    rng = np.random.default_rng(12)
+    scales = [3.0, 1000.0, float(np.float32(0.3)), 6.0, 3.0 * 2.0 ** 20, 3.0 * 2.0 ** 100]
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    s = torch.zeros(1, device=DEV)
+    parts = torch.zeros(zs.SUMSQ_PARTIALS, dtype=torch.float64, device=DEV)
+    count = 20_011
+    n_cases = n_divided = 0
+
+    def encode(x, fmt):
+        x = np.array([x], np.float32)
+        b = int(x.view(np.uint32)[0]) if fmt == "f32" else int(oracle.encode16(x, fmt)[0])
+        return b if b & 0x7fffffff else 1            # never zero: the smallest subnormal
+
+    def value(b, fmt):
+        if fmt == "f32":
+            return float(np.uint32(b).view(np.float32))
+        return float(oracle.decode16(np.array([b], np.uint16), fmt)[0])
+
+    for fmt in ("f16", "bf16", "f32"):
+        for phase in (0, 5):
+            gv = GuardedView(count, torch.float32 if fmt == "f32" else TD[fmt], phase, DEV)
+            head = line_head(phase, 4 if fmt == "f32" else 2)
+            per_vec = 4 if fmt == "f32" else 8
+            pos = sorted({*range(0, min(head, 3)), head - 1, *range(head, head + per_vec + 1),
+                          count // 2, count // 2 + 1, count - 9, count - 2, count - 1,
+                          *rng.integers(head, count, 6).tolist()} - {-1})
+            for S in scales:
+                for p in pos:
+                    q = p + 1 if p + 1 < count else p - 1
+                    sign = 1.0 if rng.random() < 0.5 else -1.0
+                    tiny = encode(sign * S * 2.0 ** rng.uniform(-152, -124), fmt)
+                    normal = encode(2.0 ** rng.uniform(-10, 10), fmt)
+                    for placed in (((p, tiny),), ((p, tiny), (q, normal)), ((p, normal),)):
+                        bits = np.zeros(count, np.uint32 if fmt == "f32" else np.uint16)
+                        for i, b in placed:
+                            bits[i] = b
+                        parts.zero_()
+                        if fmt == "f32":
+                            gv.view.copy_(torch.from_numpy(bits.view(np.float32)).to(DEV))
+                            zs.zero_overflow_check_g32(gv.view, count, 1, 0, S, flag, s, parts)
+                            rf, rs = oracle.overflow_check_g32(bits.view(np.float32), S)
+                        else:
+                            gv.view.copy_(torch.from_numpy(bits.view(np.int16).copy())
+                                          .view(TD[fmt]).to(DEV))
+                            zs.zero_overflow_check(gv.view, count, 1, 0, S, flag, s, parts)
+                            rf, rs = oracle.overflow_check(bits, fmt, S)
+                        got = parts.cpu().numpy().sum()
+                        case = (fmt, phase, S, [(i, hex(b)) for i, b in placed])
+                        assert int(flag.item()) == rf == 0, case
+                        assert np.float64(got).view(np.uint64) == np.float64(rs).view(np.uint64), \
+                            (case, got, rs)
+                        assert np.float32(s.item()).view(np.uint32) == \
+                            np.float32(rs).view(np.uint32), case
+                        n_cases += 1
+                        n_divided += any(abs(value(b, fmt) / S) < 2.0 ** -126 for _, b in placed)
+            assert gv.guards_intact()
+    log(f"sums of squares with quotients inside vectors: {n_cases} cases bit-exact "
+        f"({n_divided} with a subnormal quotient)")
+
+
 def test_calls_return_without_synchronising():
     # A bounded spin kernel ahead of them on the stream: the check and the step
     # are enqueued behind it and the calls return while it still runs.

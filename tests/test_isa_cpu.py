@@ -88,8 +88,9 @@ def test_sum_of_squares_visits_every_vector_lane(asm):
     # vector + the scalar head and tail = n visits per path).  S a power of
     # two: multiply by 1/S in FP32, widen, one FP64 FMA.  Any other S: widen,
     # one FP64 multiply by RN64(1/S), one rounding to FP32, widen again, one
-    # FP64 FMA -- and, only in the branch for subnormal quotients, the FP32
-    # divide.  Plus the two reciprocals (FP32 and FP64) once per lane.
+    # FP64 FMA -- and, in the branch a vector takes when a quotient is below
+    # 2^-125 (zeros included), one guarded FP32 divide per gradient.  Plus the
+    # two reciprocals (FP32 and FP64) once per lane.
     _, kernels = asm
     sumsq = {k: b for k, b in kernels.items() if "overflow_sumsq_kernel" in k}
     assert len(sumsq) == 3

@@ -450,8 +450,12 @@ __device__ __forceinline__ double wave_sum_to_lane63(double x) {
 //    significand, which the product of S's odd significand (> 1) and a
 //    16-bit or FP32 gradient's cannot equal, and two unequal multiples of a
 //    power of two differ by at least that power.  So the one rounding to
-//    FP32 gives exactly g / S -- wherever the quotient is a normal number; a
-//    vector with a quotient below 2^-125 in magnitude is divided as written.
+//    FP32 gives exactly g / S -- wherever the quotient is a normal number.
+//    A rounded quotient of at least 2^-125 in magnitude comes from a normal
+//    one, and g = 0 gives 0 either way; every other gradient (g != 0 with
+//    |q| < 2^-125) is divided as written.  One compare per gradient finds
+//    the vectors that hold any quotient below 2^-125 (zeros included); only
+//    those check their gradients one by one.
 //  - q*q is exact in FP64 (a 24-bit significand squared), so one FP64 fma
 //    equals the square followed by the addition.
 //  - A lane's FP64 sum is not finite iff one of its q is (finite squares of
@@ -478,9 +482,9 @@ __global__ __launch_bounds__(kThreads) void overflow_sumsq_kernel(
 
     auto run = [&](auto pow2_tag) {
         constexpr bool kPow2 = decltype(pow2_tag)::value;
-        // K gradients: unscale all, redo them by division if one quotient is
-        // subnormal (never with the power-of-two multiply), then add the
-        // squares in order
+        // K gradients: unscale all, divide those whose product may have
+        // missed the quotient (never with the power-of-two multiply), then
+        // add the squares in order
         auto visit_n = [&](auto k_tag, const float *gr) {
             constexpr int K = decltype(k_tag)::value;
             float q[K];
@@ -490,14 +494,15 @@ __global__ __launch_bounds__(kThreads) void overflow_sumsq_kernel(
                 if constexpr (kPow2) {
                     q[j] = gr[j] * inv;
                 } else {
-                    const double qq = static_cast<double>(gr[j]) * rcp;
-                    q[j] = static_cast<float>(qq);
-                    tiny |= __builtin_fabs(qq) < 0x1p-125;
+                    q[j] = static_cast<float>(static_cast<double>(gr[j]) * rcp);
+                    tiny |= __builtin_fabsf(q[j]) < 0x1p-125f;
                 }
             }
             if (!kPow2 && tiny) {
 #pragma unroll
-                for (int j = 0; j < K; ++j) q[j] = gr[j] / loss_scale;
+                for (int j = 0; j < K; ++j)
+                    if (gr[j] != 0.0f && __builtin_fabsf(q[j]) < 0x1p-125f)
+                        q[j] = gr[j] / loss_scale;
             }
 #pragma unroll
             for (int j = 0; j < K; ++j) {
