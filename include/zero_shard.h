@@ -42,8 +42,9 @@
  *   - All device work is enqueued on `stream` (a hipStream_t; 0 = the null
  *     stream) of the current HIP device, and the call returns without
  *     synchronising.  Calls are thread-safe: the library has no mutable
- *     state shared between calls other than a per-device cache of the
- *     compute-unit count and the grid cap of zero_set_grid_cap.
+ *     state shared between calls other than a per-device cache of device
+ *     properties (compute units, LDS sizes) and the settings of
+ *     zero_set_grid_cap and zero_set_step_occupancy.
  */
 #ifndef ZERO_SHARD_H_
 #define ZERO_SHARD_H_
