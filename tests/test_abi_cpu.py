@@ -536,3 +536,18 @@ def test_flag_control_and_check_outputs_may_not_overlap_the_views():
                                      1e-3, 0.9, 0.999, 1e-8, 0.0, FAKE + 64, None) == -1
     # the bias table over the control block the decision writes
     assert zs.lib.zero_scaler_update_dev(FAKE * 8, FAKE * 8 + 16, 1, 4, None) == -1
+
+
+def test_tuning_setters_take_any_32_bit_value_and_the_binding_checks_range():
+    # host-only stores; the kernels clamp what they read (grid cap: 1 .. 2^23
+    # blocks, 0 = default; occupancy: 0 = by size, 8 and above = no cap)
+    for v in (0, 1, 7, 8, 9, 2 ** 23, 2 ** 32 - 1):
+        assert zs.lib.zero_set_grid_cap(v) == 0
+        assert zs.lib.zero_set_step_occupancy(v) == 0
+    for bad in (-1, 2 ** 32):
+        with pytest.raises(ValueError):
+            zs.zero_set_grid_cap(bad)
+        with pytest.raises(ValueError):
+            zs.zero_set_step_occupancy(bad)
+    zs.zero_set_grid_cap(0)
+    zs.zero_set_step_occupancy(0)

@@ -145,6 +145,8 @@ def zero_set_grid_cap(blocks: int) -> None:
 
 def zero_set_step_occupancy(blocks_per_cu: int) -> None:
     """Resident step blocks per CU: 0 chooses by shard size, 1-7 cap, 8+ removes the cap."""
+    if not 0 <= blocks_per_cu < 1 << 32:
+        raise ValueError("blocks_per_cu must fit in 32 bits")
     lib.zero_set_step_occupancy(blocks_per_cu)
 
 
