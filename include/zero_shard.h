@@ -454,7 +454,8 @@ typedef struct {
  * into one more FNV-1a state from the same start.
  * The file is written as path + ".tmp", flushed to the device and renamed
  * over path, so a reader finds either the previous file or the complete new
- * one; on failure the temporary file is removed.
+ * one; the directory is then flushed too where the file system allows it.
+ * On failure the temporary file is removed.
  *   w16, master, m, v  HOST arrays of count elements.
  *   Errors: ZERO_EINVAL (bad layout, NULL pointers), ZERO_EDTYPE, ZERO_EIO.
  */

@@ -15,6 +15,7 @@
 // lane i mod 4 by FNV-1a (h ^= w; h *= prime), and the four lane values are
 // then folded, lane 0 first, into one more FNV-1a state.  Four lanes give four
 // independent multiply chains, so hashing keeps up with the file system.
+#include <fcntl.h>
 #include <unistd.h>
 
 #include <cstdio>
@@ -175,6 +176,19 @@ void to_info(const zero_ckpt_header &h, zero_ckpt_info *info) {
     info->scaler.clean_steps = h.clean_steps;
 }
 
+// Flush the directory entry of `path` after a rename, so that the new name
+// survives a crash too; best effort (some file systems cannot sync a
+// directory, and the file's own data is already on the device).
+void sync_parent_dir(const char *path) {
+    const std::string p(path);
+    const size_t slash = p.find_last_of('/');
+    const std::string dir = slash == std::string::npos ? "." : slash == 0 ? "/" : p.substr(0, slash);
+    const int fd = open(dir.c_str(), O_RDONLY | O_DIRECTORY);
+    if (fd < 0) return;
+    (void)fsync(fd);
+    close(fd);
+}
+
 }  // namespace
 
 extern "C" int zero_ckpt_write(const char *path, const zero_ckpt_info *info, const void *w16,
@@ -219,15 +233,19 @@ extern "C" int zero_ckpt_write(const char *path, const zero_ckpt_info *info, con
     ok = ok && std::fflush(f) == 0 && fsync(fileno(f)) == 0;
     ok = (std::fclose(f) == 0) && ok;
     if (ok && std::rename(tmp.c_str(), path) != 0) ok = false;
-    if (!ok) std::remove(tmp.c_str());
-    return ok ? ZERO_OK : ZERO_EIO;
+    if (!ok) {
+        std::remove(tmp.c_str());
+        return ZERO_EIO;
+    }
+    sync_parent_dir(path);
+    return ZERO_OK;
 }
 
 extern "C" int zero_ckpt_read_info(const char *path, zero_ckpt_info *info) {
     if (path == nullptr || info == nullptr) return ZERO_EINVAL;
     FILE *f = std::fopen(path, "rb");
     if (f == nullptr) return ZERO_EIO;
-    zero_ckpt_header h;
+    zero_ckpt_header h{};
     const int rc = read_header(f, &h);
     std::fclose(f);
     if (rc != ZERO_OK) return rc;
@@ -239,7 +257,7 @@ extern "C" int zero_ckpt_verify(const char *path) {
     if (path == nullptr) return ZERO_EINVAL;
     FILE *f = std::fopen(path, "rb");
     if (f == nullptr) return ZERO_EIO;
-    zero_ckpt_header h;
+    zero_ckpt_header h{};
     int rc = read_header(f, &h);
     if (rc == ZERO_OK && fseeko(f, sizeof h, SEEK_SET) != 0) rc = ZERO_EIO;
     Hasher hs;
@@ -266,7 +284,7 @@ extern "C" int zero_ckpt_read(const char *path, uint64_t first, uint64_t count, 
         return ZERO_EINVAL;
     FILE *f = std::fopen(path, "rb");
     if (f == nullptr) return ZERO_EIO;
-    zero_ckpt_header h;
+    zero_ckpt_header h{};
     int rc = read_header(f, &h);
     if (rc == ZERO_OK && (first > h.count || count > h.count - first)) rc = ZERO_EINVAL;
     const uint64_t base = sizeof h;
