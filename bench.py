@@ -163,25 +163,35 @@ def cpu_baseline(bufs, w, budget_s: float, sample: int):
 
 
 def copy_bandwidth(dev, gib: int = 4):
-    """Same-run plain device copy (torch copy_): GB/s of read + write bytes."""
+    """Same-run plain device copies of gib GiB, GB/s of read + write bytes: the
+    runtime's copy (torch copy_), and the library's own streaming copy (a one-shard
+    all-gather: one read and one write stream with the step's 16-B, one-tile-per-block
+    access pattern)."""
     import torch
+
+    import zero_sharded_mixed_shard_amd as zs
 
     n = gib * (1 << 30) // 4
     a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
     b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 5
-    e0.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+
+    def rate(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 2 * n * 4 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+
+    runtime = rate(lambda: b.copy_(a))
+    stream = rate(lambda: zs.zero_gather_shards(b, [a], n, 1))
     del a, b
     torch.cuda.empty_cache()
-    return 2 * n * 4 / (ms * 1e-3) / 1e9
+    return runtime, stream
 
 
 def measure_extras(dev, n_elem: int = 1 << 30, reps: int = 5) -> dict:
@@ -523,7 +533,7 @@ def main():
     achieved = STEP_BYTES_PER_PARAM * cnt / (avg_step_ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name)
 
-    copy_gbps = None if args.no_copy else copy_bandwidth(dev)
+    copy_gbps, stream_copy_gbps = (None, None) if args.no_copy else copy_bandwidth(dev)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
@@ -569,7 +579,8 @@ def main():
                     "overflow_check_ms": avg_check_ms,
                     "overflow_check_GBps": CHECK_BYTES_PER_PARAM * cnt / (avg_check_ms * 1e-3)
                     / 1e9,
-                    "device_copy_GBps": copy_gbps},
+                    "device_copy_GBps": copy_gbps,
+                    "stream_copy_GBps": stream_copy_gbps},
         "cpu_baseline": cpu,
     }
     if extras is not None:
