@@ -67,13 +67,6 @@ int device_props(zs::DeviceProps *out) {
     return ZERO_OK;
 }
 
-int device_cus(int *cus) {
-    zs::DeviceProps p;
-    const int rc = device_props(&p);
-    if (rc == ZERO_OK) *cus = p.cus;
-    return rc;
-}
-
 std::atomic<uint64_t> g_grid_cap{zs::kMaxBlocks};
 
 bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
@@ -194,12 +187,12 @@ extern "C" int zero_overflow_check(const void *g16, zero_dtype dt, uint64_t psi,
     if (!check_outputs_ok(g16, 2 * count, d_found_inf, 4, d_sumsq,
                           d_sumsq != nullptr ? d_partials : nullptr))
         return ZERO_EINVAL;
-    int cus = 0;
-    rc = device_cus(&cus);
+    zs::DeviceProps dev;
+    rc = device_props(&dev);
     if (rc != ZERO_OK) return rc;
     const hipError_t e = zs::launch_overflow_check(
         static_cast<int>(dt), static_cast<const uint16_t *>(g16), count, loss_scale, nullptr,
-        d_found_inf, d_sumsq, d_partials, cus, static_cast<hipStream_t>(stream));
+        d_found_inf, d_sumsq, d_partials, dev, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check launch");
 }
 
@@ -308,12 +301,12 @@ extern "C" int zero_overflow_check_g32(const float *g32, uint64_t psi, uint32_t 
     if (!check_outputs_ok(g32, 4 * lay.count, d_found_inf, 4, d_sumsq,
                           d_sumsq != nullptr ? d_partials : nullptr))
         return ZERO_EINVAL;
-    int cus = 0;
-    const int rc = device_cus(&cus);
+    zs::DeviceProps dev;
+    const int rc = device_props(&dev);
     if (rc != ZERO_OK) return rc;
     const hipError_t e =
         zs::launch_overflow_check_g32(g32, lay.count, loss_scale, nullptr, d_found_inf, d_sumsq,
-                                      d_partials, cus, static_cast<hipStream_t>(stream));
+                                      d_partials, dev, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check_g32 launch");
 }
 
@@ -421,12 +414,12 @@ extern "C" int zero_overflow_check_dev(const void *g16, zero_dtype dt, uint64_t 
     if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
     if (!check_outputs_ok(g16, 2 * count, d_ctl, sizeof(zero_device_ctl), nullptr, nullptr))
         return ZERO_EINVAL;
-    int cus = 0;
-    rc = device_cus(&cus);
+    zs::DeviceProps dev;
+    rc = device_props(&dev);
     if (rc != ZERO_OK) return rc;
     const hipError_t e = zs::launch_overflow_check(
         static_cast<int>(dt), static_cast<const uint16_t *>(g16), count, 1.0f,
-        &d_ctl->scaler.loss_scale, &d_ctl->found_inf, nullptr, nullptr, cus,
+        &d_ctl->scaler.loss_scale, &d_ctl->found_inf, nullptr, nullptr, dev,
         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check_dev launch");
 }
@@ -470,11 +463,11 @@ extern "C" int zero_overflow_check_g32_dev(const float *g32, uint64_t psi, uint3
     if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
     if (!check_outputs_ok(g32, 4 * lay.count, d_ctl, sizeof(zero_device_ctl), nullptr, nullptr))
         return ZERO_EINVAL;
-    int cus = 0;
-    const int rc = device_cus(&cus);
+    zs::DeviceProps dev;
+    const int rc = device_props(&dev);
     if (rc != ZERO_OK) return rc;
     const hipError_t e = zs::launch_overflow_check_g32(
-        g32, lay.count, 1.0f, &d_ctl->scaler.loss_scale, &d_ctl->found_inf, nullptr, nullptr, cus,
+        g32, lay.count, 1.0f, &d_ctl->scaler.loss_scale, &d_ctl->found_inf, nullptr, nullptr, dev,
         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check_g32_dev launch");
 }

@@ -55,7 +55,7 @@ hipError_t launch_adam_step(int dtype, uint16_t *w16, const uint16_t *g16, float
 // loss_scale with a value read on the device.
 hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
                                  const float *loss_scale_dev, int32_t *flag, float *sumsq,
-                                 double *partials, int num_cus, hipStream_t stream);
+                                 double *partials, const DeviceProps &dev, hipStream_t stream);
 
 // The step with FP32 gradients (dtype: the working weights' format); flag and
 // ctl as for launch_adam_step.
@@ -81,7 +81,8 @@ hipError_t launch_grad_accumulate_check(int dtype, float *acc, const uint16_t *g
 // loss_scale_dev as for launch_overflow_check.
 hipError_t launch_overflow_check_g32(const float *g32, uint64_t count, float loss_scale,
                                      const float *loss_scale_dev, int32_t *flag, float *sumsq,
-                                     double *partials, int num_cus, hipStream_t stream);
+                                     double *partials, const DeviceProps &dev,
+                                     hipStream_t stream);
 
 // Views of up to ZERO_MAX_LOCAL_RANKS replicas or shards, passed by value.
 constexpr uint32_t kMaxLocalRanks = 64;  // == ZERO_MAX_LOCAL_RANKS

@@ -353,7 +353,10 @@ template <int DT> struct GradBits<float, DT> {
 // the magnitude bits (packed 16-bit maxima for 16-bit gradients) and divides
 // once at the end: the pass is two integer operations per gradient and runs
 // at read bandwidth.  Elements [0, head) and [head + kPerVec*n_vec, count)
-// one at a time; in between, 16-B vectors, grid-stride, U in flight per lane.
+// one at a time; in between, 16-B vectors in tiles of U*256: lane l of tile
+// t reads vectors t*U*256 + u*256 + l, so every wave instruction covers one
+// contiguous 1 KiB, and each block reads one tile (a loop only past the grid
+// cap), like the step.
 template <typename GT, int DT, int U>
 __global__ __launch_bounds__(kThreads) void overflow_flag_kernel(
     const GT *__restrict__ g, uint64_t count, uint32_t head, uint64_t n_vec, float loss_scale,
@@ -384,16 +387,19 @@ __global__ __launch_bounds__(kThreads) void overflow_flag_kernel(
         }
     };
     const u32x4 *vec = reinterpret_cast<const u32x4 *>(g + head);
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
-    uint64_t k = static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
-    for (; k + (U - 1) * stride < n_vec; k += U * stride) {
+    constexpr uint64_t kTileVec = static_cast<uint64_t>(U) * kThreads;
+    for (uint64_t t = blockIdx.x; t * kTileVec < n_vec; t += gridDim.x) {
+        const uint64_t k0 = t * kTileVec + tid;
         u32x4 x[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = load_nt(vec + k + u * stride);
+        for (int u = 0; u < U; ++u) {
+            const uint64_t k = k0 + static_cast<uint64_t>(u) * kThreads;
+            x[u] = k < n_vec ? load_nt(vec + k) : u32x4{0u, 0u, 0u, 0u};  // 0: no magnitude
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) fold(x[u]);
     }
-    for (; k < n_vec; k += stride) fold(load_nt(vec + k));
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     for (uint64_t i = head + n_vec * B::kPerVec + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
          i < count; i += stride) {
         const uint32_t a = mag(g[i]);
@@ -638,15 +644,17 @@ __global__ void scaler_decide(zero_device_ctl *__restrict__ ctl, const float *__
 constexpr int kAdamU = 2;              // groups in flight per lane in the step
 constexpr int kAccU = 2;               // groups in flight per lane in the accumulate
 constexpr int kCheckU = 4;             // 16-B vectors in flight per lane in the check
-// Check grids (measured on MI355X, 256 CUs).  Up to 8 GiB of gradients, one
-// round of 7 blocks per CU streams fastest (6.7-7.1 TB/s against 6.3-6.8 for
-// larger grids); beyond it, 128 blocks per CU (7.0 TB/s at 20 GB against 6.65
-// for one round).  The sum of squares takes at most 1792 blocks (one round
+// The flag-only check reads one tile of 4 x 256 vectors per block, 3 resident
+// blocks per CU from 128 MiB of gradients (measured on MI355X, same arrays,
+// TB/s against the grid-stride loop it replaced at 7 or 128 blocks per CU):
+// 1e10 FP16 gradients 7.35-7.40 against 6.77-7.07, 937.5M 7.17-7.29
+// against 6.62-6.86, 137.7M 6.93-6.99 against 6.57-6.66 (2 per CU: 6.1-7.0,
+// 4: 6.8-7.1, uncapped: 6.8-7.3); below, uncapped (15.5M: 5.6 TB/s, the
+// same as before).  The sum of squares takes at most 1792 blocks (one round
 // on 256 CUs) whatever the device, so its partial sums depend on the size
 // and the view's phase only.
-constexpr int kCheckBlocksPerCURound = 7;
-constexpr int kCheckBlocksPerCU = 128;
-constexpr uint64_t kCheckRoundBytes = 8ull << 30;
+constexpr uint64_t kCheckCapFromBytes = 128ull << 20;
+constexpr int kCheckCapPerCU = 3;
 constexpr uint32_t kSumsqBlocks = 1792;
 static_assert(kSumsqBlocks <= kSumsqPartials, "one partial per block");
 
@@ -805,13 +813,14 @@ struct CheckGrid {
     uint32_t head;    // elements done one at a time before the first line-aligned vector
     uint64_t n_vec;   // 16-B vectors
     uint32_t blocks;  // grid size (with a sum of squares: the number of partials)
+    size_t lds;       // LDS reserved per block to cap resident blocks (flag only)
 };
 
 // With a sum of squares the grid depends on the size and the pointer's phase
 // only, never on the device, so the partial sums and their order are the
-// same everywhere.  The flag-only grid is sized per CU.
+// same everywhere.  The flag-only grid is one block per tile.
 template <typename GT, int DT>
-CheckGrid check_grid(const GT *g, uint64_t count, bool sumsq, int num_cus) {
+CheckGrid check_grid(const GT *g, uint64_t count, bool sumsq, const DeviceProps &dev) {
     CheckGrid c;
     c.head = align_head(addr(g), sizeof(GT), kLine);
     if (c.head > count) c.head = static_cast<uint32_t>(count);
@@ -821,21 +830,20 @@ CheckGrid check_grid(const GT *g, uint64_t count, bool sumsq, int num_cus) {
     uint64_t need = c.n_vec > 0 ? (c.n_vec + per_block - 1) / per_block
                                 : (rest + kThreads - 1) / kThreads;
     if (need == 0) need = 1;
-    const int per_cu = count * sizeof(GT) < kCheckRoundBytes ? kCheckBlocksPerCURound
-                                                             : kCheckBlocksPerCU;
-    uint64_t cap = sumsq ? kSumsqBlocks : static_cast<uint64_t>(num_cus) * per_cu;
-    if (!sumsq && cap > max_blocks()) cap = max_blocks();  // the partials' grid stays fixed
+    const uint64_t cap = sumsq ? kSumsqBlocks : max_blocks();  // the partials' grid stays fixed
     c.blocks = static_cast<uint32_t>(need < cap ? need : cap);
+    c.lds = !sumsq && count * sizeof(GT) >= kCheckCapFromBytes ? cap_lds_bytes(kCheckCapPerCU, dev)
+                                                               : 0;
     return c;
 }
 
 template <typename GT, int DT>
 hipError_t check_dispatch(const GT *g, uint64_t count, float loss_scale,
                           const float *loss_scale_dev, int32_t *flag, float *sumsq,
-                          double *partials, int num_cus, hipStream_t stream) {
-    const CheckGrid c = check_grid<GT, DT>(g, count, sumsq != nullptr, num_cus);
+                          double *partials, const DeviceProps &dev, hipStream_t stream) {
+    const CheckGrid c = check_grid<GT, DT>(g, count, sumsq != nullptr, dev);
     if (sumsq == nullptr) {
-        overflow_flag_kernel<GT, DT, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
+        overflow_flag_kernel<GT, DT, kCheckU><<<c.blocks, kThreads, c.lds, stream>>>(
             g, count, c.head, c.n_vec, loss_scale, loss_scale_dev, flag);
         return hipGetLastError();
     }
@@ -894,25 +902,26 @@ hipError_t launch_grad_accumulate_check(int dtype, float *acc, const uint16_t *g
 
 hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count, float loss_scale,
                                  const float *loss_scale_dev, int32_t *flag, float *sumsq,
-                                 double *partials, int num_cus, hipStream_t stream) {
+                                 double *partials, const DeviceProps &dev, hipStream_t stream) {
     check_init<<<1, 64, 0, stream>>>(flag, sumsq);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess || count == 0) return err;
     if (dtype == 0)
         return check_dispatch<uint16_t, 0>(g16, count, loss_scale, loss_scale_dev, flag, sumsq,
-                                           partials, num_cus, stream);
+                                           partials, dev, stream);
     return check_dispatch<uint16_t, 1>(g16, count, loss_scale, loss_scale_dev, flag, sumsq,
-                                       partials, num_cus, stream);
+                                       partials, dev, stream);
 }
 
 hipError_t launch_overflow_check_g32(const float *g32, uint64_t count, float loss_scale,
                                      const float *loss_scale_dev, int32_t *flag, float *sumsq,
-                                     double *partials, int num_cus, hipStream_t stream) {
+                                     double *partials, const DeviceProps &dev,
+                                     hipStream_t stream) {
     check_init<<<1, 64, 0, stream>>>(flag, sumsq);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess || count == 0) return err;
     return check_dispatch<float, 0>(g32, count, loss_scale, loss_scale_dev, flag, sumsq,
-                                    partials, num_cus, stream);
+                                    partials, dev, stream);
 }
 
 hipError_t launch_scaler_decide(zero_device_ctl *ctl, const float *bias, uint64_t t_first,
