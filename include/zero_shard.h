@@ -41,10 +41,11 @@
  *     slower element-wise kernel gives the same results.
  *   - All device work is enqueued on `stream` (a hipStream_t; 0 = the null
  *     stream) of the current HIP device, and the call returns without
- *     synchronising.  Calls are thread-safe: the library has no mutable
- *     state shared between calls other than a per-device cache of device
- *     properties (compute units, LDS sizes) and the settings of
- *     zero_set_grid_cap and zero_set_step_occupancy.
+ *     synchronising.  Calls are thread-safe and stateless: the only mutable
+ *     state the library keeps between calls is a per-device cache of device
+ *     properties (compute units, LDS sizes), written once with the values
+ *     the runtime reports.  (zero_shard_tuning.h declares test and tuning
+ *     overrides of launch shapes; they are per thread and change no result.)
  */
 #ifndef ZERO_SHARD_H_
 #define ZERO_SHARD_H_
@@ -341,6 +342,9 @@ typedef struct {
     float bc1;             /* 1 - beta1^t of the applied update */
     float bc2;             /* 1 - beta2^t of the applied update */
     int32_t status;        /* 0; ZERO_ERANGE if the bias table missed t (update skipped) */
+    double rcp_loss_scale; /* 1 / loss_scale_used, FP64 correctly rounded */
+    double rcp_bc1;        /* 1 / bc1, FP64 correctly rounded */
+    double rcp_bc2;        /* 1 / bc2, FP64 correctly rounded */
 } zero_device_ctl;
 
 #define ZERO_ERANGE (-4) /* written to zero_device_ctl.status: t outside the bias table */
@@ -374,7 +378,9 @@ int zero_overflow_check_dev(const void *g16, zero_dtype dt, uint64_t psi, uint32
  * reads found_inf, updates scaler, sets apply, and for an applied update
  * records loss_scale_used (S before the decision) and bc1, bc2 for the new
  * step t from the table (entries for t_first .. t_first + len - 1, as
- * zero_bias_corrections writes them).  If t falls outside the table the
+ * zero_bias_corrections writes them), with their FP64 reciprocals (the step
+ * forms its quotients by those three from them, with the same result as the
+ * FP32 division).  If t falls outside the table the
  * update is skipped, status = ZERO_ERANGE and scaler is left as it was.
  *   d_bias  device, 2*len floats.
  *   Errors: ZERO_EINVAL for a NULL or misaligned pointer, len == 0 or
@@ -510,31 +516,6 @@ int zero_reshard_plan(uint64_t psi, uint32_t n_old, uint32_t n_new, uint32_t ran
 int zero_ckpt_read_resharded(const char *const *paths_old, uint32_t n_old, uint64_t psi,
                              uint32_t n_new, uint32_t rank_new, void *w16, float *master,
                              float *m, float *v);
-
-/*
- * zero_set_grid_cap -- cap the grid of every streaming kernel at `blocks`
- * workgroups of 256 threads (0, or a value above the default, restores the
- * default of 2^23).  A shard with more tiles than the grid has blocks is
- * walked by each block in turn, as shards of more than 2^23 tiles always
- * are; tests use a small cap to run those loops at small sizes.  The
- * sum-of-squares form of the check keeps its own size-only grid, so its
- * partial sums do not change.  Process-wide; set it while no other thread is
- * launching.  Returns ZERO_OK.
- */
-int zero_set_grid_cap(uint32_t blocks);
-
-/*
- * zero_set_step_occupancy -- resident blocks per compute unit of the step's
- * vector kernel (both gradient formats, host or device control).  0 (the
- * default) chooses what measured fastest on MI355X: no cap below 2^26
- * elements; from 2^26, 3 blocks per CU with BF16 working weights and 16-bit
- * gradients, 2 with FP16 working weights (3 from 2^33 elements) and 2 with
- * FP32 gradients.  1 to 7 caps every shard at that many; 8 or more removes
- * the cap.  The cap is an LDS reservation the kernel does not use,
- * so results are bitwise the same under every setting.  Process-wide; set it
- * while no other thread is launching.  Returns ZERO_OK.
- */
-int zero_set_step_occupancy(uint32_t blocks_per_cu);
 
 /*
  * zero_strerror -- text for a return code.  For ZERO_EHIP it names the HIP

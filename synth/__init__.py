@@ -144,6 +144,21 @@ def inject_nonfinite_(g16: torch.Tensor, prob: float, seed: int) -> np.ndarray:
     return pos
 
 
+def spread_f32(n: int, seed: int, exp_lo: int, exp_hi: int, signed: bool = True) -> np.ndarray:
+    """n FP32 values whose biased exponent fields are uniform in [exp_lo, exp_hi]
+    (0 = zero and subnormals), with uniform significand bits and, if signed, a
+    random sign: inputs that reach every binade of a chosen range, from the
+    subnormals up.  A subnormal's significand is shifted right by a uniform 0
+    to 22 bits, so the subnormals spread over all of their binades too."""
+    rng = np.random.default_rng(seed)
+    exp = rng.integers(exp_lo, exp_hi + 1, n, dtype=np.uint32)
+    frac = rng.integers(0, 1 << 23, n, dtype=np.uint32)
+    shift = rng.integers(0, 23, n, dtype=np.uint32)
+    frac = np.where(exp == 0, frac >> shift, frac).astype(np.uint32)
+    sign = rng.integers(0, 2, n, dtype=np.uint32) if signed else np.zeros(n, np.uint32)
+    return ((sign << 31) | (exp << 23) | frac).view(np.float32)
+
+
 def gpt2_small_shapes() -> list[tuple[str, tuple[int, ...]]]:
     """GPT-2 small's parameter tensors in flat order (148 tensors, 124,439,808 params).
 

@@ -21,12 +21,26 @@ from zero_sharded_mixed_shard_amd import _binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "zero_shard.h")
+TUNING_HEADER = os.path.join(ROOT, "include", "zero_shard_tuning.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(zero_\w+)\s*\(", text)))
+def declared_functions(*headers):
+    """Functions the given headers declare (default: every header under include/)."""
+    if not headers:
+        inc = os.path.join(ROOT, "include")
+        headers = [os.path.join(inc, f) for f in sorted(os.listdir(inc)) if f.endswith(".h")]
+    names = set()
+    for h in headers:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(zero_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_product_header_holds_no_process_settings():
+    # the launch-shape overrides live in the tuning header only
+    product = declared_functions(HEADER)
+    assert not [n for n in product if n.startswith("zero_set_")], product
+    assert declared_functions(TUNING_HEADER) == ["zero_set_grid_cap", "zero_set_occupancy"]
 
 
 def test_header_declares_the_boundary():
@@ -212,6 +226,7 @@ def test_device_ctl_struct_matches_header():
       printf("%zu %zu", sizeof(zero_device_ctl), _Alignof(zero_device_ctl));
     #define F(f) printf(" %zu", offsetof(zero_device_ctl, f));
       F(scaler) F(found_inf) F(apply) F(loss_scale_used) F(bc1) F(bc2) F(status)
+      F(rcp_loss_scale) F(rcp_bc1) F(rcp_bc2)
       printf(" %zu %d", sizeof(zero_scaler), ZERO_ERANGE);
       return 0;
     }
@@ -225,8 +240,8 @@ def test_device_ctl_struct_matches_header():
                                                check=True).stdout.split()]
     D = _binding.DeviceCtl
     assert vals[0] == ctypes.sizeof(D) and vals[1] == ctypes.alignment(D)
-    assert vals[2:9] == [getattr(D, f).offset for f, _ in D._fields_]
-    assert vals[9] == ctypes.sizeof(_binding.Scaler) and vals[10] == -4
+    assert vals[2:12] == [getattr(D, f).offset for f, _ in D._fields_]
+    assert vals[12] == ctypes.sizeof(_binding.Scaler) and vals[13] == -4
 
 
 @pytest.mark.parametrize("b1,b2,t0,n", [(0.9, 0.999, 1, 64), (0.9, 0.999, 101, 20),
@@ -543,11 +558,11 @@ def test_tuning_setters_take_any_32_bit_value_and_the_binding_checks_range():
     # blocks, 0 = default; occupancy: 0 = by size, 8 and above = no cap)
     for v in (0, 1, 7, 8, 9, 2 ** 23, 2 ** 32 - 1):
         assert zs.lib.zero_set_grid_cap(v) == 0
-        assert zs.lib.zero_set_step_occupancy(v) == 0
+        assert zs.lib.zero_set_occupancy(v) == 0
     for bad in (-1, 2 ** 32):
         with pytest.raises(ValueError):
             zs.zero_set_grid_cap(bad)
         with pytest.raises(ValueError):
-            zs.zero_set_step_occupancy(bad)
+            zs.zero_set_occupancy(bad)
     zs.zero_set_grid_cap(0)
-    zs.zero_set_step_occupancy(0)
+    zs.zero_set_occupancy(0)

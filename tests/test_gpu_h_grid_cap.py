@@ -6,8 +6,8 @@ not fit in one GPU's memory with the step's five arrays, so these tests lower
 the grid cap with zero_set_grid_cap to 1, 3 and 7 blocks and check every
 kernel against the oracle at sizes of many tiles with ragged heads and tails:
 the step (vector and element-wise paths, 16-bit and FP32 gradients), the
-accumulate, the flag check and both exchanges.  The step's occupancy setting
-(zero_set_step_occupancy) must leave every result bit unchanged.
+accumulate, the flag check and both exchanges.  The occupancy setting
+(zero_set_occupancy) must leave every result bit and flag unchanged.
 """
 import numpy as np
 import pytest
@@ -136,9 +136,9 @@ def test_exchanges_tile_loop(cap):
 
 def test_step_occupancy_settings_change_nothing():
     # The step's occupancy cap is an LDS reservation the kernel never touches:
-    # under every setting -- by size (0; a cap of 3 per CU at this size), 1, 2,
-    # 3 and no cap (8) -- the same inputs give the same bits, and windows
-    # match the oracle.  2^28 + 12,345 elements at phase 3, both formats.
+    # under every setting -- the kernel's rule (0; 2 per CU), 1, 2, 3 and no
+    # cap (8) -- the same inputs give the same bits, and windows match the
+    # oracle.  2^28 + 12,345 elements at phase 3, both formats.
     count, phase = (1 << 28) + 12_345, 3
     for dtype in ("f16", "bf16"):
         td = TD[dtype]
@@ -150,7 +150,7 @@ def test_step_occupancy_settings_change_nothing():
         results = {}
         try:
             for occ in (0, 1, 2, 3, 8):
-                zs.zero_set_step_occupancy(occ)
+                zs.zero_set_occupancy(occ)
                 V["master"].view.copy_(master0.to(DEV))
                 for k in ("m", "v", "w16"):
                     V[k].view.zero_()
@@ -162,7 +162,7 @@ def test_step_occupancy_settings_change_nothing():
                 results[occ] = {k: V[k].view.clone() for k in ("w16", "master", "m", "v")}
         finally:
             torch.cuda.synchronize()
-            zs.zero_set_step_occupancy(0)
+            zs.zero_set_occupancy(0)
         for occ in (1, 2, 3, 8):
             for k in results[0]:
                 assert torch.equal(results[occ][k].view(torch.int16 if k == "w16" else
@@ -183,3 +183,53 @@ def test_step_occupancy_settings_change_nothing():
         del results, V
         torch.cuda.empty_cache()
     log("step occupancy settings 0/1/2/3/8: bitwise equal, windows match the oracle")
+
+
+def test_accumulate_and_check_occupancy_settings_change_nothing():
+    # The same for the accumulates (first micro-batch, later ones, the fused
+    # check) and the flag-only check: every setting gives the same bits and
+    # flags.  2^28 + 777 elements (past the size where the rules cap) at phase 1,
+    # with one non-finite gradient planted for the flags.
+    count, phase = (1 << 28) + 777, 1
+    g16 = synth.fill_normal_(torch.empty(count, dtype=torch.float16), 1e-3, 72_000)
+    g16b = synth.fill_normal_(torch.empty(count, dtype=torch.float16), 1e-3, 72_001)
+    g16b[count - 5] = float("inf")
+    G = GuardedView(count, torch.float16, phase, DEV)
+    Gb = GuardedView(count, torch.float16, phase, DEV)
+    G.view.copy_(g16.to(DEV))
+    Gb.view.copy_(g16b.to(DEV))
+    A = GuardedView(count, torch.float32, phase, DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    results = {}
+    try:
+        for occ in (0, 1, 2, 4, 8):
+            zs.zero_set_occupancy(occ)
+            flags = []
+            zs.zero_grad_accumulate(A.view, G.view, count, 1, 0, first=True)
+            zs.zero_grad_accumulate(A.view, G.view, count, 1, 0, first=False)
+            zs.zero_grad_accumulate_check(A.view, Gb.view, count, 1, 0, first=False,
+                                          loss_scale=1024.0, found_inf=flag)
+            flags.append(int(flag.item()))
+            for g in (G, Gb):
+                zs.zero_overflow_check(g.view, count, 1, 0, 1024.0, flag)
+                flags.append(int(flag.item()))
+            torch.cuda.synchronize()
+            results[occ] = (A.view.clone(), flags)
+    finally:
+        torch.cuda.synchronize()
+        zs.zero_set_occupancy(0)
+    assert results[0][1] == [1, 0, 1]
+    for occ in (1, 2, 4, 8):
+        assert results[occ][1] == results[0][1], occ
+        assert torch.equal(results[occ][0].view(torch.int32), results[0][0].view(torch.int32)), occ
+    assert A.guards_intact() and G.guards_intact() and Gb.guards_intact()
+    # two windows against the oracle's accumulate
+    for a, b in ((0, 4096), (count - 4096, count)):
+        acc = np.zeros(b - a, np.float32)
+        oracle.grad_accumulate(acc, u16(g16)[a:b], "f16", True)
+        oracle.grad_accumulate(acc, u16(g16)[a:b], "f16", False)
+        oracle.grad_accumulate(acc, u16(g16b)[a:b], "f16", False)
+        assert np.array_equal(f32(results[0][0][a:b]).view(np.uint32), acc.view(np.uint32))
+    del results
+    torch.cuda.empty_cache()
+    log("accumulate / check occupancy settings 0/1/2/4/8: bitwise equal flags and sums")

@@ -43,18 +43,36 @@ def test_no_forbidden_instructions(asm):
     assert not re.search(r"\bs_dcache_(wb|discard)\w*", text)
 
 
+# per element of the step, by unscale mode (0: S a power of two, multiply by
+# the exact 1/S; 1: FP64 reciprocal product; 2: the device control block picks
+# one of the two bodies): FP32 divisions (the update's (lr*m^)/den, and one
+# guarded fallback per quotient formed as an FP64 product) and FP64 products
+DIVS_PER_ELEM = {0: 3, 1: 4}
+PRODUCTS_PER_ELEM = {0: 2, 1: 3}
+STEP_NAME = re.compile(r"adam_step_(vec|elem)ILi(\d)E([tf])(?:Li2E)?Li(\d)EE")
+
+
 def test_step_kernels_keep_each_operation_correctly_rounded(asm):
     _, kernels = asm
     steps = {k: b for k, b in kernels.items() if "adam_step" in k}
-    # vector and element-wise kernels, FP16 and BF16 weights, 16-bit and FP32 gradients
-    assert len(steps) == 8
+    # vector and element-wise kernels x FP16 / BF16 weights x 16-bit / FP32
+    # gradients x three unscale modes
+    assert len(steps) == 24
     for name, body in steps.items():
+        mode = int(STEP_NAME.search(name).group(4))
+        modes = (0, 1) if mode == 2 else (mode,)
         sq = count(body, "v_sqrt_f32_e32") + count(body, "v_sqrt_f32_e64")
-        assert sq >= 1, name
-        # four divisions per element (unscale, two bias corrections, update),
-        # each the full scale / reciprocal / fma / fixup sequence
-        assert count(body, "v_div_fixup_f32") == 4 * sq, name
-        assert count(body, "v_div_fmas_f32") == 4 * sq, name
+        assert sq >= len(modes) and sq % len(modes) == 0, name
+        per_body = sq // len(modes)         # element bodies: tile elements, head, tail
+        # every division left is the full scale / reciprocal / fma / fixup sequence
+        divs = sum(DIVS_PER_ELEM[md] for md in modes) * per_body
+        assert count(body, "v_div_fixup_f32") == divs, name
+        assert count(body, "v_div_fmas_f32") == divs, name
+        # each constant-divisor quotient: widen, one FP64 product, one rounding
+        prods = sum(PRODUCTS_PER_ELEM[md] for md in modes) * per_body
+        assert count(body, "v_mul_f64") == prods, name
+        assert count(body, "v_cvt_f32_f64_e32") == prods, name
+        assert count(body, "v_div_fixup_f64") == 0, name   # reciprocals come from the host
         # the square root is refined to the correctly rounded result
         assert count(body, "v_cmp_class_f32_e32") + count(body, "v_cmp_class_f32_e64") >= sq
         if "ILi0E" in name:      # FP16 (the SDWA form writes the upper half-word)
@@ -66,7 +84,7 @@ def test_step_kernels_keep_each_operation_correctly_rounded(asm):
 def test_vector_step_uses_16_byte_accesses(asm):
     _, kernels = asm
     vec = {k: b for k, b in kernels.items() if "adam_step_vec" in k}
-    assert len(vec) == 4
+    assert len(vec) == 12
     for name, body in vec.items():
         g32 = "EfLi" in name     # FP32 gradients: one more 16-B load per group
         assert count(body, "global_load_dwordx4") >= (8 if g32 else 6)  # master, m, v (, g)

@@ -89,7 +89,7 @@ from ._binding import (  # noqa: F401
     zero_scaler_update,
     zero_scaler_update_dev,
     zero_set_grid_cap,
-    zero_set_step_occupancy,
+    zero_set_occupancy,
     zero_shard_layout,
     zero_strerror,
 )
@@ -129,7 +129,7 @@ __all__ = [
     "zero_reshard_plan",
     "zero_ckpt_read_resharded",
     "zero_set_grid_cap",
-    "zero_set_step_occupancy",
+    "zero_set_occupancy",
     "layout",
     "overflow_check",
     "adam_step",

@@ -78,7 +78,9 @@ class DeviceCtl(ctypes.Structure):
     """zero_device_ctl: the control block the device-resident path keeps in device memory."""
     _fields_ = [("scaler", Scaler), ("found_inf", ctypes.c_int32), ("apply", ctypes.c_int32),
                 ("loss_scale_used", ctypes.c_float), ("bc1", ctypes.c_float),
-                ("bc2", ctypes.c_float), ("status", ctypes.c_int32)]
+                ("bc2", ctypes.c_float), ("status", ctypes.c_int32),
+                ("rcp_loss_scale", ctypes.c_double), ("rcp_bc1", ctypes.c_double),
+                ("rcp_bc2", ctypes.c_double)]
 
 
 lib.zero_grad_accumulate.argtypes = [_vp, _vp, _i32, _u64, _u32, _u32, ctypes.c_int32, _vp]
@@ -125,8 +127,8 @@ lib.zero_adam_step_g32_dev.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32
                                        _f32, _f32, _f32, _f32, _vp, _vp]
 lib.zero_adam_step_g32_dev.restype = _i32
 lib.zero_set_grid_cap.argtypes = [_u32]
-lib.zero_set_step_occupancy.argtypes = [_u32]
-lib.zero_set_step_occupancy.restype = _i32
+lib.zero_set_occupancy.argtypes = [_u32]
+lib.zero_set_occupancy.restype = _i32
 lib.zero_set_grid_cap.restype = _i32
 lib.zero_strerror.argtypes = [_i32]
 lib.zero_strerror.restype = ctypes.c_char_p
@@ -143,11 +145,12 @@ def zero_set_grid_cap(blocks: int) -> None:
     lib.zero_set_grid_cap(blocks)
 
 
-def zero_set_step_occupancy(blocks_per_cu: int) -> None:
-    """Resident step blocks per CU: 0 chooses by shard size, 1-7 cap, 8+ removes the cap."""
+def zero_set_occupancy(blocks_per_cu: int) -> None:
+    """Resident blocks per CU of this thread's streaming-kernel launches (step, accumulates,
+    flag-only check): 0 leaves each kernel its own rule, 1-7 cap, 8+ removes the cap."""
     if not 0 <= blocks_per_cu < 1 << 32:
         raise ValueError("blocks_per_cu must fit in 32 bits")
-    lib.zero_set_step_occupancy(blocks_per_cu)
+    lib.zero_set_occupancy(blocks_per_cu)
 
 
 @dataclass(frozen=True)

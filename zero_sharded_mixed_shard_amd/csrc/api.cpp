@@ -11,6 +11,7 @@
 
 #include "launch.h"
 #include "zero_shard.h"
+#include "zero_shard_tuning.h"
 
 namespace {
 
@@ -30,11 +31,14 @@ std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_lds_cu[kMaxDevices];
 std::atomic<int> g_lds_block[kMaxDevices];
 
-// Resident step blocks per CU set by zero_set_step_occupancy (0: by size).
-std::atomic<int> g_step_per_cu{0};
+// Test and tuning overrides (zero_shard_tuning.h), kept per thread so that one
+// caller's setting never changes another thread's launches: the grid cap and
+// the resident blocks per CU of the streaming kernels (0: each kernel's rule).
+thread_local uint64_t t_grid_cap = zs::kMaxBlocks;
+thread_local int t_occupancy = 0;
 
 int device_props(zs::DeviceProps *out) {
-    out->step_per_cu = g_step_per_cu.load(std::memory_order_relaxed);
+    out->occupancy = t_occupancy;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
@@ -66,8 +70,6 @@ int device_props(zs::DeviceProps *out) {
     out->lds_per_block = lds_block;
     return ZERO_OK;
 }
-
-std::atomic<uint64_t> g_grid_cap{zs::kMaxBlocks};
 
 bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
@@ -103,6 +105,20 @@ bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; }
 // 1 - beta^t formed in FP64 and rounded once to FP32 (bias correction).
 float bias_correction(float beta, uint64_t t) {
     return static_cast<float>(1.0 - std::pow(static_cast<double>(beta), static_cast<double>(t)));
+}
+
+// The scalars that depend on the loss scale and the step number: S, its exact
+// inverse when it is a power of two, the bias corrections, and the FP64
+// reciprocals the kernels form their quotients with.
+void call_scalars(zs::AdamScalars *s, float loss_scale, uint64_t step) {
+    s->loss_scale = loss_scale;
+    s->scale_pow2 = zs::scale_is_pow2(loss_scale) ? 1 : 0;
+    s->inv_scale = 1.0f / loss_scale;  // exact when scale_pow2
+    s->rcp_scale = 1.0 / static_cast<double>(loss_scale);
+    s->bc1 = bias_correction(s->beta1, step);
+    s->bc2 = bias_correction(s->beta2, step);
+    s->rcp_bc1 = 1.0 / static_cast<double>(s->bc1);
+    s->rcp_bc2 = 1.0 / static_cast<double>(s->bc2);
 }
 
 // Checks of a 16-bit gradient view and its layout, shared by the checks and the
@@ -151,25 +167,21 @@ int step_args(void *w16, const void *g, uintptr_t g_align, float *master, float 
     s->eps = eps;
     const float lw = lr * weight_decay;
     s->decay = 1.0f - lw;
-    s->loss_scale = 1.0f;
-    s->bc1 = 1.0f;
-    s->bc2 = 1.0f;
+    call_scalars(s, 1.0f, 1);  // placeholders: the host forms or the control block gives them
     return ZERO_OK;
 }
 
 }  // namespace
 
-uint64_t zs::max_blocks() { return g_grid_cap.load(std::memory_order_relaxed); }
+uint64_t zs::max_blocks() { return t_grid_cap; }
 
 extern "C" int zero_set_grid_cap(uint32_t blocks) {
-    g_grid_cap.store(blocks == 0 || blocks > zs::kMaxBlocks ? zs::kMaxBlocks : blocks,
-                     std::memory_order_relaxed);
+    t_grid_cap = blocks == 0 || blocks > zs::kMaxBlocks ? zs::kMaxBlocks : blocks;
     return ZERO_OK;
 }
 
-extern "C" int zero_set_step_occupancy(uint32_t blocks_per_cu) {
-    g_step_per_cu.store(blocks_per_cu >= 8 ? 8 : static_cast<int>(blocks_per_cu),
-                        std::memory_order_relaxed);
+extern "C" int zero_set_occupancy(uint32_t blocks_per_cu) {
+    t_occupancy = blocks_per_cu >= 8 ? 8 : static_cast<int>(blocks_per_cu);
     return ZERO_OK;
 }
 
@@ -210,9 +222,7 @@ extern "C" int zero_adam_step(void *w16, const void *g16, float *master, float *
     if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
     if (d_found_inf != nullptr && !aligned(d_found_inf, 4)) return ZERO_EINVAL;
     if (count == 0) return ZERO_OK;
-    s.loss_scale = loss_scale;
-    s.bc1 = bias_correction(beta1, step);
-    s.bc2 = bias_correction(beta2, step);
+    call_scalars(&s, loss_scale, step);
     zs::DeviceProps dev;
     const int prc = device_props(&dev);
     if (prc != ZERO_OK) return prc;
@@ -324,9 +334,7 @@ extern "C" int zero_adam_step_g32(void *w16, const float *g32, float *master, fl
     if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
     if (d_found_inf != nullptr && !aligned(d_found_inf, 4)) return ZERO_EINVAL;
     if (count == 0) return ZERO_OK;
-    s.loss_scale = loss_scale;
-    s.bc1 = bias_correction(beta1, step);
-    s.bc2 = bias_correction(beta2, step);
+    call_scalars(&s, loss_scale, step);
     zs::DeviceProps dev;
     const int prc = device_props(&dev);
     if (prc != ZERO_OK) return prc;

@@ -10,8 +10,19 @@
 namespace zs {
 
 // Per-call scalars of the Adam step, all formed on the host.
+//
+// Three of the step's four FP32 divisions divide by per-call constants: the
+// loss scale S and the bias corrections bc1, bc2.  The kernels form those
+// quotients without a division, bit for bit the same:
+//  - S a power of two whose reciprocal is a normal FP32 number: g * (1/S) is
+//    the same real number as g / S, rounded once (inv_scale).
+//  - any other divisor d: (float)((double)a * RN64(1/d)), with a true
+//    division wherever that result is below 2^-125 in magnitude and a != 0
+//    (rcp_scale, rcp_bc1, rcp_bc2; the argument is beside the kernels).
 struct AdamScalars {
     float loss_scale;  // S: gradients are divided by it
+    float inv_scale;   // 1/S (exact) when scale_pow2, else unused
+    int scale_pow2;    // S = 2^k with -126 <= k <= 126
     float lr;
     float beta1;
     float beta2;
@@ -21,24 +32,38 @@ struct AdamScalars {
     float bc1;         // 1 - beta1^t, FP64 then rounded to FP32
     float bc2;         // 1 - beta2^t, FP64 then rounded to FP32
     float decay;       // 1 - lr * weight_decay (two FP32 operations)
+    double rcp_scale;  // RN64(1 / S)
+    double rcp_bc1;    // RN64(1 / bc1)
+    double rcp_bc2;    // RN64(1 / bc2)
 };
+
+// S = 2^k with a normal FP32 reciprocal: biased exponent 1..253, no
+// significand bits.
+inline bool scale_is_pow2(float S) {
+    uint32_t b;
+    __builtin_memcpy(&b, &S, 4);
+    const uint32_t e = (b >> 23) & 0xffu;
+    return (b & 0x807fffffu) == 0 && e >= 1 && e <= 253;
+}
 
 // Largest grid of the streaming kernels, in 256-thread blocks: one tile per
 // block measured fastest, and 2^23 blocks keep the grid below 2^32 threads.
 // Larger shards loop over tiles.
 constexpr uint64_t kMaxBlocks = 1ull << 23;
 
-// The grid cap in force: kMaxBlocks, or the lower cap set by
-// zero_set_grid_cap (tests use it to run the tile loops at small sizes).
+// The grid cap in force for the calling thread: kMaxBlocks, or the lower cap
+// that thread set with zero_tuning_set_grid_cap (tests use it to run the tile
+// loops at small sizes).
 uint64_t max_blocks();
 
-// What the launchers need to know of the current device, and the step's
-// occupancy setting in force.
+// What the launchers need to know of the current device, and the calling
+// thread's occupancy override.
 struct DeviceProps {
     int cus;              // compute units
     int lds_per_cu;       // LDS bytes of one compute unit
     int lds_per_block;    // largest LDS allocation of one workgroup
-    int step_per_cu;      // resident step blocks per CU: 0 = by shard size, else this cap
+    int occupancy;        // resident blocks per CU of the streaming kernels: 0 = each
+                          // kernel's own rule, 1-7 this cap, 8 no cap
 };
 
 // Enqueue the Adam step over `count` elements of five shard views.  The

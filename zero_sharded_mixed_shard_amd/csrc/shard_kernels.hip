@@ -105,49 +105,131 @@ __device__ __forceinline__ void grad4(const GT *__restrict__ g, uint64_t e, floa
     }
 }
 
-// ---- one element of the step ---------------------------------------------
+// ---- quotients by the per-call constants ------------------------------------
+//
+// The update divides by three numbers that are the same for every element:
+// S, bc1 = 1 - beta1^t and bc2 = 1 - beta2^t.  Each quotient a / d (FP32 a,
+// FP32 d > 0) is formed as q = (float)((double)a * r) with r = RN64(1/d):
+//  - r is within 2^-53 of 1/d and the FP64 product rounds once more, so the
+//    product is within 2^-52 (relative, plus a negligible cross term) of the
+//    real quotient a/d.
+//  - Write a = A*2^x and d = D*2^y with A, D odd integers below 2^24.  A
+//    rounding boundary of FP32 in the normal range (a midpoint between
+//    neighbours, or the overflow threshold) is M*2^z with M odd,
+//    2^24 <= M < 2^25.  a/d equals no such point: that needs A = M*D >= M
+//    > A.  So A*2^x - M*D*2^(y+z) is a non-zero multiple of
+//    2^min(x, y+z), and for a boundary next to a/d (M*2^z within a factor
+//    1 + 2^-23 of a/d) the distance |a/d - M*2^z| is at least 2^-49 * |a/d|.
+//    The product therefore never lies across a boundary from a/d, and one
+//    rounding to FP32 gives exactly the correctly rounded a / d --
+//    wherever a/d and the product lie in the normal range.
+//  - A rounded q of at least 2^-125 in magnitude puts both there; q = 0 from
+//    a = 0 is exact too.  Every other element (a != 0 with |q| < 2^-125,
+//    where subnormal spacing breaks the argument) is divided as written.
+//    One compare per quotient finds them; a lane divides only when one of
+//    its elements needs it.
+//  - S = 2^k with a normal reciprocal needs nothing of this: g * 2^-k is the
+//    same real number as g / S, rounded once.
+// tests/method/quotient_check.c compares the rule with the FP32 division on
+// the CPU, including numerators built to sit next to a boundary.
 
-template <int DT>
-__device__ __forceinline__ void adam_update(float graw, float &p, float &m, float &v, uint32_t &w,
-                                            const AdamScalars &s) {
-    const float g = graw / s.loss_scale;
-    const float pd = p * s.decay;
-    const float m_new = s.beta1 * m + s.omb1 * g;
-    const float v_new = s.beta2 * v + s.omb2 * (g * g);
-    const float m_hat = m_new / s.bc1;
-    const float v_hat = v_new / s.bc2;
-    const float denom = __builtin_sqrtf(v_hat) + s.eps;
-    const float p_new = pd - s.lr * m_hat / denom;
-    p = p_new;
-    m = m_new;
-    v = v_new;
-    w = narrow<DT>(p_new);
+__device__ __forceinline__ float quot_rcp(float a, double rcp) {
+    return static_cast<float>(static_cast<double>(a) * rcp);
 }
 
-template <int DT, typename GT>
+// The product differs from a / d only if this holds.
+__device__ __forceinline__ bool needs_division(float q, float a) {
+    return __builtin_fabsf(q) < 0x1p-125f && a != 0.0f;
+}
+
+// How the kernels undo the loss scale: multiply by the exact 1/S (S a power
+// of two), the FP64 reciprocal product, or either as the device control
+// block says (S is known only on the device).
+enum Unscale : int { kUnscaleMul = 0, kUnscaleRcp = 1, kUnscaleCtl = 2 };
+
+// ---- K elements of the step -------------------------------------------------
+
+template <int DT, int MODE, int K>
+__device__ __forceinline__ void adam_update(const float (&graw)[K], float (&p)[K], float (&m)[K],
+                                            float (&v)[K], uint32_t (&w)[K],
+                                            const AdamScalars &s) {
+    static_assert(MODE == kUnscaleMul || MODE == kUnscaleRcp, "resolved unscale mode");
+    float g[K];
+    if constexpr (MODE == kUnscaleMul) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) g[j] = graw[j] * s.inv_scale;
+    } else {
+        bool redo = false;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            g[j] = quot_rcp(graw[j], s.rcp_scale);
+            redo |= needs_division(g[j], graw[j]);
+        }
+        if (redo) {
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                if (needs_division(g[j], graw[j])) g[j] = graw[j] / s.loss_scale;
+        }
+    }
+    float mh[K], vh[K];
+    bool redo = false;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        m[j] = s.beta1 * m[j] + s.omb1 * g[j];
+        v[j] = s.beta2 * v[j] + s.omb2 * (g[j] * g[j]);
+        mh[j] = quot_rcp(m[j], s.rcp_bc1);
+        vh[j] = quot_rcp(v[j], s.rcp_bc2);
+        redo |= needs_division(mh[j], m[j]) | needs_division(vh[j], v[j]);
+    }
+    if (redo) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            if (needs_division(mh[j], m[j])) mh[j] = m[j] / s.bc1;
+            if (needs_division(vh[j], v[j])) vh[j] = v[j] / s.bc2;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const float pd = p[j] * s.decay;
+        const float denom = __builtin_sqrtf(vh[j]) + s.eps;
+        p[j] = pd - s.lr * mh[j] / denom;
+        w[j] = narrow<DT>(p[j]);
+    }
+}
+
+template <int DT, int MODE, typename GT>
 __device__ __forceinline__ void adam_one(uint16_t *__restrict__ w16, const GT *__restrict__ g,
                                          float *__restrict__ master, float *__restrict__ m,
                                          float *__restrict__ v, uint64_t i,
                                          const AdamScalars &s) {
-    float p = master[i], mm = m[i], vv = v[i];
-    uint32_t w;
-    adam_update<DT>(grad_at<GT, DT>(g, i), p, mm, vv, w, s);
-    master[i] = p;
-    m[i] = mm;
-    v[i] = vv;
-    w16[i] = static_cast<uint16_t>(w);
+    const float gr[1] = {grad_at<GT, DT>(g, i)};
+    float p[1] = {master[i]}, mm[1] = {m[i]}, vv[1] = {v[i]};
+    uint32_t w[1];
+    adam_update<DT, MODE, 1>(gr, p, mm, vv, w, s);
+    master[i] = p[0];
+    m[i] = mm[0];
+    v[i] = vv[0];
+    w16[i] = static_cast<uint16_t>(w[0]);
 }
 
-// With a device control block, the update runs only if the decision applied
-// it, and S and the bias corrections come from the block.
+// With a device control block, S, the bias corrections and their FP64
+// reciprocals come from the block (the decision wrote them); returns whether
+// the loss scale is a power of two with a normal reciprocal, whose exact
+// inverse it then stores.
 __device__ __forceinline__ bool take_device_scalars(const zero_device_ctl *__restrict__ ctl,
                                                     AdamScalars &s) {
-    if (ctl == nullptr) return true;
-    if (ctl->apply == 0) return false;
     s.loss_scale = ctl->loss_scale_used;
     s.bc1 = ctl->bc1;
     s.bc2 = ctl->bc2;
-    return true;
+    s.rcp_scale = ctl->rcp_loss_scale;
+    s.rcp_bc1 = ctl->rcp_bc1;
+    s.rcp_bc2 = ctl->rcp_bc2;
+    const uint32_t b = __builtin_bit_cast(uint32_t, s.loss_scale);
+    const uint32_t e = (b >> 23) & 0xffu;
+    const bool pow2 = (b & 0x807fffffu) == 0 && e >= 1 && e <= 253;
+    // S = 2^(e - 127), so 1/S = 2^(127 - e): biased exponent 254 - e (used only if pow2)
+    s.inv_scale = __builtin_bit_cast(float, (254u - e) << 23);
+    return pow2;
 }
 
 // ---- the step: aligned vector path ----------------------------------------
@@ -158,16 +240,13 @@ __device__ __forceinline__ bool take_device_scalars(const zero_device_ctl *__res
 // guarantees that master/m/v (and FP32 gradients) + head are 16-B aligned
 // and 16-bit arrays + head are 8-B aligned.
 
-template <int DT, typename GT, int U>
-__global__ __launch_bounds__(kThreads) void adam_step_vec(
-    uint16_t *__restrict__ w16, const GT *__restrict__ g, float *__restrict__ master,
-    float *__restrict__ m, float *__restrict__ v, uint64_t count, uint32_t head,
-    uint64_t n_tiles, AdamScalars s, const int32_t *__restrict__ flag,
-    const zero_device_ctl *__restrict__ ctl) {
-    if (flag != nullptr && *flag != 0) return;
-    if (!take_device_scalars(ctl, s)) return;
+template <int DT, typename GT, int U, int MODE>
+__device__ __forceinline__ void step_tiles(uint16_t *__restrict__ w16, const GT *__restrict__ g,
+                                           float *__restrict__ master, float *__restrict__ m,
+                                           float *__restrict__ v, uint64_t count, uint32_t head,
+                                           uint64_t n_tiles, const AdamScalars &s) {
     const uint32_t tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid < head) adam_one<DT>(w16, g, master, m, v, tid, s);
+    if (blockIdx.x == 0 && tid < head) adam_one<DT, MODE>(w16, g, master, m, v, tid, s);
 
     constexpr uint64_t kTile = static_cast<uint64_t>(U) * kGroup;
     for (uint64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
@@ -182,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void adam_step_vec(
             M[u] = load_nt(reinterpret_cast<const f32x4 *>(m + e));
             V[u] = load_nt(reinterpret_cast<const f32x4 *>(v + e));
         }
+        // one group at a time: its stores go out while the next group computes
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint64_t e = base + static_cast<uint64_t>(u) * kGroup;
@@ -189,8 +269,7 @@ __global__ __launch_bounds__(kThreads) void adam_step_vec(
             float mm[4] = {M[u].x, M[u].y, M[u].z, M[u].w};
             float vv[4] = {V[u].x, V[u].y, V[u].z, V[u].w};
             uint32_t w[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) adam_update<DT>(G[u][j], p[j], mm[j], vv[j], w[j], s);
+            adam_update<DT, MODE, 4>(G[u], p, mm, vv, w, s);
             store_nt(reinterpret_cast<f32x4 *>(master + e), f32x4{p[0], p[1], p[2], p[3]});
             store_nt(reinterpret_cast<f32x4 *>(m + e), f32x4{mm[0], mm[1], mm[2], mm[3]});
             store_nt(reinterpret_cast<f32x4 *>(v + e), f32x4{vv[0], vv[1], vv[2], vv[3]});
@@ -202,22 +281,55 @@ __global__ __launch_bounds__(kThreads) void adam_step_vec(
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     for (uint64_t i = head + n_tiles * kTile + static_cast<uint64_t>(blockIdx.x) * kThreads + tid;
          i < count; i += stride)
-        adam_one<DT>(w16, g, master, m, v, i, s);
+        adam_one<DT, MODE>(w16, g, master, m, v, i, s);
+}
+
+template <int DT, typename GT, int U, int MODE>
+__global__ __launch_bounds__(kThreads) void adam_step_vec(
+    uint16_t *__restrict__ w16, const GT *__restrict__ g, float *__restrict__ master,
+    float *__restrict__ m, float *__restrict__ v, uint64_t count, uint32_t head,
+    uint64_t n_tiles, AdamScalars s, const int32_t *__restrict__ flag,
+    const zero_device_ctl *__restrict__ ctl) {
+    if (flag != nullptr && *flag != 0) return;
+    if constexpr (MODE == kUnscaleCtl) {
+        if (ctl->apply == 0) return;
+        if (take_device_scalars(ctl, s))
+            step_tiles<DT, GT, U, kUnscaleMul>(w16, g, master, m, v, count, head, n_tiles, s);
+        else
+            step_tiles<DT, GT, U, kUnscaleRcp>(w16, g, master, m, v, count, head, n_tiles, s);
+    } else {
+        step_tiles<DT, GT, U, MODE>(w16, g, master, m, v, count, head, n_tiles, s);
+    }
 }
 
 // ---- the step: element-wise path for views of different alignment phase --
 
-template <int DT, typename GT>
+template <int DT, typename GT, int MODE>
+__device__ __forceinline__ void step_elems(uint16_t *__restrict__ w16, const GT *__restrict__ g,
+                                           float *__restrict__ master, float *__restrict__ m,
+                                           float *__restrict__ v, uint64_t count,
+                                           const AdamScalars &s) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < count;
+         i += stride)
+        adam_one<DT, MODE>(w16, g, master, m, v, i, s);
+}
+
+template <int DT, typename GT, int MODE>
 __global__ __launch_bounds__(kThreads) void adam_step_elem(
     uint16_t *__restrict__ w16, const GT *__restrict__ g, float *__restrict__ master,
     float *__restrict__ m, float *__restrict__ v, uint64_t count, AdamScalars s,
     const int32_t *__restrict__ flag, const zero_device_ctl *__restrict__ ctl) {
     if (flag != nullptr && *flag != 0) return;
-    if (!take_device_scalars(ctl, s)) return;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
-    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < count;
-         i += stride)
-        adam_one<DT>(w16, g, master, m, v, i, s);
+    if constexpr (MODE == kUnscaleCtl) {
+        if (ctl->apply == 0) return;
+        if (take_device_scalars(ctl, s))
+            step_elems<DT, GT, kUnscaleMul>(w16, g, master, m, v, count, s);
+        else
+            step_elems<DT, GT, kUnscaleRcp>(w16, g, master, m, v, count, s);
+    } else {
+        step_elems<DT, GT, MODE>(w16, g, master, m, v, count, s);
+    }
 }
 
 // ---- FP32 accumulation of 16-bit micro-batch gradients ----------------------
@@ -599,7 +711,8 @@ __global__ __launch_bounds__(kThreads) void sumsq_finalize(const double *__restr
 // One lane applies the host policy of zero_scaler_update to the control
 // block: overflow halves S; a clean step advances t, doubles S after a run of
 // growth_interval clean steps (unless 2S overflows), and records the S the
-// update unscales with and the bias corrections of t from the host's table.
+// update unscales with and the bias corrections of t from the host's table,
+// with the FP64 reciprocals of all three.
 __global__ void scaler_decide(zero_device_ctl *__restrict__ ctl, const float *__restrict__ bias,
                               uint64_t t_first, uint32_t len) {
     if (threadIdx.x != 0) return;
@@ -632,9 +745,14 @@ __global__ void scaler_decide(zero_device_ctl *__restrict__ ctl, const float *__
         sc.clean_steps = 0;
     }
     ctl->scaler = sc;
+    const float bc1 = bias[t - t_first], bc2 = bias[len + (t - t_first)];
     ctl->loss_scale_used = S;
-    ctl->bc1 = bias[t - t_first];
-    ctl->bc2 = bias[len + (t - t_first)];
+    ctl->bc1 = bc1;
+    ctl->bc2 = bc2;
+    // FP64 division is correctly rounded, as on the host
+    ctl->rcp_loss_scale = 1.0 / static_cast<double>(S);
+    ctl->rcp_bc1 = 1.0 / static_cast<double>(bc1);
+    ctl->rcp_bc2 = 1.0 / static_cast<double>(bc2);
     ctl->apply = 1;
     ctl->status = ZERO_OK;
 }
@@ -699,33 +817,20 @@ bool common_phase(const float *ref, const float *a, const float *b, const GT *g,
 // Resident step blocks per CU.  One tile per block keeps the hardware
 // dispatcher feeding CUs in tile order; how many tiles are in flight at once
 // is set by reserving LDS the kernel does not use (the code and the bytes
-// moved are the same).  Fewer tiles in flight stream faster from 2^26
-// elements on; the best number differs between the kernels, not with the
-// size.  Measured on MI355X, the same arrays in one process, means of two
-// processes (TB/s; uncapped / 3 per CU / 2 per CU):
-//   FP16 weights, 16-bit gradients: 67M 5.84 / 5.88 / 5.95; 137.7M 5.69 /
-//     5.64 / 5.90; 2^28 5.77 / 5.85 / 6.12; 2^30 5.87 / 5.88 / 6.05; 2^32
-//     5.80 / 5.88 / 6.08.  At 1e10, where the driver places 160 GB well,
-//     3 per CU is best (6.30-6.40 / 6.33-6.46 / 6.18-6.24; elsewhere
-//     6.01 / 6.01 / 6.09).
-//   BF16 weights, 16-bit gradients: 67M 5.71 / 6.08 / 5.64; 137.7M 5.57 /
-//     5.92 / 5.60; 2^28 5.65 / 6.24 / 5.72; 2^30 5.88 / 6.05 / 5.77; 2^32
-//     5.81 / 6.05 / 5.71; 1e10 5.98 / 6.06 / 5.75.
-//   FP32 gradients (either format): 137.7M 5.62 / 5.72-5.79 / 6.01-6.08;
-//     2^28 5.69 / 5.85 / 6.19; 2^30 5.51 / 5.69 / 6.07; 2^32 6.21 / 6.24 /
-//     6.29.
-// At 15.5M elements a cap gains nothing (FP16: 5.60-5.65 uncapped, 5.58
-// at 3, 5.16-5.39 at 2).
-constexpr uint64_t kStepCapFrom = 1ull << 26;
-constexpr uint64_t kStepF16ThreeFrom = 1ull << 33;
+// moved are the same).  Two per CU (8 waves) is the one rule, for every size,
+// format and gradient type.  Measured on MI355X with the arrays of one process
+// timed under every setting in turn, three rounds, three fresh processes per
+// size (median TB/s at 2 / 3 / 4 / uncapped blocks per CU):
+//   FP16: 15.5M 6.11 / 5.80 / 5.79 / 5.81; 2^26 6.29 / 6.02 / 5.95 / 5.80;
+//     137.7M (view phase 5) 6.00 / 5.70 / 5.69 / 5.64; 2^32 6.29 / 5.78 /
+//     5.72 / 5.58; 1e10 6.18 / 5.98 / 6.02 / 5.99 (one process placed the
+//     160 GB well: 6.45 / 6.54 / 6.49 / 6.47).
+//   BF16: 2^28 6.27 / 5.90 / 5.81 / 5.66; 937.5M 6.26 / 5.81 / 5.74 / 5.53;
+//     1.5e9 6.03 / 5.65 / 5.63 / 5.44.
+//   FP32 gradients (30 B per element): 2^30 5.98 / 5.58 / 5.59 / 5.47;
+//     2^32 6.44 / 6.45 / 6.46 / 6.43.
+constexpr int kStepPerCU = 2;
 
-template <int DT, typename GT>
-int step_blocks_per_cu(uint64_t count) {
-    if (count < kStepCapFrom) return 8;
-    if constexpr (sizeof(GT) == 4) return 2;  // FP32 gradients
-    if constexpr (DT == 1) return 3;          // BF16 weights
-    return count < kStepF16ThreeFrom ? 2 : 3;
-}
 // The accumulate (three streams, the same tiles) gains more from fewer blocks:
 // 2 per CU run 2^28 elements at 6.35-6.44 TB/s against 6.07-6.17 uncapped,
 // 2^30 at 6.37-6.40 against 5.84-5.91 and 2^32 at 6.33-6.39 against
@@ -748,17 +853,23 @@ inline size_t cap_lds_bytes(int per_cu, const DeviceProps &dev) {
     return bytes <= static_cast<size_t>(dev.lds_per_block) ? bytes : 0;
 }
 
-template <int DT, typename GT>
-size_t step_lds_bytes(uint64_t count, const DeviceProps &dev) {
-    const int per_cu = dev.step_per_cu != 0 ? dev.step_per_cu : step_blocks_per_cu<DT, GT>(count);
-    return cap_lds_bytes(per_cu, dev);
+// The calling thread's override of resident blocks per CU, if any, else the
+// kernel's own rule.
+inline int per_cu_or(int rule, const DeviceProps &dev) {
+    return dev.occupancy != 0 ? dev.occupancy : rule;
+}
+
+inline size_t step_lds_bytes(const DeviceProps &dev) {
+    return cap_lds_bytes(per_cu_or(kStepPerCU, dev), dev);
 }
 
 inline size_t accumulate_lds_bytes(uint64_t count, bool first, bool check,
                                    const DeviceProps &dev) {
-    if (count < kAccCapFrom) return 0;
-    return cap_lds_bytes(first ? kAccFirstCapPerCU : check ? kAccCheckCapPerCU : kAccCapPerCU,
-                         dev);
+    const int rule = count < kAccCapFrom ? 8
+                     : first             ? kAccFirstCapPerCU
+                     : check             ? kAccCheckCapPerCU
+                                         : kAccCapPerCU;
+    return cap_lds_bytes(per_cu_or(rule, dev), dev);
 }
 
 inline uint32_t grid_for(uint64_t need) {
@@ -767,15 +878,14 @@ inline uint32_t grid_for(uint64_t need) {
     return static_cast<uint32_t>(need < cap ? need : cap);
 }
 
-template <int DT, typename GT>
-hipError_t adam_dispatch(uint16_t *w16, const GT *g, float *master, float *m, float *v,
-                         uint64_t count, const AdamScalars &s, const int32_t *flag,
-                         const zero_device_ctl *ctl, const DeviceProps &dev,
-                         hipStream_t stream) {
+template <int DT, typename GT, int MODE>
+hipError_t adam_launch(uint16_t *w16, const GT *g, float *master, float *m, float *v,
+                       uint64_t count, const AdamScalars &s, const int32_t *flag,
+                       const zero_device_ctl *ctl, const DeviceProps &dev, hipStream_t stream) {
     uint32_t head = 0;
     if (!common_phase<GT>(master, m, v, g, w16, &head)) {
-        adam_step_elem<DT, GT><<<grid_for((count + kThreads - 1) / kThreads), kThreads, 0,
-                                 stream>>>(w16, g, master, m, v, count, s, flag, ctl);
+        adam_step_elem<DT, GT, MODE><<<grid_for((count + kThreads - 1) / kThreads), kThreads, 0,
+                                       stream>>>(w16, g, master, m, v, count, s, flag, ctl);
         return hipGetLastError();
     }
     if (head > count) head = static_cast<uint32_t>(count);
@@ -783,10 +893,26 @@ hipError_t adam_dispatch(uint16_t *w16, const GT *g, float *master, float *m, fl
     const uint64_t n_tiles = (count - head) / kTile;
     const uint64_t rest = count - head - n_tiles * kTile;
     const uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
-    adam_step_vec<DT, GT, kAdamU><<<grid_for(need), kThreads, step_lds_bytes<DT, GT>(count, dev),
-                                    stream>>>(w16, g, master, m, v, count, head, n_tiles, s,
-                                              flag, ctl);
+    adam_step_vec<DT, GT, kAdamU, MODE><<<grid_for(need), kThreads,
+                                          step_lds_bytes(dev), stream>>>(
+        w16, g, master, m, v, count, head, n_tiles, s, flag, ctl);
     return hipGetLastError();
+}
+
+// The unscale mode: from the control block when there is one, else by S.
+template <int DT, typename GT>
+hipError_t adam_dispatch(uint16_t *w16, const GT *g, float *master, float *m, float *v,
+                         uint64_t count, const AdamScalars &s, const int32_t *flag,
+                         const zero_device_ctl *ctl, const DeviceProps &dev,
+                         hipStream_t stream) {
+    if (ctl != nullptr)
+        return adam_launch<DT, GT, kUnscaleCtl>(w16, g, master, m, v, count, s, flag, ctl, dev,
+                                                stream);
+    if (s.scale_pow2)
+        return adam_launch<DT, GT, kUnscaleMul>(w16, g, master, m, v, count, s, flag, ctl, dev,
+                                                stream);
+    return adam_launch<DT, GT, kUnscaleRcp>(w16, g, master, m, v, count, s, flag, ctl, dev,
+                                            stream);
 }
 
 template <int DT, bool FIRST, bool CHECK>
@@ -832,8 +958,8 @@ CheckGrid check_grid(const GT *g, uint64_t count, bool sumsq, const DeviceProps 
     if (need == 0) need = 1;
     const uint64_t cap = sumsq ? kSumsqBlocks : max_blocks();  // the partials' grid stays fixed
     c.blocks = static_cast<uint32_t>(need < cap ? need : cap);
-    c.lds = !sumsq && count * sizeof(GT) >= kCheckCapFromBytes ? cap_lds_bytes(kCheckCapPerCU, dev)
-                                                               : 0;
+    const int rule = count * sizeof(GT) >= kCheckCapFromBytes ? kCheckCapPerCU : 8;
+    c.lds = sumsq ? 0 : cap_lds_bytes(per_cu_or(rule, dev), dev);
     return c;
 }
 
