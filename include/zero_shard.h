@@ -137,6 +137,26 @@ int zero_overflow_check(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n
                         double *d_partials, void *stream);
 
 /*
+ * zero_overflow_check_noalloc -- zero_overflow_check for callers that cannot
+ * allocate device memory or pass a workspace: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, outputs and errors, without d_partials: the partial sums of the
+ * sum of squares live in a fixed array of ZERO_SUMSQ_PARTIALS doubles (32 KiB)
+ * that the library holds on each device it runs on until the process ends.
+ * The call allocates nothing.  Every call on a device shares that device's
+ * array, so calls that overlap in time on one device (different streams, or
+ * threads racing on one stream) corrupt each other's sums; calls enqueued one
+ * after another on a stream are safe (each writes the partials it reads).
+ * Without d_sumsq the array is not used.
+ *   Errors: as zero_overflow_check, and ZERO_EINVAL if the sum of squares
+ *   would need more partial sums than the array holds (never for a shard the
+ *   layout accepts: that grid has at most 1792 blocks).
+ */
+int zero_overflow_check_noalloc(const void *g16, zero_dtype dt, uint64_t psi, uint32_t n,
+                                uint32_t rank, float loss_scale, int32_t *d_found_inf,
+                                float *d_sumsq, void *stream);
+
+/*
  * zero_adam_step -- one Adam (weight_decay == 0) or AdamW step over this
  * rank's shard, elementwise, each operation one FP32 rounding to nearest
  * even, no contraction:

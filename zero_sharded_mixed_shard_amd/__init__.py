@@ -81,6 +81,7 @@ from ._binding import (  # noqa: F401
     zero_grad_accumulate_check_dev,
     zero_overflow_check,
     zero_overflow_check_dev,
+    zero_overflow_check_noalloc,
     zero_overflow_check_g32,
     zero_overflow_check_g32_dev,
     zero_peak_memory,
@@ -108,6 +109,7 @@ __all__ = [
     "device_ctl_read",
     "zero_bias_corrections",
     "zero_overflow_check_dev",
+    "zero_overflow_check_noalloc",
     "zero_scaler_update_dev",
     "zero_adam_step_dev",
     "zero_grad_accumulate",

@@ -55,6 +55,8 @@ lib.zero_shard_layout.argtypes = [_u64, _u32, _u32, ctypes.POINTER(_Layout)]
 lib.zero_shard_layout.restype = _i32
 lib.zero_overflow_check.argtypes = [_vp, _i32, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _vp]
 lib.zero_overflow_check.restype = _i32
+lib.zero_overflow_check_noalloc.argtypes = [_vp, _i32, _u64, _u32, _u32, _f32, _vp, _vp, _vp]
+lib.zero_overflow_check_noalloc.restype = _i32
 lib.zero_adam_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32, _u32, _f32, _f32, _f32,
                                _f32, _f32, _u64, _f32, _vp, _vp]
 lib.zero_adam_step.restype = _i32
@@ -231,6 +233,24 @@ def zero_overflow_check(g16: torch.Tensor, psi: int, n: int, rank: int, loss_sca
                                      p_p, _stream_handle(stream, dev))
     if rc != 0:
         raise ZeroError(rc, "zero_overflow_check")
+
+
+def zero_overflow_check_noalloc(g16: torch.Tensor, psi: int, n: int, rank: int,
+                                loss_scale: float, found_inf: torch.Tensor,
+                                sumsq: torch.Tensor | None = None, stream=None) -> None:
+    """zero_overflow_check with the library's fixed per-device partials (no workspace)."""
+    lay = zero_shard_layout(psi, n, rank)
+    dev = g16.device
+    if dev.type != "cuda":
+        raise ValueError("g16 must be a device tensor")
+    p_g = _view(g16, "g16", _DTYPES, lay.count, dev)
+    p_f = _view(found_inf, "found_inf", (torch.int32,), 1, dev)
+    p_s = _view(sumsq, "sumsq", (torch.float32,), 1, dev) if sumsq is not None else None
+    with torch.cuda.device(dev):
+        rc = lib.zero_overflow_check_noalloc(p_g, _DTYPES[g16.dtype], psi, n, rank, loss_scale,
+                                             p_f, p_s, _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_overflow_check_noalloc")
 
 
 def zero_adam_step(w16: torch.Tensor, g16: torch.Tensor, master: torch.Tensor, m: torch.Tensor,

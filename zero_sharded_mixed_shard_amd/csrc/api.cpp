@@ -208,6 +208,28 @@ extern "C" int zero_overflow_check(const void *g16, zero_dtype dt, uint64_t psi,
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check launch");
 }
 
+extern "C" int zero_overflow_check_noalloc(const void *g16, zero_dtype dt, uint64_t psi,
+                                           uint32_t n, uint32_t rank, float loss_scale,
+                                           int32_t *d_found_inf, float *d_sumsq, void *stream) {
+    uint64_t count = 0;
+    int rc = check_args(g16, dt, psi, n, rank, &count);
+    if (rc != ZERO_OK) return rc;
+    if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
+    if (d_found_inf == nullptr || !aligned(d_found_inf, 4)) return ZERO_EINVAL;
+    if (d_sumsq != nullptr && !aligned(d_sumsq, 4)) return ZERO_EINVAL;
+    if (!check_outputs_ok(g16, 2 * count, d_found_inf, 4, d_sumsq, nullptr)) return ZERO_EINVAL;
+    if (d_sumsq != nullptr && zs::sumsq_partials_needed(static_cast<int>(dt), g16, count) >
+                                  static_cast<uint64_t>(zs::scratch_partials_capacity()))
+        return ZERO_EINVAL;
+    zs::DeviceProps dev;
+    rc = device_props(&dev);
+    if (rc != ZERO_OK) return rc;
+    const hipError_t e = zs::launch_overflow_check_noalloc(
+        static_cast<int>(dt), static_cast<const uint16_t *>(g16), count, loss_scale, d_found_inf,
+        d_sumsq, dev, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_overflow_check_noalloc launch");
+}
+
 extern "C" int zero_adam_step(void *w16, const void *g16, float *master, float *m, float *v,
                               zero_dtype dt, uint64_t psi, uint32_t n, uint32_t rank, float lr,
                               float beta1, float beta2, float eps, float weight_decay,

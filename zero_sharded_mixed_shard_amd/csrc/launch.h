@@ -82,6 +82,18 @@ hipError_t launch_overflow_check(int dtype, const uint16_t *g16, uint64_t count,
                                  const float *loss_scale_dev, int32_t *flag, float *sumsq,
                                  double *partials, const DeviceProps &dev, hipStream_t stream);
 
+// launch_overflow_check with the partial sums in the library's fixed device
+// array (ZERO_SUMSQ_PARTIALS doubles per device, shared by every such call on
+// the device) instead of caller memory; no allocation.  The sum-of-squares
+// grid never exceeds the array (scratch_partials_capacity() partials).
+hipError_t launch_overflow_check_noalloc(int dtype, const uint16_t *g16, uint64_t count,
+                                         float loss_scale, int32_t *flag, float *sumsq,
+                                         const DeviceProps &dev, hipStream_t stream);
+int scratch_partials_capacity();
+// Partial sums the sum-of-squares check of `count` gradients at `g` writes
+// (dtype 0/1: 16-bit, 2: FP32).
+uint64_t sumsq_partials_needed(int dtype, const void *g, uint64_t count);
+
 // The step with FP32 gradients (dtype: the working weights' format); flag and
 // ctl as for launch_adam_step.
 hipError_t launch_adam_step_g32(int dtype, uint16_t *w16, const float *g32, float *master,

@@ -25,12 +25,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "launch.h"
 #include "zero_shard.h"
 
 #pragma clang fp contract(off)
+
+// Partial sums of the sum-of-squares check for callers that cannot allocate
+// (zero_overflow_check_noalloc): 4096 doubles (32 KiB), one copy per device,
+// held until the process ends and shared by every such call on the device.
+// Host code never passes this name to a kernel: it stands for the host-side
+// shadow.  The device address comes from hipGetSymbolAddress (below).
+static __device__ __align__(256) double scratch[ZERO_SUMSQ_PARTIALS];
 
 namespace zs {
 namespace {
@@ -775,6 +783,7 @@ constexpr uint64_t kCheckCapFromBytes = 128ull << 20;
 constexpr int kCheckCapPerCU = 3;
 constexpr uint32_t kSumsqBlocks = 1792;
 static_assert(kSumsqBlocks <= kSumsqPartials, "one partial per block");
+static_assert(kSumsqPartials == ZERO_SUMSQ_PARTIALS, "the caller's and the fixed partials agree");
 
 inline uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
@@ -1054,6 +1063,54 @@ hipError_t launch_scaler_decide(zero_device_ctl *ctl, const float *bias, uint64_
                                 uint32_t len, hipStream_t stream) {
     scaler_decide<<<1, 64, 0, stream>>>(ctl, bias, t_first, len);
     return hipGetLastError();
+}
+
+namespace {
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (each device holds its own copy at its own address).
+constexpr int kScratchDevices = 64;
+std::atomic<double *> g_scratch[kScratchDevices];
+
+hipError_t scratch_on_current_device(double **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    double *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void *addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (addr == nullptr) return hipErrorInvalidSymbol;
+        p = static_cast<double *>(addr);
+        g_scratch[dev].store(p, std::memory_order_release);  // same value from any thread
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace
+
+int scratch_partials_capacity() { return ZERO_SUMSQ_PARTIALS; }
+
+uint64_t sumsq_partials_needed(int dtype, const void *g, uint64_t count) {
+    const DeviceProps none{1, 0, 0, 0};  // the sum-of-squares grid ignores the device
+    if (dtype == 2)
+        return check_grid<float, 0>(static_cast<const float *>(g), count, true, none).blocks;
+    return check_grid<uint16_t, 0>(static_cast<const uint16_t *>(g), count, true, none).blocks;
+}
+
+hipError_t launch_overflow_check_noalloc(int dtype, const uint16_t *g16, uint64_t count,
+                                         float loss_scale, int32_t *flag, float *sumsq,
+                                         const DeviceProps &dev, hipStream_t stream) {
+    double *partials = nullptr;
+    if (sumsq != nullptr) {
+        const hipError_t e = scratch_on_current_device(&partials);
+        if (e != hipSuccess) return e;
+    }
+    return launch_overflow_check(dtype, g16, count, loss_scale, nullptr, flag, sumsq, partials,
+                                 dev, stream);
 }
 
 }  // namespace zs
