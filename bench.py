@@ -14,8 +14,12 @@ m = v = 0 at the start, AdamW lr 1e-4, wd 0.1.
 Prints one JSON line: params/s over the timed steps, the step kernel's HBM
 roofline (algorithmic 28 B/param over its HIP-event-timed average duration,
 against the 8 TB/s peak), the HBM traffic measured by rocprofv3 counters when
-the profiled kernel's machine code matches the built one, and the CPU oracle
-timed on a bounded sample of the same inputs.
+the profiled kernel's machine code matches the built one, the parity of the
+run's own steps against the oracle (windows of the benchmarked buffers
+replayed on the host, and the flag of every step against the oracle's over the
+whole gradient buffer), the same measurements on the other roofline
+configurations (the 7.5B rank, the ragged 8.81B rank, 1.5B) under
+'workloads', and the CPU oracle timed on a bounded sample of the same inputs.
 
     python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload 4]
 """
@@ -112,6 +116,160 @@ def make_workload(cfg: int, dev):
     return w, rank, lay, bufs
 
 
+PARITY_WINDOW = 8192
+PARITY_RANDOM = 8
+
+
+def parity_windows(count: int, seed: int) -> list:
+    """Element ranges whose state the oracle replays: head, tail, past 2^32, and seeded
+    random windows of PARITY_WINDOW elements."""
+    import numpy as np
+
+    w = min(PARITY_WINDOW, count)
+    starts = {0, count - w}
+    if count > (1 << 32) + w:
+        starts.add(1 << 32)
+    rng = np.random.default_rng(seed)
+    for _ in range(PARITY_RANDOM):
+        starts.add(int(rng.integers(0, count - w + 1)))
+    return sorted((a, a + w) for a in starts)
+
+
+def snapshot(bufs, wins) -> list:
+    """Host copies of every buffer over each window (16-bit arrays as bit patterns)."""
+    import synth
+
+    out = []
+    for a, b in wins:
+        out.append({k: (synth.to_numpy_u16(bufs[k][a:b]) if k in ("g16", "w16")
+                        else bufs[k][a:b].cpu().numpy().copy())
+                    for k in ("g16", "master", "m", "v", "w16")})
+    return out
+
+
+def full_flag_oracle(g16, dtype: str, loss_scale: float, chunk: int = 1 << 28) -> int:
+    """The oracle's overflow flag over a whole device gradient buffer, in host chunks."""
+    import oracle
+    import synth
+
+    n = g16.numel()
+    for a in range(0, n, chunk):
+        if oracle.overflow_flag_mt(synth.to_numpy_u16(g16[a:min(n, a + chunk)]), dtype,
+                                   loss_scale):
+            return 1
+    return 0
+
+
+def replay_parity(w, start, final, applied, flags) -> dict:
+    """Replay the run's applied steps (t, S) through the oracle on the start windows and
+    compare with the device's final windows: max ulp and non-bitwise counts per array,
+    and the device's flag of every step against the oracle's over the whole buffer."""
+    import numpy as np
+
+    import oracle
+
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    stats = {k: [0, 0] for k in ("master", "m", "v", "w16")}
+    elems = 0
+    for s0, s1 in zip(start, final):
+        ref = {k: s0[k].copy() for k in ("master", "m", "v", "w16")}
+        for t, S in applied:
+            oracle.adam_step(ref["w16"], s0["g16"], ref["master"], ref["m"], ref["v"], w.dtype,
+                             step=t, loss_scale=S, **hp)
+        elems += s0["g16"].size
+        for k in ("master", "m", "v"):
+            d = oracle.ulp_distance32(s1[k], ref[k])
+            stats[k][0] = max(stats[k][0], int(d.max()))
+            stats[k][1] += int(np.count_nonzero(s1[k].view(np.uint32) != ref[k].view(np.uint32)))
+        d = oracle.ulp_distance16(s1["w16"], ref["w16"], w.dtype)
+        stats["w16"][0] = max(stats["w16"][0], int(d.max()))
+        stats["w16"][1] += int(np.count_nonzero(s1["w16"] != ref["w16"]))
+    flags_equal = all(got == want for got, want in flags)
+    return {"windows": len(start), "elements": elems, "steps_replayed": len(applied),
+            "max_ulp": {k: v[0] for k, v in stats.items()},
+            "non_bitwise": {k: v[1] for k, v in stats.items()},
+            "flag_steps": len(flags), "flags_equal": flags_equal,
+            "bar": "master/m/v <= 2 ulp, w16 <= 1 ulp, flag bit-exact",
+            "ok": flags_equal and all(stats[k][0] <= 2 for k in ("master", "m", "v"))
+            and stats["w16"][0] <= 1}
+
+
+def run_steps(w, rank, lay, b, dev, warmup: int, steps: int, stream, seed: int) -> dict:
+    """The host-controlled sequence (check, 4-byte read-back, decision, step) on one
+    workload's buffers: HIP-event times of the check and the step over the timed steps,
+    and the parity of every step against the oracle."""
+    import torch
+
+    import zero_sharded_mixed_shard_amd as zs
+
+    psi, n, cnt = w.psi, w.n, lay.count
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    scaler = zs.Scaler(w.loss_scale, step=w.warm_steps)
+    wins = parity_windows(cnt, seed)
+    start = snapshot(b, wins)
+    applied, found_flags, ev = [], [], []
+    for i in range(warmup + steps):
+        timed = i >= warmup
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        S = scaler.loss_scale
+        if timed:
+            e[0].record(stream)
+        zs.zero_overflow_check(b["g16"], psi, n, rank, S, flag, stream=stream)
+        if timed:
+            e[1].record(stream)
+        found = int(flag.item())
+        found_flags.append((found, S))
+        if zs.zero_scaler_update(scaler, found):
+            if timed:
+                e[2].record(stream)
+            zs.zero_adam_step(b["w16"], b["g16"], b["master"], b["m"], b["v"], psi, n, rank,
+                              step=scaler.step, loss_scale=S, found_inf=flag, stream=stream, **hp)
+            applied.append((scaler.step, S))
+            if timed:
+                e[3].record(stream)
+                ev.append(e)
+    torch.cuda.synchronize()
+    final = snapshot(b, wins)
+    want = {S: full_flag_oracle(b["g16"], w.dtype, S) for S in {S for _, S in found_flags}}
+    parity = replay_parity(w, start, final, applied, [(f, want[S]) for f, S in found_flags])
+    step_ms = [x[2].elapsed_time(x[3]) for x in ev]
+    check_ms = [x[0].elapsed_time(x[1]) for x in ev]
+    return {"step_ms": step_ms, "check_ms": check_ms, "parity": parity}
+
+
+def measure_workloads(dev, ids, warmup: int, steps: int) -> dict:
+    """The other roofline configurations, one after another: the check and the step timed
+    with HIP events (median and min) and the parity of the run's steps."""
+    import statistics
+
+    import torch
+
+    out = {}
+    for cfg in ids:
+        w, rank, lay, b = make_workload(cfg, dev)
+        stream = torch.cuda.current_stream(dev)
+        r = run_steps(w, rank, lay, b, dev, warmup, steps, stream, seed=cfg)
+        cnt = lay.count
+        med, mn = statistics.median(r["step_ms"]), min(r["step_ms"])
+        cmed = statistics.median(r["check_ms"])
+        gbps = STEP_BYTES_PER_PARAM * cnt / (med * 1e-3) / 1e9
+        out[w.name] = {
+            "shard_params": cnt, "psi": w.psi, "zero_ranks": w.n, "rank": rank,
+            "grad_weight_dtype": w.dtype, "steps": steps, "warmup": warmup,
+            "adam_step_ms_median": med, "adam_step_ms_min": mn,
+            "adam_step_GBps": gbps, "frac": gbps / PEAK_HBM_GBPS,
+            "adam_step_params_per_s": cnt / (med * 1e-3),
+            "overflow_check_ms_median": cmed, "overflow_check_ms_min": min(r["check_ms"]),
+            "overflow_check_GBps": CHECK_BYTES_PER_PARAM * cnt / (cmed * 1e-3) / 1e9,
+            "parity": r["parity"]}
+        log(f"[bench] {w.name}: step {med:.4f} ms ({gbps / 1e3:.3f} TB/s), parity "
+            f"{'ok' if r['parity']['ok'] else 'FAILED'}")
+        del b
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -127,7 +285,8 @@ def cpu_baseline(bufs, w, budget_s: float, sample: int):
     """The oracle as it stands, on the host's cores, over a slice of the same inputs.
 
     A quarter of the budget times it on one thread, the rest on the host's CPU
-    share; the reported value is the latter."""
+    share (the threads this process may use: 16 on the MI355X machines, whatever
+    the machine's core count); the reported value is the latter."""
     import numpy as np
 
     import oracle
@@ -153,10 +312,18 @@ def cpu_baseline(bufs, w, budget_s: float, sample: int):
                 return n * steps / el, used, steps, el
 
     one, _, steps1, el1 = run(1, budget_s / 4)
-    rate, used, steps, el = run(oracle.host_threads(), budget_s * 3 / 4)
+    share = oracle.host_threads()
+    rate, used, steps, el = run(share, budget_s * 3 / 4)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = None
     return {"value": rate, "unit": "params/s", "cores": used, "kind": "oracle",
             "sample": f"first {n} params of the same shard inputs, {steps} Adam steps "
                       f"({el:.1f} s wall) on {used} host threads",
+            "threads_used": used, "nproc": os.cpu_count(), "affinity_cpus": affinity,
+            "threads_rule": "the host's CPU share: at most 16 threads (the worker budget per "
+                            "GPU on the MI355X machines), fewer if the affinity mask is smaller",
             "single_thread": {"value": one, "unit": "params/s",
                               "sample": f"same slice, {steps1} Adam steps ({el1:.1f} s wall)"},
             "GBps": rate * STEP_BYTES_PER_PARAM / 1e9, "cpu": cpu_model()}
@@ -423,14 +590,21 @@ def main():
                     help="workload id (4 = 1e10 params, N=1; the reported configuration)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle baseline")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 24,
+    ap.add_argument("--cpu-sample", type=int, default=1 << 27,
                     help="parameters in the CPU baseline's sample")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle baseline")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other roofline configurations (7.5B rank, ragged 8.81B "
+                         "rank, 1.5B) reported under 'workloads'")
+    ap.add_argument("--workload-steps", type=int, default=10,
+                    help="timed steps of each configuration under 'workloads'")
     ap.add_argument("--extras", action="store_true",
                     help="also time the accumulate / FP32-gradient / device-control / exchange "
-                         "kernels on 2^30-element shards (reported under 'extras')")
+                         "kernels on shards of --extras-elems elements (reported under 'extras')")
+    ap.add_argument("--extras-elems", type=int, default=1 << 30,
+                    help="shard size of the --extras measurements (elements)")
     ap.add_argument("--small", action="store_true",
                     help="also time whole steps of the launch-bound small workloads under host "
                          "control, device control and HIP-graph replay (reported under 'small')")
@@ -464,6 +638,7 @@ def main():
         scaler.step = w.warm_steps
     stream = torch.cuda.current_stream(dev)
     ev = []
+    applied, found_flags = [], []     # (t, S) of every applied update; (flag, S) of every check
 
     def one_step(timed: bool):
         layout = zs.zero_shard_layout(psi, n, rank)                          # shard range
@@ -475,12 +650,14 @@ def main():
         if timed:
             e[1].record(stream)
         found = int(flag.item())                                            # 4 bytes to host
+        found_flags.append((found, S))
         if zs.zero_scaler_update(scaler, found):                            # skip or apply
             if timed:
                 e[2].record(stream)
             zs.zero_adam_step(b["w16"], b["g16"], b["master"], b["m"], b["v"], psi, n, rank,
                               step=scaler.step, loss_scale=S, found_inf=flag, stream=stream,
                               **hp)
+            applied.append((scaler.step, S))
             if timed:
                 e[3].record(stream)
                 ev.append(e)
@@ -510,6 +687,8 @@ def main():
                 ev.append(e)
             return layout
 
+    wins = parity_windows(cnt, seed=args.workload)
+    start = snapshot(b, wins)
     for _ in range(args.warmup):
         one_step(False)
     torch.cuda.synchronize()
@@ -521,9 +700,12 @@ def main():
 
     if args.control == "device":
         c = zs.device_ctl_read(ctl)
-        if c.status != 0 or c.scaler.step != scaler.step + args.warmup + args.steps:
+        total = args.warmup + args.steps
+        if c.status != 0 or c.scaler.step != scaler.step + total:
             raise RuntimeError(f"device control skipped steps: status {c.status}, "
                                f"t {c.scaler.step}")
+        applied = [(t_first + i, w.loss_scale) for i in range(total)]
+        found_flags = [(c.found_inf, w.loss_scale)]
     step_ms = [x[2].elapsed_time(x[3]) for x in ev]
     check_ms = [x[0].elapsed_time(x[1]) for x in ev]
     if not step_ms:
@@ -533,11 +715,24 @@ def main():
     achieved = STEP_BYTES_PER_PARAM * cnt / (avg_step_ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name)
 
+    log("[bench] parity of the run's steps against the oracle ...")
+    final = snapshot(b, wins)
+    want = {S: full_flag_oracle(b["g16"], w.dtype, S) for S in {S for _, S in found_flags}}
+    parity = replay_parity(w, start, final, applied, [(f, want[S]) for f, S in found_flags])
+    log(f"[bench] parity {'ok' if parity['ok'] else 'FAILED'}: max ulp {parity['max_ulp']}")
+
     copy_gbps, stream_copy_gbps = (None, None) if args.no_copy else copy_bandwidth(dev)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
         cpu = cpu_baseline(b, w, args.cpu_seconds, args.cpu_sample)
+    del b
+    torch.cuda.empty_cache()
+    workloads = None
+    if not args.no_workloads:
+        log("[bench] other roofline configurations ...")
+        workloads = measure_workloads(dev, [c for c in (3, 5, 6) if c != args.workload],
+                                      warmup=2, steps=args.workload_steps)
     ckpt = None
     if args.ckpt:
         log("[bench] checkpoint files ...")
@@ -548,10 +743,8 @@ def main():
         small = measure_small(dev)
     extras = None
     if args.extras:
-        del b
-        torch.cuda.empty_cache()
         log("[bench] extras ...")
-        extras = measure_extras(dev)
+        extras = measure_extras(dev, n_elem=args.extras_elems)
 
     out = {
         "metric": METRIC,
@@ -577,12 +770,16 @@ def main():
         "kernels": {"adam_step_ms": avg_step_ms, "adam_step_ms_min": min(step_ms),
                     "adam_step_ms_median": statistics.median(step_ms),
                     "overflow_check_ms": avg_check_ms,
+                    "overflow_check_ms_median": statistics.median(check_ms),
                     "overflow_check_GBps": CHECK_BYTES_PER_PARAM * cnt / (avg_check_ms * 1e-3)
                     / 1e9,
                     "device_copy_GBps": copy_gbps,
                     "stream_copy_GBps": stream_copy_gbps},
+        "parity": parity,
         "cpu_baseline": cpu,
     }
+    if workloads is not None:
+        out["workloads"] = workloads
     if extras is not None:
         out["extras"] = extras
     if small is not None:

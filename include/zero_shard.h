@@ -528,10 +528,15 @@ int zero_reshard_plan(uint64_t psi, uint32_t n_old, uint32_t n_new, uint32_t ran
 /*
  * zero_ckpt_read_resharded -- rank rank_new's slice of a layout with n_new
  * ranks, read from the n_old shard files of the same flat buffer (paths_old[k]
- * is old rank k's file; only the files zero_reshard_plan names are opened),
- * into HOST arrays of the new rank's count elements.  Every file read is
- * checked against psi, n_old and its rank, and all must share one format.
- *   Errors: ZERO_EINVAL, ZERO_EIO, ZERO_ECORRUPT.
+ * is old rank k's file), into HOST arrays of the new rank's count elements.
+ * Every one of the n_old headers is checked against psi, n_old and its rank,
+ * and all must share one format and one scaler state (loss scale, growth
+ * interval, step, clean steps): a save interrupted between ranks leaves files
+ * of two steps, which are refused.  The payload hash of every file the new
+ * rank reads (those zero_reshard_plan names) is verified before its pieces
+ * are copied, so such files are read twice.
+ *   Errors: ZERO_EINVAL (NULL paths or arrays, bad layouts), ZERO_EIO,
+ *   ZERO_ECORRUPT (a bad header, a mismatch between files, a bad hash).
  */
 int zero_ckpt_read_resharded(const char *const *paths_old, uint32_t n_old, uint64_t psi,
                              uint32_t n_new, uint32_t rank_new, void *w16, float *master,

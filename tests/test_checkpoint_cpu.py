@@ -218,3 +218,52 @@ def test_resume_on_another_rank_count_is_exact(tmp_path):
                              "f16", step=t, loss_scale=1.0, **HP)
         for a, b in zip(full, sh):
             assert np.array_equal(a[sl].view(np.uint8), b.view(np.uint8))
+
+
+def test_resharded_read_refuses_mixed_steps_and_bad_payloads(tmp_path):
+    # a save that failed part-way leaves rank 1's file one step behind; every
+    # new rank must refuse the set (also new rank 0, which reads only old file 0)
+    psi, n_old, n_new = 40_009, 4, 2
+    flat = state(psi, 5)
+    paths = []
+    for k in range(n_old):
+        lay = oracle.layout(psi, n_old, k)
+        sl = slice(lay.offset, lay.offset + lay.count)
+        p = str(tmp_path / f"s{k}.zshard")
+        zs.zero_ckpt_write(p, psi, n_old, k, "f16", zs.Scaler(1024.0, step=10),
+                           *(np.ascontiguousarray(a[sl]) for a in flat))
+        paths.append(p)
+    for r in range(n_new):
+        zs.zero_ckpt_read_resharded(paths, psi, n_new, r)           # consistent: reads
+    lay1 = oracle.layout(psi, n_old, 1)
+    sl1 = slice(lay1.offset, lay1.offset + lay1.count)
+    stale = zs.Scaler(1024.0, step=9)
+    zs.zero_ckpt_write(paths[1], psi, n_old, 1, "f16", stale,
+                       *(np.ascontiguousarray(a[sl1]) for a in flat))
+    for r in range(n_new):
+        with pytest.raises(zs.ZeroError) as e:
+            zs.zero_ckpt_read_resharded(paths, psi, n_new, r)
+        assert e.value.code == -6, r
+    # other scaler fields and the format must agree too
+    for sc, dt in ((zs.Scaler(2048.0, step=10), "f16"), (zs.Scaler(1024.0, step=10), "bf16"),
+                   (zs.Scaler(1024.0, growth_interval=7, step=10), "f16")):
+        zs.zero_ckpt_write(paths[1], psi, n_old, 1, dt, sc,
+                           *(np.ascontiguousarray(a[sl1]) for a in flat))
+        with pytest.raises(zs.ZeroError) as e:
+            zs.zero_ckpt_read_resharded(paths, psi, n_new, 0)
+        assert e.value.code == -6, (sc.loss_scale, dt)
+    sc = zs.Scaler(1024.0, step=10)
+    zs.zero_ckpt_write(paths[1], psi, n_old, 1, "f16", sc,
+                       *(np.ascontiguousarray(a[sl1]) for a in flat))
+    zs.zero_ckpt_read_resharded(paths, psi, n_new, 0)               # whole again
+    # a flipped payload byte in a file the new rank reads is caught by its hash
+    raw = bytearray(open(paths[3], "rb").read())
+    raw[128 + 777] ^= 0x01
+    open(paths[3], "wb").write(bytes(raw))
+    zs.zero_ckpt_read_resharded(paths, psi, n_new, 0)               # reads old files 0-1 only
+    with pytest.raises(zs.ZeroError) as e:
+        zs.zero_ckpt_read_resharded(paths, psi, n_new, 1)           # reads old files 2-3
+    assert e.value.code == -6
+    # a missing old file is an argument error for every new rank
+    with pytest.raises((zs.ZeroError, TypeError, ValueError)):
+        zs.zero_ckpt_read_resharded(paths[:3] + [None], psi, n_new, 0)

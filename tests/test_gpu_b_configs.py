@@ -4,13 +4,16 @@ C1 (1M params, rank 3 of 8)    three ZeRO layouts, every element, all agree bitw
 C2 (GPT-2-small shapes, N=8)  every element of all 8 ranks for 10 steps, and the
                               concatenated shards equal the unsharded (N=1) update
 C3 (7.5e9, N=8, BF16)         rank 1's 937.5M-element shard, 20 warm steps, sampled windows
+                              against the oracle, and invariants at every element
 C4 (1e10, N=1, 160 GB)        the whole buffer, 5 steps, windows up to the last element
-                              (indices past 2^32), flag property at a far position
+                              (indices past 2^32) against the oracle, invariants at every
+                              element, flag property at a far position
 C5 (8,810,000,003, N=64)      rank 63's ragged shard (61 padding elements, start = 5 mod 8),
                               10 steps with inf/NaN injection on even steps: every flag,
                               every element, S halving and t bit-exact against the oracle
-C6 (1.5e9, N=1, BF16, 24 GB)  the whole buffer, 10 steps, sampled windows, and at every
-                              element w16 = RNE16(master) and v >= 0
+C6 (1.5e9, N=1, BF16, 24 GB)  the whole buffer, 10 steps, sampled windows, and invariants
+                              at every element
+(invariants: w16 = RNE16(master) bitwise, v >= 0, master, m and v finite)
 
 Inputs come from `synth` (seeded); expected values only from `oracle`.
 """
@@ -184,6 +187,21 @@ def windows_of(count, rng, n_random=24, width=8192, edge=4096):
     return sorted(w)
 
 
+def full_buffer_invariants(master, m, v, w16, what, chunk=1 << 28):
+    """At every element, chunk by chunk on the device: the working weights are the
+    master weights rounded to nearest even in their 16-bit format (torch's own
+    conversion), v >= 0 (a sum of squares), and master, m, v finite."""
+    n = master.numel()
+    for a in range(0, n, chunk):
+        b = min(n, a + chunk)
+        rne = master[a:b].to(w16.dtype).view(torch.int16)
+        assert torch.equal(rne, w16[a:b].view(torch.int16)), (what, "w16", a)
+        assert bool((v[a:b] >= 0).all()), (what, "v", a)
+        for k, t in (("master", master), ("m", m), ("v", v)):
+            assert bool(torch.isfinite(t[a:b]).all()), (what, k, a)
+    log(f"  {what}: w16 == RNE16(master), v >= 0, master/m/v finite at all {n} elements")
+
+
 def take(t, wins, conv):
     return [conv(t[a:b]) for a, b in wins]
 
@@ -234,6 +252,7 @@ def test_c3_bf16_warm_shard_windows():
     keys = ("master", "m", "v", "w16")
     log("  C3 windows", assert_close({k: cat(got, k) for k in keys},
                                      {k: cat(host, k) for k in keys}, "bf16", "C3"))
+    full_buffer_invariants(master, m, v, w16, "C3")
 
 
 def test_c4_ten_billion_unsharded_windows():
@@ -273,6 +292,7 @@ def test_c4_ten_billion_unsharded_windows():
     keys = ("master", "m", "v", "w16")
     log("  C4 windows", assert_close({k: cat(got, k) for k in keys},
                                      {k: cat(host, k) for k in keys}, "f16", "C4"))
+    full_buffer_invariants(master, m, v, w16, "C4")
     # flag property at full size: one NaN far past 2^32 is seen, and only while there
     far = psi - 12345
     keep = g16[far].clone()
@@ -320,14 +340,7 @@ def test_c6_one_and_a_half_billion_unsharded_windows():
     keys = ("master", "m", "v", "w16")
     log("  C6 windows", assert_close({k: cat(got, k) for k in keys},
                                      {k: cat(host, k) for k in keys}, "bf16", "C6"))
-    # at every element: the working weights are the master weights rounded to
-    # nearest even in BF16, and v >= 0 (squares only)
-    chunk = 1 << 28
-    for a in range(0, psi, chunk):
-        b = min(psi, a + chunk)
-        rne = master[a:b].to(torch.bfloat16).view(torch.int16)
-        assert torch.equal(rne, w16[a:b].view(torch.int16)), a
-        assert bool((v[a:b] >= 0).all()), a
+    full_buffer_invariants(master, m, v, w16, "C6")
 
 
 # ---------------------------------------------------------------------------

@@ -347,17 +347,37 @@ extern "C" int zero_ckpt_read_resharded(const char *const *paths_old, uint32_t n
     std::vector<zero_ckpt_piece> plan(np);
     rc = zero_reshard_plan(psi, n_old, n_new, rank_new, plan.data(), np, &np);
     if (rc != ZERO_OK) return rc;
-    int dtype = -1;
-    for (const zero_ckpt_piece &pc : plan) {
-        const char *path = paths_old[pc.src_rank];
-        if (path == nullptr) return ZERO_EINVAL;
+    // Every old file's header must name this layout and share one format and one
+    // scaler state: each rank renames its own file into place, so a save that
+    // failed part-way leaves files of two steps side by side, and new ranks that
+    // read disjoint subsets of them would otherwise resume from different steps.
+    zero_ckpt_info first{};
+    for (uint32_t k = 0; k < n_old; ++k) {
+        if (paths_old[k] == nullptr) return ZERO_EINVAL;
         zero_ckpt_info info;
-        rc = zero_ckpt_read_info(path, &info);
+        rc = zero_ckpt_read_info(paths_old[k], &info);
         if (rc != ZERO_OK) return rc;
-        if (info.psi != psi || info.n != n_old || info.rank != pc.src_rank) return ZERO_ECORRUPT;
-        if (dtype < 0) dtype = static_cast<int>(info.dtype);
-        if (static_cast<int>(info.dtype) != dtype) return ZERO_ECORRUPT;
-        rc = zero_ckpt_read(path, pc.src_first, pc.count,
+        if (info.psi != psi || info.n != n_old || info.rank != k) return ZERO_ECORRUPT;
+        if (k == 0) {
+            first = info;
+            continue;
+        }
+        const zero_scaler &a = first.scaler, &b = info.scaler;
+        if (info.dtype != first.dtype || a.step != b.step || a.clean_steps != b.clean_steps ||
+            a.growth_interval != b.growth_interval ||
+            std::memcmp(&a.loss_scale, &b.loss_scale, sizeof(float)) != 0)
+            return ZERO_ECORRUPT;
+    }
+    // the payload of every file this rank reads must match its hash
+    std::vector<char> verified(n_old, 0);
+    for (const zero_ckpt_piece &pc : plan) {
+        if (verified[pc.src_rank]) continue;
+        rc = zero_ckpt_verify(paths_old[pc.src_rank]);
+        if (rc != ZERO_OK) return rc;
+        verified[pc.src_rank] = 1;
+    }
+    for (const zero_ckpt_piece &pc : plan) {
+        rc = zero_ckpt_read(paths_old[pc.src_rank], pc.src_first, pc.count,
                             static_cast<uint16_t *>(w16) + pc.dst_first, master + pc.dst_first,
                             m + pc.dst_first, v + pc.dst_first);
         if (rc != ZERO_OK) return rc;
