@@ -125,7 +125,9 @@ int zero_shard_layout(uint64_t psi, uint32_t n, uint32_t rank, zero_layout *out)
  *                FP64 in a fixed order (so repeatable bit for bit) and
  *                rounded to FP32: the local term of a gradient norm.
  *   d_partials   device buffer of ZERO_SUMSQ_PARTIALS doubles, scratch for
- *                d_sumsq; required iff d_sumsq is given, otherwise ignored.
+ *                d_sumsq (the per-block partial sums of the two-pass sum: the
+ *                library allocates nothing, so they live in caller memory);
+ *                required iff d_sumsq is given, otherwise ignored.
  *   An empty rank (count == 0) still writes 0 to d_found_inf (and d_sumsq).
  *   Errors: ZERO_EDTYPE for a bad dt; ZERO_EINVAL for bad layout arguments,
  *   a NULL d_found_inf, a NULL g16 with count > 0, a NULL d_partials with a
