@@ -32,8 +32,9 @@ int zero_set_grid_cap(uint32_t blocks);
 /*
  * zero_set_occupancy -- resident blocks per compute unit of the streaming
  * kernels this thread launches afterwards: the step (both gradient formats,
- * host or device control), the accumulates and the flag-only overflow check.
- * 0 (the default) leaves each kernel its own rule; 1 to 7 caps every launch
+ * host or device control), the accumulates, the flag-only overflow check and
+ * the exchange stand-ins (reduce and gather).  0 (the default) leaves each
+ * kernel its own rule; 1 to 7 caps every launch
  * at that many; 8 or more removes the cap.  The cap is an LDS reservation the
  * kernels do not use, so results are bitwise the same under every setting.
  * Returns ZERO_OK.

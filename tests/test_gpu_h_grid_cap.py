@@ -233,3 +233,31 @@ def test_accumulate_and_check_occupancy_settings_change_nothing():
     del results
     torch.cuda.empty_cache()
     log("accumulate / check occupancy settings 0/1/2/4/8: bitwise equal flags and sums")
+
+
+def test_exchange_occupancy_settings_change_nothing():
+    # the reduce and the gather under every occupancy setting: the same bits
+    psi, n = 3 * (1 << 20) + 101, 4
+    reps = [synth.fill_normal_(torch.empty(psi, dtype=torch.float16, device=DEV), 1e-2,
+                               73_000 + k) for k in range(n)]
+    lay = zs.zero_shard_layout(psi, n, 1)
+    shards = [r[:zs.zero_shard_layout(psi, n, k).count].clone() for k, r in enumerate(reps)]
+    results = {}
+    try:
+        for occ in (0, 1, 2, 4, 8):
+            zs.zero_set_occupancy(occ)
+            out = torch.empty(lay.count, dtype=torch.float16, device=DEV)
+            full = torch.zeros(psi, dtype=torch.float16, device=DEV)
+            zs.zero_reduce_shard(out, reps, psi, n, 1)
+            zs.zero_gather_shards(full, shards, psi, n)
+            torch.cuda.synchronize()
+            results[occ] = (out, full)
+    finally:
+        torch.cuda.synchronize()
+        zs.zero_set_occupancy(0)
+    for occ in (1, 2, 4, 8):
+        for a, b in zip(results[occ], results[0]):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), occ
+    want = oracle.reduce_shard([u16(r) for r in reps], "f16", "f16", psi, n, 1)
+    assert np.array_equal(u16(results[0][0]), want)
+    log("exchange occupancy settings 0/1/2/4/8: bitwise equal, reduce equals the oracle")

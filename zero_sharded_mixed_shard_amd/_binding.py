@@ -149,7 +149,8 @@ def zero_set_grid_cap(blocks: int) -> None:
 
 def zero_set_occupancy(blocks_per_cu: int) -> None:
     """Resident blocks per CU of this thread's streaming-kernel launches (step, accumulates,
-    flag-only check): 0 leaves each kernel its own rule, 1-7 cap, 8+ removes the cap."""
+    flag-only check, reduce and gather): 0 leaves each kernel its own rule, 1-7 cap, 8+ removes
+    the cap."""
     if not 0 <= blocks_per_cu < 1 << 32:
         raise ValueError("blocks_per_cu must fit in 32 bits")
     lib.zero_set_occupancy(blocks_per_cu)

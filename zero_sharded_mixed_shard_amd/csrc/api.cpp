@@ -389,8 +389,11 @@ extern "C" int zero_reduce_shard(void *out, zero_dtype out_dt, const void *const
         if (!in_place && overlap(out, out_b * lay.count, set.p[k], in_b * lay.count))
             return ZERO_EINVAL;
     }
+    zs::DeviceProps dev;
+    const int prc = device_props(&dev);
+    if (prc != ZERO_OK) return prc;
     const hipError_t e = zs::launch_reduce_shard(out, static_cast<int>(out_dt), set,
-                                                 static_cast<int>(in_dt), n, lay.count,
+                                                 static_cast<int>(in_dt), n, lay.count, dev,
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_reduce_shard launch");
 }
@@ -420,8 +423,12 @@ extern "C" int zero_gather_shards(void *full, const void *const *shards, zero_dt
         set.vec[k] = 0;
         if (lk.count > max_count) max_count = lk.count;
     }
+    zs::DeviceProps dev;
+    const int prc = device_props(&dev);
+    if (prc != ZERO_OK) return prc;
     const hipError_t e = zs::launch_gather_shards(full, static_cast<int>(eb), set, n, lay.shard,
-                                                  max_count, static_cast<hipStream_t>(stream));
+                                                  max_count, dev,
+                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_gather_shards launch");
 }
 

@@ -59,18 +59,20 @@ __device__ __forceinline__ typename Fmt<F>::T from_f32(float f) {
         return f;
 }
 
-// kPerVec<F> consecutive elements from a 16-B aligned address.
+// One 16-B vector (kPerVec<F> consecutive elements) from a 16-B aligned address,
+// as raw bits; widen() turns it into FP32 values.
 template <int F>
-__device__ __forceinline__ void load_vec(const typename Fmt<F>::T *p, float out[kPerVec<F>]) {
+__device__ __forceinline__ u32x4 load_raw(const typename Fmt<F>::T *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+template <int F>
+__device__ __forceinline__ void widen(const u32x4 &x, float out[kPerVec<F>]) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
     if constexpr (F == 2) {
-        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-        out[0] = x.x;
-        out[1] = x.y;
-        out[2] = x.z;
-        out[3] = x.w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = __builtin_bit_cast(float, w[j]);
     } else {
-        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             out[2 * j] = to_f32<F>(static_cast<uint16_t>(w[j] & 0xffffu));
@@ -134,9 +136,12 @@ __global__ __launch_bounds__(kThreads) void reduce_shard_kernel(
             float s[K];
 #pragma unroll
             for (int j = 0; j < K; ++j) s[j] = 0.0f;
+            // one replica at a time, in rank order: keeping several replicas' loads
+            // in flight per lane (4 or 8, with or without an occupancy cap) measured
+            // no better over sizes on MI355X -- nine streams at once are what limit it
             for (uint32_t k = 0; k < n; ++k) {
                 float x[K];
-                load_vec<IN>(static_cast<const TI *>(in.p[k]) + e, x);
+                widen<IN>(load_raw<IN>(static_cast<const TI *>(in.p[k]) + e), x);
 #pragma unroll
                 for (int j = 0; j < K; ++j) s[j] = s[j] + x[j];
             }
@@ -206,9 +211,13 @@ inline uint32_t head_to_line(const void *p, uint32_t elem_bytes) {
     return static_cast<uint32_t>(((kLine - addr(p) % kLine) % kLine) / elem_bytes);
 }
 
+// Resident blocks per CU of the exchange kernels: no cap by default.
+constexpr int kReducePerCU = 8;
+constexpr int kGatherPerCU = 8;
+
 template <int IN, int OUT>
 hipError_t reduce_dispatch(void *out, const ReplicaSet &in, uint32_t n, uint64_t count,
-                           hipStream_t stream) {
+                           const DeviceProps &dev, hipStream_t stream) {
     constexpr uint32_t in_b = kBytes<IN>, out_b = kBytes<OUT>;
     constexpr uint32_t K = kPerVec<IN>;
     constexpr uint32_t out_align = K * out_b < kVecBytes ? K * out_b : kVecBytes;
@@ -220,7 +229,8 @@ hipError_t reduce_dispatch(void *out, const ReplicaSet &in, uint32_t n, uint64_t
         if ((addr(in.p[k]) + static_cast<uint64_t>(head) * in_b) % kVecBytes != 0) vec = false;
     const uint64_t n_vec = vec ? (count - head) / K : 0;
     if (n_vec == 0) head = 0;  // every element one at a time
-    reduce_shard_kernel<IN, OUT><<<blocks_for(n_vec > 0 ? n_vec : count), kThreads, 0, stream>>>(
+    reduce_shard_kernel<IN, OUT><<<blocks_for(n_vec > 0 ? n_vec : count), kThreads,
+                                   cap_lds_bytes(per_cu_or(kReducePerCU, dev), dev), stream>>>(
         static_cast<typename Fmt<OUT>::T *>(out), in, n, count, head, n_vec);
     return hipGetLastError();
 }
@@ -228,9 +238,10 @@ hipError_t reduce_dispatch(void *out, const ReplicaSet &in, uint32_t n, uint64_t
 }  // namespace
 
 hipError_t launch_reduce_shard(void *out, int out_fmt, const ReplicaSet &in, int in_fmt,
-                               uint32_t n, uint64_t count, hipStream_t stream) {
+                               uint32_t n, uint64_t count, const DeviceProps &dev,
+                               hipStream_t stream) {
 #define ZS_REDUCE(I, O) \
-    if (in_fmt == I && out_fmt == O) return reduce_dispatch<I, O>(out, in, n, count, stream);
+    if (in_fmt == I && out_fmt == O) return reduce_dispatch<I, O>(out, in, n, count, dev, stream);
     ZS_REDUCE(0, 0) ZS_REDUCE(0, 1) ZS_REDUCE(0, 2)
     ZS_REDUCE(1, 0) ZS_REDUCE(1, 1) ZS_REDUCE(1, 2)
     ZS_REDUCE(2, 0) ZS_REDUCE(2, 1) ZS_REDUCE(2, 2)
@@ -239,7 +250,8 @@ hipError_t launch_reduce_shard(void *out, int out_fmt, const ReplicaSet &in, int
 }
 
 hipError_t launch_gather_shards(void *full, int elem_bytes, GatherSet &set, uint32_t n,
-                                uint64_t shard, uint64_t max_count, hipStream_t stream) {
+                                uint64_t shard, uint64_t max_count, const DeviceProps &dev,
+                                hipStream_t stream) {
     const uint32_t eb = static_cast<uint32_t>(elem_bytes);
     for (uint32_t k = 0; k < n; ++k) {
         const uintptr_t s = addr(set.p[k]);
@@ -252,11 +264,13 @@ hipError_t launch_gather_shards(void *full, int elem_bytes, GatherSet &set, uint
     }
     const uint64_t per_vec = kVecBytes / eb;
     const dim3 grid(blocks_for((max_count + per_vec - 1) / per_vec), n);
+    const size_t lds = cap_lds_bytes(per_cu_or(kGatherPerCU, dev), dev);
     if (elem_bytes == 4)
-        gather_kernel<float><<<grid, kThreads, 0, stream>>>(static_cast<float *>(full), set, shard);
+        gather_kernel<float><<<grid, kThreads, lds, stream>>>(static_cast<float *>(full), set,
+                                                              shard);
     else
-        gather_kernel<uint16_t><<<grid, kThreads, 0, stream>>>(static_cast<uint16_t *>(full), set,
-                                                               shard);
+        gather_kernel<uint16_t><<<grid, kThreads, lds, stream>>>(static_cast<uint16_t *>(full), set,
+                                                                 shard);
     return hipGetLastError();
 }
 

@@ -66,6 +66,21 @@ struct DeviceProps {
                           // kernel's own rule, 1-7 this cap, 8 no cap
 };
 
+// Dynamic LDS to reserve, unused by the kernel, so that at most per_cu blocks
+// of 256 threads are resident on a CU (0: no reservation; 8 or more is the
+// kernels' own limit).  One more block than per_cu would not fit.
+inline size_t cap_lds_bytes(int per_cu, const DeviceProps &dev) {
+    if (per_cu <= 0 || per_cu >= 8 || dev.lds_per_cu <= 0) return 0;
+    const size_t bytes = static_cast<size_t>(dev.lds_per_cu) / (per_cu + 1) + 256;
+    return bytes <= static_cast<size_t>(dev.lds_per_block) ? bytes : 0;
+}
+
+// The calling thread's override of resident blocks per CU, if any, else the
+// kernel's own rule.
+inline int per_cu_or(int rule, const DeviceProps &dev) {
+    return dev.occupancy != 0 ? dev.occupancy : rule;
+}
+
 // Enqueue the Adam step over `count` elements of five shard views.  The
 // caller has validated every argument; count > 0.  flag (nullable): skip if
 // set.  ctl (nullable): skip unless ctl->apply, and take S, bc1, bc2 from it.
@@ -136,11 +151,13 @@ struct GatherSet {
 // out[i] = FP32 sum over k < n of in.p[k][i], rounded to out_fmt (0 FP16,
 // 1 BF16, 2 FP32), i < count; count > 0.
 hipError_t launch_reduce_shard(void *out, int out_fmt, const ReplicaSet &in, int in_fmt,
-                               uint32_t n, uint64_t count, hipStream_t stream);
+                               uint32_t n, uint64_t count, const DeviceProps &dev,
+                               hipStream_t stream);
 
 // full[k*shard + i] = set.p[k][i] for i < set.count[k], k < n.
 hipError_t launch_gather_shards(void *full, int elem_bytes, GatherSet &set, uint32_t n,
-                                uint64_t shard, uint64_t max_count, hipStream_t stream);
+                                uint64_t shard, uint64_t max_count, const DeviceProps &dev,
+                                hipStream_t stream);
 
 // Enqueue the one-lane skip-or-apply decision on a device control block.
 hipError_t launch_scaler_decide(zero_device_ctl *ctl, const float *bias, uint64_t t_first,

@@ -854,20 +854,6 @@ constexpr int kAccCapPerCU = 2;
 constexpr int kAccFirstCapPerCU = 4;
 constexpr int kAccCheckCapPerCU = 4;
 
-// LDS to reserve so that at most per_cu blocks are resident on a CU (0: none).
-inline size_t cap_lds_bytes(int per_cu, const DeviceProps &dev) {
-    if (per_cu <= 0 || per_cu >= 8 || dev.lds_per_cu <= 0) return 0;  // 8: the kernels' own limit
-    // one more block than per_cu would not fit
-    const size_t bytes = static_cast<size_t>(dev.lds_per_cu) / (per_cu + 1) + 256;
-    return bytes <= static_cast<size_t>(dev.lds_per_block) ? bytes : 0;
-}
-
-// The calling thread's override of resident blocks per CU, if any, else the
-// kernel's own rule.
-inline int per_cu_or(int rule, const DeviceProps &dev) {
-    return dev.occupancy != 0 ? dev.occupancy : rule;
-}
-
 inline size_t step_lds_bytes(const DeviceProps &dev) {
     return cap_lds_bytes(per_cu_or(kStepPerCU, dev), dev);
 }
