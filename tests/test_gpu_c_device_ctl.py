@@ -118,3 +118,23 @@ def test_device_nonpositive_scale_reads_as_overflow():
         zs.zero_scaler_update_dev(ctl, bias, 1)
         c = zs.device_ctl_read(ctl)
         assert c.found_inf == 1 and c.apply == 0 and c.status == -1 and c.scaler.step == 0
+
+
+def test_decision_writes_the_reciprocals_the_step_multiplies_by():
+    # after an applied decision the block holds S, bc1, bc2 and their FP64
+    # reciprocals, each the correctly rounded 1/x (Python's float division is
+    # IEEE round-to-nearest); S = 3 and 1000 take the reciprocal-product path
+    count = 4096
+    g = make_grads(count, 1, "f16", 900)[0].to(DEV)
+    for S, b1, b2, t0 in ((65536.0, 0.9, 0.999, 1), (3.0, 0.9, 0.999, 1),
+                          (1000.0, 0.95, 0.9999, 37), (2.0 ** -20, 0.5, 0.99, 5)):
+        ctl = zs.device_ctl_new(S, DEV, step=t0 - 1)
+        bias = zs.zero_bias_corrections(b1, b2, t0, 4).to(DEV)
+        zs.zero_overflow_check_dev(g, count, 1, 0, ctl)
+        zs.zero_scaler_update_dev(ctl, bias, t0)
+        c = zs.device_ctl_read(ctl)
+        host = zs.zero_bias_corrections(b1, b2, t0, 4).numpy()
+        assert c.apply == 1 and c.status == 0 and c.scaler.step == t0
+        assert (c.loss_scale_used, c.bc1, c.bc2) == (S, float(host[0]), float(host[4]))
+        for got, x in ((c.rcp_loss_scale, S), (c.rcp_bc1, c.bc1), (c.rcp_bc2, c.bc2)):
+            assert np.float64(got).view(np.uint64) == np.float64(1.0 / x).view(np.uint64), (S, x)

@@ -2,21 +2,24 @@
 //
 // The step is elementwise over five structure-of-arrays streams (gradients,
 // FP32 master / m / v, 16-bit working weights): 28 bytes of HBM traffic per
-// element with 16-bit gradients (30 with FP32 gradients) and ~80 VALU
+// element with 16-bit gradients (30 with FP32 gradients) and ~54 VALU
 // operations, far below the FP32 ridge point, so the kernels are built for
 // bandwidth: every lane moves one 16-B FP32 vector per array and one 8-B
 // 16-bit vector per group of 4 elements, a wave's accesses are contiguous
 // 1 KiB (FP32) or 512 B (16-bit) runs, and each lane keeps U groups in
-// flight.  No LDS: nothing is reused.  Every access of the streaming kernels
-// is non-temporal (the data is touched once), and the step launches one block
-// per tile (a grid-stride loop only past 2^23 tiles): both measured faster on
-// MI355X than a resident grid looping over tiles.
+// flight.  No LDS is read or written: nothing is reused (launches may reserve
+// LDS only to cap the resident blocks per CU).  Every access of the streaming
+// kernels is non-temporal (the data is touched once), and the step launches
+// one block per tile (a grid-stride loop only past 2^23 tiles): both measured
+// faster on MI355X than a resident grid looping over tiles.
 //
 // Numerics follow the update of "Training models too big for one GPU: ZeRO &
 // FSDP" ("Adam, and why it's expensive", "Mixed-precision training") with
 // one binary32 rounding per operation: contraction is off for this file,
 // FP32 division and square root stay correctly rounded (the HIP default),
-// denormals are kept, and the 16-bit conversions round to nearest even.
+// denormals are kept, and the 16-bit conversions round to nearest even.  The
+// quotients by per-call constants are formed without a division but with the
+// division's exact result (the argument is below, before adam_update).
 //
 // Gradient element types: uint16_t holds FP16 (DT = 0) or BF16 (DT = 1) bit
 // patterns; float holds FP32 gradients (accumulated across micro-batches,
