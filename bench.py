@@ -194,6 +194,15 @@ def replay_parity(w, start, final, applied, flags) -> dict:
             and stats["w16"][0] <= 1}
 
 
+def layouts_equal(psi: int, n: int) -> bool:
+    """Every rank's layout from the library equals the oracle's, field by field."""
+    import oracle
+    import zero_sharded_mixed_shard_amd as zs
+
+    return all(zs.zero_shard_layout(psi, n, r).__dict__ == oracle.layout(psi, n, r).__dict__
+               for r in range(n))
+
+
 def run_steps(w, rank, lay, b, dev, warmup: int, steps: int, stream, seed: int) -> dict:
     """The host-controlled sequence (check, 4-byte read-back, decision, step) on one
     workload's buffers: HIP-event times of the check and the step over the timed steps,
@@ -233,6 +242,8 @@ def run_steps(w, rank, lay, b, dev, warmup: int, steps: int, stream, seed: int) 
     final = snapshot(b, wins)
     want = {S: full_flag_oracle(b["g16"], w.dtype, S) for S in {S for _, S in found_flags}}
     parity = replay_parity(w, start, final, applied, [(f, want[S]) for f, S in found_flags])
+    parity["layouts_equal"] = layouts_equal(w.psi, w.n)
+    parity["ok"] = parity["ok"] and parity["layouts_equal"]
     step_ms = [x[2].elapsed_time(x[3]) for x in ev]
     check_ms = [x[0].elapsed_time(x[1]) for x in ev]
     return {"step_ms": step_ms, "check_ms": check_ms, "parity": parity}
@@ -719,6 +730,8 @@ def main():
     final = snapshot(b, wins)
     want = {S: full_flag_oracle(b["g16"], w.dtype, S) for S in {S for _, S in found_flags}}
     parity = replay_parity(w, start, final, applied, [(f, want[S]) for f, S in found_flags])
+    parity["layouts_equal"] = layouts_equal(psi, n)
+    parity["ok"] = parity["ok"] and parity["layouts_equal"]
     log(f"[bench] parity {'ok' if parity['ok'] else 'FAILED'}: max ulp {parity['max_ulp']}")
 
     copy_gbps, stream_copy_gbps = (None, None) if args.no_copy else copy_bandwidth(dev)

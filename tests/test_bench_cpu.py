@@ -117,3 +117,8 @@ def test_replay_parity_reports_zero_ulp_on_oracle_data_and_finds_a_flipped_bit(b
     assert not r["ok"] and not r["flags_equal"]
     assert r["max_ulp"]["m"] == 1 and r["non_bitwise"]["m"] == 1
     assert r["max_ulp"]["master"] > 2 and r["non_bitwise"]["master"] == 1
+
+
+def test_bench_layout_parity_covers_every_rank(bench):
+    for psi, n in ((10_000_000_000, 1), (7_500_000_000, 8), (8_810_000_003, 64), (1_500_000_000, 1)):
+        assert bench.layouts_equal(psi, n)
