@@ -787,7 +787,12 @@ def main():
                     "overflow_check_GBps": CHECK_BYTES_PER_PARAM * cnt / (avg_check_ms * 1e-3)
                     / 1e9,
                     "device_copy_GBps": copy_gbps,
-                    "stream_copy_GBps": stream_copy_gbps},
+                    "stream_copy_GBps": stream_copy_gbps,
+                    # the step's algorithmic rate as a fraction of the library's own plain
+                    # streaming copy in this run: the practical ceiling of a stream that
+                    # mixes reads and writes
+                    "step_vs_stream_copy": (achieved / stream_copy_gbps
+                                            if stream_copy_gbps else None)},
         "parity": parity,
         "cpu_baseline": cpu,
     }
