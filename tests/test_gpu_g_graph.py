@@ -82,3 +82,44 @@ def test_graph_replays_match_eager_and_oracle(dtype, phase):
     log(f"  graph x{steps} {dtype}", assert_close(host_state(G), ref, dtype, "graph replay"))
     assert all(v.guards_intact() for v in G.values())
     del graph
+
+
+def test_graph_captures_the_allocation_free_check():
+    # the allocation-free check (flag and sum of squares, its partial sums in the
+    # library's fixed array) captured once and replayed over new gradients, with an
+    # eager call of another size between replays rewriting the shared array: every
+    # replay equals the workspace form on the same gradients, bit for bit
+    count, S = 1_000_003, 3.0
+    g = GuardedView(count, torch.float16, 1, DEV)
+    other = torch.empty(70_001, dtype=torch.bfloat16, device=DEV).fill_(0.5)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ssq = torch.zeros(1, device=DEV)
+    oflag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ossq = torch.zeros(1, device=DEV)
+    wflag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    wssq = torch.zeros(1, device=DEV)
+    parts = torch.empty(zs.SUMSQ_PARTIALS, dtype=torch.float64, device=DEV)
+    g.view.copy_(synth.fill_normal_(torch.empty(count, dtype=torch.float16), 1e-2, 95).to(DEV))
+    zs.zero_overflow_check_noalloc(g.view, count, 1, 0, S, flag, ssq)   # before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        zs.zero_overflow_check_noalloc(g.view, count, 1, 0, S, flag, ssq)
+    torch.cuda.synchronize()
+    for i in range(5):
+        grads = synth.fill_normal_(torch.empty(count, dtype=torch.float16), 1e-2, 96 + i)
+        if i == 3:
+            grads[count // 2] = float("inf")
+        g.view.copy_(grads.to(DEV))
+        graph.replay()
+        zs.zero_overflow_check_noalloc(other, other.numel(), 1, 0, 1.0, oflag, ossq)
+        torch.cuda.synchronize()
+        got = (int(flag.item()), int(ssq.view(torch.int32).item()))
+        zs.zero_overflow_check(g.view, count, 1, 0, S, wflag, wssq, parts)
+        torch.cuda.synchronize()
+        want = (int(wflag.item()), int(wssq.view(torch.int32).item()))
+        assert got == want, (i, got, want)
+        assert got[0] == (1 if i == 3 else 0)
+        assert float(ossq.item()) == 0.25 * other.numel() and int(oflag.item()) == 0
+    assert g.guards_intact()
+    del graph
