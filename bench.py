@@ -12,9 +12,11 @@ gradients ~N(0,1e-3) carrying a loss scale of 65536, FP32 master ~N(0,0.02),
 m = v = 0 at the start, AdamW lr 1e-4, wd 0.1.
 
 Prints one JSON line: params/s over the timed steps, the step kernel's HBM
-roofline (algorithmic 28 B/param over its HIP-event-timed average duration,
-against the 8 TB/s peak), the HBM traffic measured by rocprofv3 counters when
-the profiled kernel's machine code matches the built one, the parity of the
+roofline (algorithmic 28 B/param over its HIP-event-timed duration, against the
+8 TB/s peak; the library enqueues a step as consecutive launches of the step
+kernel, so this is the launches' average bytes over their average duration with
+the gaps between them counted), the HBM traffic per step measured by rocprofv3
+counters when the profiled kernel's machine code matches the built one, the parity of the
 run's own steps against the oracle (windows of the benchmarked buffers
 replayed on the host, and the flag of every step against the oracle's over the
 whole gradient buffer), the same measurements on the other roofline
@@ -55,7 +57,8 @@ def built_isa_hashes() -> dict:
 
 
 def measured_traffic(workload_name: str):
-    """HBM bytes per step-kernel launch from the committed rocprofv3 counter summary.
+    """HBM bytes per step (the sum over its launches of the step kernel) from the committed
+    rocprofv3 counter summary.
 
     Returns None unless the summary was taken on this workload with the same
     machine code of the step kernel as the library built now."""
@@ -73,7 +76,7 @@ def measured_traffic(workload_name: str):
     if kv.get("workload") != workload_name:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["hbm_bytes_per_step"])
     except (KeyError, ValueError):
         return None
 

@@ -40,7 +40,8 @@ def test_product_header_holds_no_process_settings():
     # the launch-shape overrides live in the tuning header only
     product = declared_functions(HEADER)
     assert not [n for n in product if n.startswith("zero_set_")], product
-    assert declared_functions(TUNING_HEADER) == ["zero_set_grid_cap", "zero_set_occupancy"]
+    assert declared_functions(TUNING_HEADER) == ["zero_set_grid_cap", "zero_set_launch_piece",
+                                                 "zero_set_occupancy"]
 
 
 def test_header_declares_the_boundary():
@@ -566,3 +567,10 @@ def test_tuning_setters_take_any_32_bit_value_and_the_binding_checks_range():
             zs.zero_set_occupancy(bad)
     zs.zero_set_grid_cap(0)
     zs.zero_set_occupancy(0)
+    # elements per launch: any 64-bit value (0 = each kernel's rule)
+    for v in (0, 1, 2047, 2048, 1 << 28, 2 ** 64 - 1):
+        assert zs.lib.zero_set_launch_piece(v) == 0
+    for bad in (-1, 2 ** 64):
+        with pytest.raises(ValueError):
+            zs.zero_set_launch_piece(bad)
+    zs.zero_set_launch_piece(0)

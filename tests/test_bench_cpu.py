@@ -54,7 +54,7 @@ def write_profile(path, symbol, isa, workload, traffic):
     with open(path, "w") as f:
         f.write("# test profile\n\n")
         f.write(f"- kernel_symbol: `{symbol}`\n- kernel_isa_sha256: `{isa}`\n")
-        f.write(f"- workload: {workload}\n- hbm_bytes_per_launch: {traffic:.6e}\n")
+        f.write(f"- workload: {workload}\n- hbm_bytes_per_step: {traffic:.6e}\n")
 
 
 def test_traffic_used_only_for_matching_code_and_workload(bench, hashes, tmp_path, monkeypatch):

@@ -47,14 +47,18 @@ def test_step_tile_loop(cap, dtype):
 
 
 def test_step_g32_and_accumulate_tile_loop(cap):
-    rng = np.random.default_rng(cap)
+    g32_and_accumulate_case(f"cap={cap}", cap)
+
+
+def g32_and_accumulate_case(label, seed):
+    rng = np.random.default_rng(seed)
     for count in COUNTS:
         for dtype in ("f16", "bf16"):
             acc = GuardedView(count, torch.float32, 1, DEV)
             gv = GuardedView(count, TD[dtype], 1, DEV)
             ref_acc = np.zeros(count, np.float32)
             flag = torch.full((1,), 7, dtype=torch.int32, device=DEV)
-            mbs = micro_batches(count, 3, dtype, 70 + cap)
+            mbs = micro_batches(count, 3, dtype, 70 + seed)
             for j, g in enumerate(mbs):
                 gv.view.copy_(g.to(DEV))
                 if j == len(mbs) - 1:      # the last one with the fused FP32 check
@@ -87,8 +91,37 @@ def test_step_g32_and_accumulate_tile_loop(cap):
             torch.cuda.synchronize()
             got = dict(master=f32(V["master"].view), m=f32(V["m"].view), v=f32(V["v"].view),
                        w16=u16(V["w16"].view))
-            assert_close(got, ref, dtype, f"g32 cap={cap} count={count}")
+            assert_close(got, ref, dtype, f"g32 {label} count={count}")
             assert all(x.guards_intact() for x in list(V.values()) + [G])
+
+
+# Elements per launch of the step and the accumulates: below one tile (one
+# tile per launch), three tiles and a remainder (rounded down to three), and
+# seven tiles.  The shard goes out as consecutive launches; every result bit
+# must match the oracle, heads, tails and the element-wise path included.
+PIECES = (1, 3 * 2048 + 5, 7 * 2048)
+
+
+@pytest.fixture(params=PIECES)
+def piece(request):
+    zs.zero_set_launch_piece(request.param)
+    yield request.param
+    torch.cuda.synchronize()
+    zs.zero_set_launch_piece(0)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_step_in_pieces(piece, dtype):
+    for count in COUNTS:
+        for phase in (0, 3):
+            run_case(count, dtype, dict.fromkeys(("g16", "w16", "master", "m", "v"), phase),
+                     steps=2, seed=count + phase + 7)
+        run_case(count, dtype, dict(g16=1, w16=2, master=0, m=3, v=1), steps=2, seed=count + 7)
+    log(f"step {dtype} in pieces of {piece}: within the bar")
+
+
+def test_step_g32_and_accumulate_in_pieces(piece):
+    g32_and_accumulate_case(f"piece={piece}", piece % 97)
 
 
 def test_flag_tile_loop(cap):
@@ -183,6 +216,54 @@ def test_step_occupancy_settings_change_nothing():
         del results, V
         torch.cuda.empty_cache()
     log("step occupancy settings 0/1/2/3/8: bitwise equal, windows match the oracle")
+
+
+def test_step_launch_pieces_change_nothing():
+    # The step's own rule splits a shard past 2^27 elements into launches of
+    # 2^27 (here three and a ragged fourth): the default, one launch over
+    # everything, and pieces of 3 * 2^20 + 7 elements give the same bits, and
+    # windows across piece boundaries match the oracle.  2^28 + 2^27 + 12,345
+    # elements at phase 3, FP16.
+    count, phase, dtype = (1 << 28) + (1 << 27) + 12_345, 3, "f16"
+    td = TD[dtype]
+    g16 = synth.fill_normal_(torch.empty(count, dtype=td), 1e-3, 73_000)
+    master0 = synth.fill_normal_(torch.empty(count), 0.02, 73_001)
+    V = {k: GuardedView(count, td if k in ("g16", "w16") else torch.float32, phase, DEV)
+         for k in ("g16", "w16", "master", "m", "v")}
+    V["g16"].view.copy_(g16.to(DEV))
+    results = {}
+    try:
+        for piece in (0, 2 ** 64 - 1, 3 * (1 << 20) + 7):
+            zs.zero_set_launch_piece(piece)
+            V["master"].view.copy_(master0.to(DEV))
+            for k in ("m", "v", "w16"):
+                V[k].view.zero_()
+            for t in (1, 2):
+                zs.zero_adam_step(V["w16"].view, V["g16"].view, V["master"].view, V["m"].view,
+                                  V["v"].view, count, 1, 0, step=t, loss_scale=1000.0, **HP)
+            torch.cuda.synchronize()
+            results[piece] = {k: V[k].view.clone() for k in ("w16", "master", "m", "v")}
+    finally:
+        torch.cuda.synchronize()
+        zs.zero_set_launch_piece(0)
+    for piece in list(results)[1:]:
+        for k in results[0]:
+            iv = torch.int16 if k == "w16" else torch.int32
+            assert torch.equal(results[piece][k].view(iv), results[0][k].view(iv)), (piece, k)
+    assert all(v.guards_intact() for v in V.values())
+    gh = u16(g16)
+    b28 = 1 << 28
+    for a, b in ((0, 4096), (b28 - 4096, b28 + 4096), (count - 4096, count)):
+        ref = dict(master=master0[a:b].numpy().copy(), m=np.zeros(b - a, np.float32),
+                   v=np.zeros(b - a, np.float32), w16=np.zeros(b - a, np.uint16))
+        for t in (1, 2):
+            oracle.adam_step(ref["w16"], gh[a:b], ref["master"], ref["m"], ref["v"], dtype,
+                             step=t, loss_scale=1000.0, **HP)
+        got = {k: (u16 if k == "w16" else f32)(results[0][k][a:b]) for k in ref}
+        assert_close(got, ref, dtype, f"piece window {a}")
+    del results, V
+    torch.cuda.empty_cache()
+    log("step launch pieces default/one/3M+7: bitwise equal, windows match the oracle")
 
 
 def test_accumulate_and_check_occupancy_settings_change_nothing():

@@ -91,6 +91,7 @@ from ._binding import (  # noqa: F401
     zero_scaler_update_dev,
     zero_set_grid_cap,
     zero_set_occupancy,
+    zero_set_launch_piece,
     zero_shard_layout,
     zero_strerror,
 )
@@ -132,6 +133,7 @@ __all__ = [
     "zero_ckpt_read_resharded",
     "zero_set_grid_cap",
     "zero_set_occupancy",
+    "zero_set_launch_piece",
     "layout",
     "overflow_check",
     "adam_step",

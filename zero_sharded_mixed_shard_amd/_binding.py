@@ -132,6 +132,8 @@ lib.zero_set_grid_cap.argtypes = [_u32]
 lib.zero_set_occupancy.argtypes = [_u32]
 lib.zero_set_occupancy.restype = _i32
 lib.zero_set_grid_cap.restype = _i32
+lib.zero_set_launch_piece.argtypes = [_u64]
+lib.zero_set_launch_piece.restype = _i32
 lib.zero_strerror.argtypes = [_i32]
 lib.zero_strerror.restype = ctypes.c_char_p
 
@@ -154,6 +156,15 @@ def zero_set_occupancy(blocks_per_cu: int) -> None:
     if not 0 <= blocks_per_cu < 1 << 32:
         raise ValueError("blocks_per_cu must fit in 32 bits")
     lib.zero_set_occupancy(blocks_per_cu)
+
+
+def zero_set_launch_piece(elements: int) -> None:
+    """Most elements per launch of this thread's step and accumulate launches; a longer shard
+    goes out as consecutive launches on one stream.  0 restores each kernel's rule (step: 2^27,
+    accumulates: one launch); 2**64 - 1 means one launch."""
+    if not 0 <= elements < 1 << 64:
+        raise ValueError("elements must fit in 64 bits")
+    lib.zero_set_launch_piece(elements)
 
 
 @dataclass(frozen=True)

@@ -33,12 +33,15 @@ std::atomic<int> g_lds_block[kMaxDevices];
 
 // Test and tuning overrides (zero_shard_tuning.h), kept per thread so that one
 // caller's setting never changes another thread's launches: the grid cap and
-// the resident blocks per CU of the streaming kernels (0: each kernel's rule).
+// the resident blocks per CU of the streaming kernels and the elements per
+// launch (0: each kernel's rule).
 thread_local uint64_t t_grid_cap = zs::kMaxBlocks;
 thread_local int t_occupancy = 0;
+thread_local uint64_t t_piece = 0;
 
 int device_props(zs::DeviceProps *out) {
     out->occupancy = t_occupancy;
+    out->piece = t_piece;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
@@ -182,6 +185,11 @@ extern "C" int zero_set_grid_cap(uint32_t blocks) {
 
 extern "C" int zero_set_occupancy(uint32_t blocks_per_cu) {
     t_occupancy = blocks_per_cu >= 8 ? 8 : static_cast<int>(blocks_per_cu);
+    return ZERO_OK;
+}
+
+extern "C" int zero_set_launch_piece(uint64_t elements) {
+    t_piece = elements;
     return ZERO_OK;
 }
 

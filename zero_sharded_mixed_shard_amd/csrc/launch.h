@@ -57,13 +57,15 @@ constexpr uint64_t kMaxBlocks = 1ull << 23;
 uint64_t max_blocks();
 
 // What the launchers need to know of the current device, and the calling
-// thread's occupancy override.
+// thread's overrides of the launch shape.
 struct DeviceProps {
     int cus;              // compute units
     int lds_per_cu;       // LDS bytes of one compute unit
     int lds_per_block;    // largest LDS allocation of one workgroup
     int occupancy;        // resident blocks per CU of the streaming kernels: 0 = each
                           // kernel's own rule, 1-7 this cap, 8 no cap
+    uint64_t piece;       // most elements per launch of the step and the accumulates:
+                          // 0 = each kernel's own rule
 };
 
 // Dynamic LDS to reserve, unused by the kernel, so that at most per_cu blocks

@@ -11,7 +11,8 @@
 // LDS only to cap the resident blocks per CU).  Every access of the streaming
 // kernels is non-temporal (the data is touched once), and the step launches
 // one block per tile (a grid-stride loop only past 2^23 tiles): both measured
-// faster on MI355X than a resident grid looping over tiles.
+// faster on MI355X than a resident grid looping over tiles.  A long shard's
+// step goes out as consecutive launches of 2^27 elements (kStepPiece).
 //
 // Numerics follow the update of "Training models too big for one GPU: ZeRO &
 // FSDP" ("Adam, and why it's expensive", "Mixed-precision training") with
@@ -876,6 +877,51 @@ inline uint32_t grid_for(uint64_t need) {
     return static_cast<uint32_t>(need < cap ? need : cap);
 }
 
+// Elements per launch of the step.  A long shard goes out as launches of at
+// most this many elements, back to back on one stream, which ran faster than
+// one launch over the whole shard at every size past it (MI355X, the arrays
+// of one process timed under every setting in turn, median TB/s):
+//   1e10 FP16, three processes, one launch / 2^28 / 2^27 / 2^26 / 2^25 / 2^24:
+//     6.33 / 6.44 / 6.44 / 6.41 / 6.34 / 6.18;  6.32 / 6.42 / 6.41 / 6.38 /
+//     6.31 / 6.16;  6.25 / 6.36 / 6.35 / 6.31 / 6.23 / 6.08
+//   two processes each, one launch against 2^27: 937.5M BF16 6.09, 6.02 ->
+//     6.21, 6.15; 1.5e9 BF16 6.00, 6.00 -> 6.17, 6.18; 2^32 FP16 6.22, 6.22 ->
+//     6.41, 6.41; FP32 gradients 2^30 5.85, 5.51 -> 6.09, 5.61 and 2^32
+//     6.33, 6.38 -> 6.43, 6.43
+// Between 2^26 and 2^28 the sizes differ by less than the spread between
+// processes; below 2^26 the gaps between launches cost more than the split
+// gains.  The accumulates gain nothing from it (2^30 and 2^32 elements: 6.33
+// TB/s in one launch, 6.28-6.34 in pieces of 2^27 or 2^28) and stay one launch.
+constexpr uint64_t kStepPiece = 1ull << 27;
+
+// Consecutive ranges of at most piece_tiles whole tiles of a shard, each
+// enqueued by launch(offset, count, head, n_tiles) over the views advanced by
+// offset elements: the first range keeps the shard's head, the last one its
+// ragged rest.  piece_tiles == 0, or a shard of at most piece_tiles tiles:
+// one launch over everything.
+template <typename F>
+hipError_t by_pieces(uint64_t count, uint32_t head, uint64_t n_tiles, uint64_t tile,
+                     uint64_t piece_tiles, F &&launch) {
+    if (piece_tiles == 0 || n_tiles <= piece_tiles) return launch(0, count, head, n_tiles);
+    for (uint64_t t0 = 0; t0 < n_tiles; t0 += piece_tiles) {
+        const uint64_t nt = n_tiles - t0 < piece_tiles ? n_tiles - t0 : piece_tiles;
+        const uint64_t off = t0 == 0 ? 0 : head + t0 * tile;
+        const uint32_t h = t0 == 0 ? head : 0;
+        const uint64_t cnt = t0 + nt == n_tiles ? count - off : h + nt * tile;
+        const hipError_t e = launch(off, cnt, h, nt);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Whole tiles per launch: the thread's override, else the kernel's rule
+// (0: one launch).
+inline uint64_t piece_tiles(uint64_t rule, uint64_t tile, const DeviceProps &dev) {
+    const uint64_t elems = dev.piece != 0 ? dev.piece : rule;
+    if (elems == 0) return 0;
+    return elems < tile ? 1 : elems / tile;
+}
+
 template <int DT, typename GT, int MODE>
 hipError_t adam_launch(uint16_t *w16, const GT *g, float *master, float *m, float *v,
                        uint64_t count, const AdamScalars &s, const int32_t *flag,
@@ -889,12 +935,16 @@ hipError_t adam_launch(uint16_t *w16, const GT *g, float *master, float *m, floa
     if (head > count) head = static_cast<uint32_t>(count);
     constexpr uint64_t kTile = static_cast<uint64_t>(kAdamU) * kGroup;
     const uint64_t n_tiles = (count - head) / kTile;
-    const uint64_t rest = count - head - n_tiles * kTile;
-    const uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
-    adam_step_vec<DT, GT, kAdamU, MODE><<<grid_for(need), kThreads,
-                                          step_lds_bytes(dev), stream>>>(
-        w16, g, master, m, v, count, head, n_tiles, s, flag, ctl);
-    return hipGetLastError();
+    const size_t lds = step_lds_bytes(dev);
+    return by_pieces(
+        count, head, n_tiles, kTile, piece_tiles(kStepPiece, kTile, dev),
+        [&](uint64_t off, uint64_t cnt, uint32_t h, uint64_t nt) {
+            const uint64_t r = cnt - h - nt * kTile;
+            const uint64_t need = nt > 0 ? nt : (r + kThreads - 1) / kThreads;
+            adam_step_vec<DT, GT, kAdamU, MODE><<<grid_for(need), kThreads, lds, stream>>>(
+                w16 + off, g + off, master + off, m + off, v + off, cnt, h, nt, s, flag, ctl);
+            return hipGetLastError();
+        });
 }
 
 // The unscale mode: from the control block when there is one, else by S.
@@ -925,12 +975,16 @@ hipError_t accumulate_dispatch(float *acc, const uint16_t *g16, uint64_t count,
     if (head > count) head = static_cast<uint32_t>(count);
     constexpr uint64_t kTile = static_cast<uint64_t>(kAccU) * kGroup;
     const uint64_t n_tiles = (count - head) / kTile;
-    const uint64_t rest = count - head - n_tiles * kTile;
-    const uint64_t need = n_tiles > 0 ? n_tiles : (rest + kThreads - 1) / kThreads;
-    accumulate_vec<DT, FIRST, kAccU, CHECK><<<grid_for(need), kThreads,
-                                              accumulate_lds_bytes(count, FIRST, CHECK, dev), stream>>>(
-        acc, g16, count, head, n_tiles, chk);
-    return hipGetLastError();
+    const size_t lds = accumulate_lds_bytes(count, FIRST, CHECK, dev);
+    return by_pieces(
+        count, head, n_tiles, kTile, piece_tiles(0, kTile, dev),
+        [&](uint64_t off, uint64_t cnt, uint32_t h, uint64_t nt) {
+            const uint64_t r = cnt - h - nt * kTile;
+            const uint64_t need = nt > 0 ? nt : (r + kThreads - 1) / kThreads;
+            accumulate_vec<DT, FIRST, kAccU, CHECK><<<grid_for(need), kThreads, lds, stream>>>(
+                acc + off, g16 + off, cnt, h, nt, chk);
+            return hipGetLastError();
+        });
 }
 
 struct CheckGrid {
