@@ -3,21 +3,26 @@
 C1 (1M params, rank 3 of 8)    three ZeRO layouts, every element, all agree bitwise
 C2 (GPT-2-small shapes, N=8)  every element of all 8 ranks for 10 steps, and the
                               concatenated shards equal the unsharded (N=1) update
-C3 (7.5e9, N=8, BF16)         rank 1's 937.5M-element shard, 20 warm steps, sampled windows
-                              against the oracle, and invariants at every element
-C4 (1e10, N=1, 160 GB)        the whole buffer, 5 steps, windows up to the last element
-                              (indices past 2^32) against the oracle, invariants at every
-                              element, flag property at a far position
+C3 (7.5e9, N=8, BF16)         rank 1's 937.5M-element shard, 20 warm steps: the first step
+                              against the oracle at every element, all 20 on sampled windows,
+                              and invariants at every element
+C4 (1e10, N=1, 160 GB)        the whole buffer, 5 steps: the first step against the oracle at
+                              every element (indices past 2^32 included), all 5 on windows up
+                              to the last element, invariants at every element, flag
+                              property at a far position
 C5 (8,810,000,003, N=64)      rank 63's ragged shard (61 padding elements, start = 5 mod 8),
                               10 steps with inf/NaN injection on even steps: every flag,
                               every element, S halving and t bit-exact against the oracle
-C6 (1.5e9, N=1, BF16, 24 GB)  the whole buffer, 10 steps, sampled windows, and invariants
-                              at every element
+C6 (1.5e9, N=1, BF16, 24 GB)  the whole buffer, 10 steps: the last step against the oracle at
+                              every element, all 10 on sampled windows, and invariants at
+                              every element
 (invariants: w16 = RNE16(master) bitwise, v >= 0, master, m and v finite)
 
 Inputs come from `synth` (seeded); expected values only from `oracle`.
 """
 import gc
+
+import time
 
 import numpy as np
 import pytest
@@ -202,6 +207,49 @@ def full_buffer_invariants(master, m, v, w16, what, chunk=1 << 28):
     log(f"  {what}: w16 == RNE16(master), v >= 0, master/m/v finite at all {n} elements")
 
 
+def every_element_vs_oracle(g16, before, after, dtype, t, S, hp, what, chunk=1 << 27):
+    """One step of a full-size shard against the oracle at every element: chunk by
+    chunk, the state before the step (device copies, or None for zeros) and the
+    gradients go to pinned host buffers, the oracle steps them on the host's threads,
+    and the device's result must meet the bar at every element."""
+    n = g16.numel()
+    c = min(chunk, n)
+    pin = lambda dt: torch.empty(c, dtype=dt, pin_memory=True)
+    hg, hw = pin(g16.dtype), pin(after["w16"].dtype)
+    state = {k: pin(torch.float32) for k in ("master", "m", "v")}
+    got = {k: pin(torch.float32) for k in ("master", "m", "v")}
+    w16_ref = np.zeros(c, np.uint16)
+    bits16 = lambda x: x.view(torch.int16).numpy().view(np.uint16)
+    worst = {}
+    t0 = time.time()
+    for a in range(0, n, chunk):
+        b = min(n, a + chunk)
+        L = b - a
+        if a and (a // chunk) % 8 == 0:
+            log(f"  {what}: {a} of {n} elements compared ({time.time() - t0:.0f} s)")
+        hg[:L].copy_(g16[a:b])
+        hw[:L].copy_(after["w16"][a:b])
+        for k in ("master", "m", "v"):
+            if before[k] is None:
+                state[k][:L].zero_()
+            else:
+                state[k][:L].copy_(before[k][a:b])
+            got[k][:L].copy_(after[k][a:b])
+        h = {k: state[k][:L].numpy() for k in ("master", "m", "v")}
+        h["w16"] = w16_ref[:L]
+        oracle.adam_step_mt(h["w16"], bits16(hg[:L]), h["master"], h["m"], h["v"], dtype, step=t,
+                            loss_scale=S, **hp)
+        dev = {k: got[k][:L].numpy() for k in ("master", "m", "v")}
+        dev["w16"] = bits16(hw[:L])
+        st = assert_close(dev, h, dtype, f"{what} [{a}, {b})")
+        for k, (mx, nz) in st.items():
+            pm, pn = worst.get(k, (0, 0))
+            worst[k] = (max(pm, mx), pn + nz)
+    log(f"  {what} step {t} at all {n} elements against the oracle ({time.time() - t0:.0f} s): "
+        f"(max ulp, non-bitwise) {worst}")
+    return worst
+
+
 def take(t, wins, conv):
     return [conv(t[a:b]) for a, b in wins]
 
@@ -240,8 +288,15 @@ def test_c3_bf16_warm_shard_windows():
         zs.zero_overflow_check(g16, psi, n, r, S, flag)
         if i in (0, len(steps) - 1):
             assert oracle.overflow_flag_mt(u16(g16), "bf16", S) == flag.item() == 0
+        before = dict(master=master.clone(), m=m.clone(), v=v.clone()) if i == 0 else None
         zs.zero_adam_step(w16, g16, master, m, v, psi, n, r, step=t, loss_scale=S,
                           found_inf=flag, **hp)
+        if i == 0:   # the first step (warm moments, t = 101) at every element
+            torch.cuda.synchronize()
+            every_element_vs_oracle(g16, before, dict(master=master, m=m, v=v, w16=w16), "bf16",
+                                    t, S, hp, "C3")
+            del before
+            torch.cuda.empty_cache()
     torch.cuda.synchronize()
     log("C3 GPU steps done; oracle on windows")
     run_windows_oracle(host, gsteps, "bf16", hp, steps, S)
@@ -260,7 +315,7 @@ def test_c4_ten_billion_unsharded_windows():
     psi = w.psi
     hp, S = hp_of(w), w.loss_scale
     free, total = torch.cuda.mem_get_info(DEV)
-    need = psi * 16 + (1 << 30)
+    need = psi * 20 + (1 << 30)     # the five arrays and a copy of the starting master
     if free < need:
         pytest.skip(f"needs {need / 1e9:.0f} GB of device memory, {free / 1e9:.0f} GB free")
     log(f"C4 allocating 160 GB ({free / 1e9:.0f} GB free)")
@@ -277,11 +332,19 @@ def test_c4_ten_billion_unsharded_windows():
     gw = take(g16, wins, u16)
     flag = flag_buf()
     steps = list(range(1, w.steps + 1))
+    master0 = master.clone()
     for t in steps:
         zs.zero_overflow_check(g16, psi, 1, 0, S, flag)
         zs.zero_adam_step(w16, g16, master, m, v, psi, 1, 0, step=t, loss_scale=S,
                           found_inf=flag, **hp)
         log(f"  step {t} enqueued")
+        if t == 1:   # the first step at every element, in the launch shape bench.py times
+            torch.cuda.synchronize()
+            assert flag.item() == 0
+            every_element_vs_oracle(g16, dict(master=master0, m=None, v=None),
+                                    dict(master=master, m=m, v=v, w16=w16), "f16", t, S, hp, "C4")
+            del master0
+            torch.cuda.empty_cache()
     torch.cuda.synchronize()
     assert flag.item() == 0
     run_windows_oracle(host, [gw] * len(steps), "f16", hp, steps, S)
@@ -327,8 +390,16 @@ def test_c6_one_and_a_half_billion_unsharded_windows():
         synth.fill_normal_(g16, w.grad_std, synth.seed_of(6, 1, t))
         gsteps.append(take(g16, wins, u16))
         zs.zero_overflow_check(g16, psi, 1, 0, S, flag)
+        last = t == steps[-1]
+        before = dict(master=master.clone(), m=m.clone(), v=v.clone()) if last else None
         zs.zero_adam_step(w16, g16, master, m, v, psi, 1, 0, step=t, loss_scale=S,
                           found_inf=flag, **hp)
+        if last:   # the last step (moments of nine steps, t = 10) at every element
+            torch.cuda.synchronize()
+            every_element_vs_oracle(g16, before, dict(master=master, m=m, v=v, w16=w16), "bf16",
+                                    t, S, hp, "C6")
+            del before
+            torch.cuda.empty_cache()
     torch.cuda.synchronize()
     assert flag.item() == 0
     log("C6 GPU steps done; oracle on windows")
