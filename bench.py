@@ -56,12 +56,10 @@ def built_isa_hashes() -> dict:
     return mod.read_isa_hashes()
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per step (the sum over its launches of the step kernel) from the committed
-    rocprofv3 counter summary.
-
-    Returns None unless the summary was taken on this workload with the same
-    machine code of the step kernel as the library built now."""
+def traffic_profile(workload_name: str):
+    """The machine-readable fields of the committed rocprofv3 counter summary, or None
+    unless it was taken on this workload with the same machine code of the step kernel
+    as the library built now."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -75,8 +73,25 @@ def measured_traffic(workload_name: str):
         return None
     if kv.get("workload") != workload_name:
         return None
+    return kv
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per step (the sum over its launches of the step kernel) from the committed
+    rocprofv3 counter summary, or None (see traffic_profile)."""
+    kv = traffic_profile(workload_name)
     try:
-        return float(kv["hbm_bytes_per_step"])
+        return float(kv["hbm_bytes_per_step"]) if kv else None
+    except (KeyError, ValueError):
+        return None
+
+
+def launches_per_step(workload_name: str):
+    """Launches of the step kernel per step, as the same summary's trace counted them
+    (the library enqueues a long shard's step as consecutive launches), or None."""
+    kv = traffic_profile(workload_name)
+    try:
+        return int(kv["launches_per_step"]) if kv else None
     except (KeyError, ValueError):
         return None
 
@@ -728,6 +743,7 @@ def main():
     avg_check_ms = sum(check_ms) / len(check_ms)
     achieved = STEP_BYTES_PER_PARAM * cnt / (avg_step_ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name)
+    launches = launches_per_step(w.name)
 
     log("[bench] parity of the run's steps against the oracle ...")
     final = snapshot(b, wins)
@@ -782,7 +798,11 @@ def main():
                    "control": args.control},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     # one step is this many launches of the step kernel (from the profile's
+                     # trace); achieved = their average bytes over their average duration
+                     "launches_per_step": launches,
+                     "ms_per_launch": avg_step_ms / launches if launches else None},
         "kernels": {"adam_step_ms": avg_step_ms, "adam_step_ms_min": min(step_ms),
                     "adam_step_ms_median": statistics.median(step_ms),
                     "overflow_check_ms": avg_check_ms,

@@ -50,11 +50,12 @@ def test_every_step_kernel_has_a_hash(hashes):
     assert hashes[step_symbol(hashes, 0)] != hashes[step_symbol(hashes, 1)]
 
 
-def write_profile(path, symbol, isa, workload, traffic):
+def write_profile(path, symbol, isa, workload, traffic, launches=75):
     with open(path, "w") as f:
         f.write("# test profile\n\n")
         f.write(f"- kernel_symbol: `{symbol}`\n- kernel_isa_sha256: `{isa}`\n")
-        f.write(f"- workload: {workload}\n- hbm_bytes_per_step: {traffic:.6e}\n")
+        f.write(f"- workload: {workload}\n- launches_per_step: {launches}\n")
+        f.write(f"- hbm_bytes_per_step: {traffic:.6e}\n")
 
 
 def test_traffic_used_only_for_matching_code_and_workload(bench, hashes, tmp_path, monkeypatch):
@@ -63,7 +64,9 @@ def test_traffic_used_only_for_matching_code_and_workload(bench, hashes, tmp_pat
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(prof))
     write_profile(prof, sym, hashes[sym], "flat10B_n1_f16_adamw", 2.8e11)
     assert bench.measured_traffic("flat10B_n1_f16_adamw") == pytest.approx(2.8e11)
+    assert bench.launches_per_step("flat10B_n1_f16_adamw") == 75
     assert bench.measured_traffic("other_workload") is None
+    assert bench.launches_per_step("other_workload") is None
     write_profile(prof, sym, "0" * 64, "flat10B_n1_f16_adamw", 2.8e11)
     assert bench.measured_traffic("flat10B_n1_f16_adamw") is None
     write_profile(prof, step_symbol(hashes, 1), hashes[sym], "flat10B_n1_f16_adamw", 2.8e11)
