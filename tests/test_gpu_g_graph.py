@@ -1,8 +1,9 @@
 """The device-controlled step captured once into a HIP graph and replayed.
 
 With S, t and the skip flag in device memory, check -> decision -> step needs
-no host read-back, so the three launches can be captured into one graph and
-replayed once per training step.  Each replay is checked against the same
+no host read-back, so its launches (the step's as several consecutive launches
+on a long shard) can be captured into one graph and replayed once per training
+step.  Each replay is checked against the same
 step run eagerly on a second copy of the state (bitwise: the same kernels on
 the same inputs), with eager work and synchronisation between the replays,
 and the final state against the oracle's host-driven sequence.
@@ -42,8 +43,19 @@ def host_state(V):
                 w16=u16(V["w16"].view))
 
 
-@pytest.mark.parametrize("dtype,phase", [("f16", 0), ("bf16", 3)])
-def test_graph_replays_match_eager_and_oracle(dtype, phase):
+@pytest.mark.parametrize("dtype,phase,piece", [("f16", 0, 0), ("bf16", 3, 0), ("f16", 1, 7 * 2048)])
+def test_graph_replays_match_eager_and_oracle(dtype, phase, piece):
+    # piece: elements per step launch (0: the library's rule, one launch at this size;
+    # 7 tiles: the step is captured as 70 consecutive launches, as long shards are)
+    zs.zero_set_launch_piece(piece)
+    try:
+        graph_replays_case(dtype, phase)
+    finally:
+        torch.cuda.synchronize()
+        zs.zero_set_launch_piece(0)
+
+
+def graph_replays_case(dtype, phase):
     count, steps, S0 = 1_000_003, 8, 65536.0
     grads = make_grads(count, steps, dtype, 900, bad_steps=(3, 6))
     dgrads = [g.to(DEV) for g in grads]
