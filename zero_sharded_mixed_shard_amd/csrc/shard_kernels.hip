@@ -11,8 +11,8 @@
 // LDS only to cap the resident blocks per CU).  Every access of the streaming
 // kernels is non-temporal (the data is touched once), and the step launches
 // one block per tile (a grid-stride loop only past 2^23 tiles): both measured
-// faster on MI355X than a resident grid looping over tiles.  A long shard's
-// step goes out as consecutive launches of 2^27 elements (kStepPiece).
+// faster on MI355X than a resident grid looping over tiles.  A shard of at
+// least 2^28 elements steps in consecutive launches of 2^27 (kStepPiece).
 //
 // Numerics follow the update of "Training models too big for one GPU: ZeRO &
 // FSDP" ("Adam, and why it's expensive", "Mixed-precision training") with
@@ -890,8 +890,13 @@ inline uint32_t grid_for(uint64_t need) {
 //     6.33, 6.38 -> 6.43, 6.43
 // Between 2^26 and 2^28 the sizes differ by less than the spread between
 // processes; below 2^26 the gaps between launches cost more than the split
-// gains.  The accumulates gain nothing from it (2^30 and 2^32 elements: 6.33
-// TB/s in one launch, 6.28-6.34 in pieces of 2^27 or 2^28) and stay one launch.
+// gains.  Pieces of exactly 2^27 beat equal pieces of another size (1.5e9 BF16,
+// three processes: 6.28 TB/s in 2^27-element launches, 6.22 in twelve equal
+// ones), and a shard of less than two pieces runs best in one launch (137.7M
+// FP16, three processes: 6.09 / 6.00 / 6.01 in one, 6.07 / 5.97 / 5.98 as
+// 2^27 + the rest).  The accumulates gain nothing from it (2^30 and 2^32
+// elements: 6.33 TB/s in one launch, 6.28-6.34 in pieces of 2^27 or 2^28) and
+// stay one launch.
 constexpr uint64_t kStepPiece = 1ull << 27;
 
 // Consecutive ranges of at most piece_tiles whole tiles of a shard, each
@@ -914,12 +919,14 @@ hipError_t by_pieces(uint64_t count, uint32_t head, uint64_t n_tiles, uint64_t t
     return hipSuccess;
 }
 
-// Whole tiles per launch: the thread's override, else the kernel's rule
-// (0: one launch).
-inline uint64_t piece_tiles(uint64_t rule, uint64_t tile, const DeviceProps &dev) {
-    const uint64_t elems = dev.piece != 0 ? dev.piece : rule;
-    if (elems == 0) return 0;
-    return elems < tile ? 1 : elems / tile;
+// Whole tiles per launch of a shard of n_tiles tiles: the thread's override
+// as it stands, else the kernel's rule (0: one launch), which splits only a
+// shard that holds at least two whole pieces.
+inline uint64_t piece_tiles(uint64_t rule, uint64_t tile, uint64_t n_tiles,
+                            const DeviceProps &dev) {
+    if (dev.piece != 0) return dev.piece < tile ? 1 : dev.piece / tile;
+    const uint64_t per = rule / tile;
+    return per != 0 && n_tiles >= 2 * per ? per : 0;
 }
 
 template <int DT, typename GT, int MODE>
@@ -937,7 +944,7 @@ hipError_t adam_launch(uint16_t *w16, const GT *g, float *master, float *m, floa
     const uint64_t n_tiles = (count - head) / kTile;
     const size_t lds = step_lds_bytes(dev);
     return by_pieces(
-        count, head, n_tiles, kTile, piece_tiles(kStepPiece, kTile, dev),
+        count, head, n_tiles, kTile, piece_tiles(kStepPiece, kTile, n_tiles, dev),
         [&](uint64_t off, uint64_t cnt, uint32_t h, uint64_t nt) {
             const uint64_t r = cnt - h - nt * kTile;
             const uint64_t need = nt > 0 ? nt : (r + kThreads - 1) / kThreads;
@@ -977,7 +984,7 @@ hipError_t accumulate_dispatch(float *acc, const uint16_t *g16, uint64_t count,
     const uint64_t n_tiles = (count - head) / kTile;
     const size_t lds = accumulate_lds_bytes(count, FIRST, CHECK, dev);
     return by_pieces(
-        count, head, n_tiles, kTile, piece_tiles(0, kTile, dev),
+        count, head, n_tiles, kTile, piece_tiles(0, kTile, n_tiles, dev),
         [&](uint64_t off, uint64_t cnt, uint32_t h, uint64_t nt) {
             const uint64_t r = cnt - h - nt * kTile;
             const uint64_t need = nt > 0 ? nt : (r + kThreads - 1) / kThreads;
