@@ -877,10 +877,11 @@ inline uint32_t grid_for(uint64_t need) {
     return static_cast<uint32_t>(need < cap ? need : cap);
 }
 
-// Elements per launch of the step.  A long shard goes out as launches of at
-// most this many elements, back to back on one stream, which ran faster than
-// one launch over the whole shard at every size past it (MI355X, the arrays
-// of one process timed under every setting in turn, median TB/s):
+// Elements per launch of the step.  A shard of two or more such pieces goes
+// out as launches of at most this many elements, back to back on one stream,
+// which ran faster than one launch over the whole shard at every such size
+// (MI355X, the arrays of one process timed under every setting in turn,
+// median TB/s):
 //   1e10 FP16, three processes, one launch / 2^28 / 2^27 / 2^26 / 2^25 / 2^24:
 //     6.33 / 6.44 / 6.44 / 6.41 / 6.34 / 6.18;  6.32 / 6.42 / 6.41 / 6.38 /
 //     6.31 / 6.16;  6.25 / 6.36 / 6.35 / 6.31 / 6.23 / 6.08
