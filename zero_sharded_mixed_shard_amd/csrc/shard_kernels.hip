@@ -12,7 +12,8 @@
 // kernels is non-temporal (the data is touched once), and the step launches
 // one block per tile (a grid-stride loop only past 2^23 tiles): both measured
 // faster on MI355X than a resident grid looping over tiles.  A shard of at
-// least 2^28 elements steps in consecutive launches of 2^27 (kStepPiece).
+// least 2^28 elements steps (and accumulates its last micro-batch with the
+// fused check) in consecutive launches of 2^27 (kStepPiece).
 //
 // Numerics follow the update of "Training models too big for one GPU: ZeRO &
 // FSDP" ("Adam, and why it's expensive", "Mixed-precision training") with
@@ -895,9 +896,13 @@ inline uint32_t grid_for(uint64_t need) {
 // three processes: 6.28 TB/s in 2^27-element launches, 6.22 in twelve equal
 // ones), and a shard of less than two pieces runs best in one launch (137.7M
 // FP16, three processes: 6.09 / 6.00 / 6.01 in one, 6.07 / 5.97 / 5.98 as
-// 2^27 + the rest).  The accumulates gain nothing from it (2^30 and 2^32
-// elements: 6.33 TB/s in one launch, 6.28-6.34 in pieces of 2^27 or 2^28) and
-// stay one launch.
+// 2^27 + the rest).
+//   The accumulate with the fused check (a later micro-batch) gains as well,
+// two processes each, one launch against 2^27: 2^30 6.16, 6.18 -> 6.22, 6.24;
+// 2^32 6.26, 6.27 -> 6.31, 6.30; 2^33 6.19, 6.05 -> 6.25, 6.13.  The plain
+// accumulate does not (2^30 6.35, 6.37 -> 6.35, 6.34; 2^33 6.34, 6.34 -> 6.34,
+// 6.33) and the first micro-batch loses (2^30 6.41, 6.45 -> 6.38, 6.38; 2^33
+// 6.50, 6.51 -> 6.44, 6.44), so those stay one launch.
 constexpr uint64_t kStepPiece = 1ull << 27;
 
 // Consecutive ranges of at most piece_tiles whole tiles of a shard, each
@@ -985,7 +990,8 @@ hipError_t accumulate_dispatch(float *acc, const uint16_t *g16, uint64_t count,
     const uint64_t n_tiles = (count - head) / kTile;
     const size_t lds = accumulate_lds_bytes(count, FIRST, CHECK, dev);
     return by_pieces(
-        count, head, n_tiles, kTile, piece_tiles(0, kTile, n_tiles, dev),
+        count, head, n_tiles, kTile,
+        piece_tiles(CHECK && !FIRST ? kStepPiece : 0, kTile, n_tiles, dev),
         [&](uint64_t off, uint64_t cnt, uint32_t h, uint64_t nt) {
             const uint64_t r = cnt - h - nt * kTile;
             const uint64_t need = nt > 0 ? nt : (r + kThreads - 1) / kThreads;
