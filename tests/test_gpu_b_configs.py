@@ -315,7 +315,9 @@ def test_c4_ten_billion_unsharded_windows():
     psi = w.psi
     hp, S = hp_of(w), w.loss_scale
     free, total = torch.cuda.mem_get_info(DEV)
-    need = psi * 20 + (1 << 30)     # the five arrays and a copy of the starting master
+    need = psi * 16 + (1 << 30)
+    # a copy of the starting master for the every-element check of the first step
+    full_check = free >= need + psi * 4
     if free < need:
         pytest.skip(f"needs {need / 1e9:.0f} GB of device memory, {free / 1e9:.0f} GB free")
     log(f"C4 allocating 160 GB ({free / 1e9:.0f} GB free)")
@@ -332,13 +334,15 @@ def test_c4_ten_billion_unsharded_windows():
     gw = take(g16, wins, u16)
     flag = flag_buf()
     steps = list(range(1, w.steps + 1))
-    master0 = master.clone()
+    master0 = master.clone() if full_check else None
+    if not full_check:
+        log(f"  C4: {free / 1e9:.0f} GB free, too little for the every-element check; windows only")
     for t in steps:
         zs.zero_overflow_check(g16, psi, 1, 0, S, flag)
         zs.zero_adam_step(w16, g16, master, m, v, psi, 1, 0, step=t, loss_scale=S,
                           found_inf=flag, **hp)
         log(f"  step {t} enqueued")
-        if t == 1:   # the first step at every element, in the launch shape bench.py times
+        if t == 1 and full_check:   # the first step at every element, as bench.py launches it
             torch.cuda.synchronize()
             assert flag.item() == 0
             every_element_vs_oracle(g16, dict(master=master0, m=None, v=None),
