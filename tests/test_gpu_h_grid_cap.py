@@ -124,6 +124,24 @@ def test_step_g32_and_accumulate_in_pieces(piece):
     g32_and_accumulate_case(f"piece={piece}", piece % 97)
 
 
+def test_pieces_with_a_lowered_grid_cap():
+    # both overrides at once: launches of seven tiles, each walked by three
+    # blocks in turn (the tile loop inside every piece)
+    zs.zero_set_launch_piece(7 * 2048)
+    zs.zero_set_grid_cap(3)
+    try:
+        for dtype in ("f16", "bf16"):
+            for count in COUNTS:
+                run_case(count, dtype, dict.fromkeys(("g16", "w16", "master", "m", "v"), 3),
+                         steps=2, seed=count + 11)
+        g32_and_accumulate_case("piece=7 tiles, cap=3", 13)
+    finally:
+        torch.cuda.synchronize()
+        zs.zero_set_grid_cap(0)
+        zs.zero_set_launch_piece(0)
+    log("pieces of seven tiles under a grid cap of three blocks: within the bar")
+
+
 def test_flag_tile_loop(cap):
     count = 200_003
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
