@@ -3,7 +3,8 @@ UndefinedBehaviorSanitizer, on the CPU.
 
 Two drivers in tests/sanitize/ call every oracle function and every host-only
 entry point (layout, loss-scale decision, accounting, sharded checkpoints) on
-heap buffers of exactly the sizes the calls may touch.  They are built with
+heap buffers of exactly the sizes the calls may touch; a third runs the
+launchers' plan that cuts a long shard into consecutive launches (launch.h).  They are built with
 gcc/g++ and the sanitizers, so a read or write past an end, a use after free,
 a leak or undefined arithmetic aborts the run; the drivers also check the
 documented results and error codes.  The kernels' host wrappers (api.cpp)
@@ -54,3 +55,16 @@ def test_host_code_under_sanitizers(tmp_path):
     scratch = tmp_path / "files"
     scratch.mkdir()
     _run([exe, scratch])
+
+
+def test_launch_plan_under_sanitizers(tmp_path):
+    # by_pieces / piece_tiles from launch.h, host-only code that needs the HIP
+    # headers for its types but no GPU and no HIP runtime
+    inc = "/opt/rocm/include"
+    if not os.path.exists(os.path.join(inc, "hip", "hip_runtime_api.h")):
+        pytest.skip("HIP headers not found")
+    exe = tmp_path / "launch_plan_driver"
+    _build("g++", ["-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I", inc, "-I",
+                   os.path.join(ROOT, "include"), "-I", CSRC,
+                   os.path.join(HERE, "launch_plan_driver.cpp")], exe)
+    _run([exe])

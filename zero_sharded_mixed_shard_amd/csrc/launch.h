@@ -83,6 +83,37 @@ inline int per_cu_or(int rule, const DeviceProps &dev) {
     return dev.occupancy != 0 ? dev.occupancy : rule;
 }
 
+// Consecutive ranges of at most piece_tiles whole tiles of a shard, each
+// enqueued by launch(offset, count, head, n_tiles) over the views advanced by
+// offset elements: the first range keeps the shard's head, the last one its
+// ragged rest, and every later range starts head + a multiple of the tile in,
+// so it keeps the shard's alignment.  piece_tiles == 0, or a shard of at most
+// piece_tiles tiles: one launch over everything.  Stops at the first error.
+template <typename F>
+hipError_t by_pieces(uint64_t count, uint32_t head, uint64_t n_tiles, uint64_t tile,
+                     uint64_t piece_tiles, F &&launch) {
+    if (piece_tiles == 0 || n_tiles <= piece_tiles) return launch(0, count, head, n_tiles);
+    for (uint64_t t0 = 0; t0 < n_tiles; t0 += piece_tiles) {
+        const uint64_t nt = n_tiles - t0 < piece_tiles ? n_tiles - t0 : piece_tiles;
+        const uint64_t off = t0 == 0 ? 0 : head + t0 * tile;
+        const uint32_t h = t0 == 0 ? head : 0;
+        const uint64_t cnt = t0 + nt == n_tiles ? count - off : h + nt * tile;
+        const hipError_t e = launch(off, cnt, h, nt);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Whole tiles per launch of a shard of n_tiles tiles: the thread's override
+// as it stands, else the kernel's rule (elements per piece; 0: one launch),
+// which splits only a shard that holds at least two whole pieces.
+inline uint64_t piece_tiles(uint64_t rule, uint64_t tile, uint64_t n_tiles,
+                            const DeviceProps &dev) {
+    if (dev.piece != 0) return dev.piece < tile ? 1 : dev.piece / tile;
+    const uint64_t per = rule / tile;
+    return per != 0 && n_tiles >= 2 * per ? per : 0;
+}
+
 // Enqueue the Adam step over `count` elements of five shard views.  The
 // caller has validated every argument; count > 0.  flag (nullable): skip if
 // set.  ctl (nullable): skip unless ctl->apply, and take S, bc1, bc2 from it.
