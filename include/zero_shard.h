@@ -483,7 +483,8 @@ typedef struct {
  * The file is written as path + ".tmp", flushed to the device and renamed
  * over path, so a reader finds either the previous file or the complete new
  * one; the directory is then flushed too where the file system allows it.
- * On failure the temporary file is removed.
+ * On failure the temporary file is removed.  Two writers of the same path at
+ * once share that temporary name and race: give each rank its own path.
  *   w16, master, m, v  HOST arrays of count elements.
  *   Errors: ZERO_EINVAL (bad layout, NULL pointers), ZERO_EDTYPE, ZERO_EIO.
  */
@@ -500,9 +501,12 @@ int zero_ckpt_verify(const char *path);
 
 /*
  * zero_ckpt_read -- elements [first, first + count) of a shard file's arrays
- * into HOST arrays (w16: 2-byte elements; master, m, v: FP32).  Errors:
- * ZERO_EINVAL for a range outside the shard or NULL pointers with count > 0;
- * ZERO_EIO; ZERO_ECORRUPT for a bad header or size.
+ * into HOST arrays (w16: 2-byte elements; master, m, v: FP32).  It checks the
+ * header and the file size but not the payload hash, so that a range can be
+ * read without reading the whole file: call zero_ckpt_verify first to detect
+ * changed payload bytes (zero_ckpt_read_resharded does).  Errors: ZERO_EINVAL
+ * for a range outside the shard or NULL pointers with count > 0; ZERO_EIO;
+ * ZERO_ECORRUPT for a bad header or size.
  */
 int zero_ckpt_read(const char *path, uint64_t first, uint64_t count, void *w16, float *master,
                    float *m, float *v);
