@@ -1,7 +1,9 @@
 """Seeded random parity sweep: check -> decision -> step against the oracle.
 
-Each case draws a shard size (1 to ~300k elements, biased toward tile and
-line boundaries), view phases (all equal, or mixed: the element-wise kernel),
+Each case draws the elements per launch (half the cases the library's rule,
+the others random pieces of whole tiles), a shard size (1 to ~300k elements,
+biased toward tile and line boundaries), view phases (all equal, or mixed:
+the element-wise kernel),
 a 16-bit format, hyperparameters (including beta = 0, eps = 0, wd = 0 and
 negative lr), a loss scale (powers of two and not), a gradient spread from
 deep in the FP16 subnormal range to values that overflow after unscaling,
@@ -49,12 +51,33 @@ def draw_case(rng):
     return count, phases, dtype, hp, S, std, inject, steps
 
 
-def test_random_sweep_matches_oracle():
+def draw_piece(prng, count):
+    """Elements per launch for one case, from a generator of its own (so the cases
+    themselves are the same with or without it): half the cases the library's
+    rule, the others pieces of 1 to ~count/2048 tiles plus a remainder."""
+    if prng.random() < 0.5:
+        return 0
+    return int(prng.integers(1, count // 2048 + 2)) * 2048 + int(prng.integers(0, 2048))
+
+
+@pytest.fixture
+def launch_pieces():
+    yield
+    torch.cuda.synchronize()
+    zs.zero_set_launch_piece(0)
+
+
+def test_random_sweep_matches_oracle(launch_pieces):
     rng = np.random.default_rng(20261202)
-    stats = {"cases": 0, "skipped_steps": 0, "applied_steps": 0, "mixed_phase": 0}
+    prng = np.random.default_rng(31)
+    stats = {"cases": 0, "skipped_steps": 0, "applied_steps": 0, "mixed_phase": 0, "split": 0}
     worst = {k: [0, 0] for k in ("master", "m", "v", "w16")}   # max ulp, non-bitwise count
     for case in range(N_CASES):
         count, phases, dtype, hp, S, std, inject, steps = draw_case(rng)
+        piece = draw_piece(prng, count)
+        zs.zero_set_launch_piece(piece)
+        # split for sure: more whole tiles than a piece holds, whatever the head
+        stats["split"] += piece != 0 and max(0, count - 63) // 2048 > piece // 2048
         td = TD[dtype]
         V = {k: GuardedView(count, td if k in ("g16", "w16") else torch.float32, phases[k], DEV)
              for k in KEYS}
@@ -90,7 +113,7 @@ def test_random_sweep_matches_oracle():
         got = dict(master=f32(V["master"].view), m=f32(V["m"].view), v=f32(V["v"].view),
                    w16=u16(V["w16"].view))
         st = assert_close(got, ref, dtype, f"case {case}: count={count} phases={phases} {dtype} "
-                                           f"hp={hp} S={S} std={std:.3g}")
+                                           f"hp={hp} S={S} std={std:.3g} piece={piece}")
         for k, (mx, nz) in st.items():
             worst[k][0] = max(worst[k][0], mx)
             worst[k][1] += nz
@@ -99,12 +122,16 @@ def test_random_sweep_matches_oracle():
         stats["mixed_phase"] += len(set(phases.values())) > 1
     log(f"random sweep: {stats}; max ulp / non-bitwise elements {worst}")
     assert stats["skipped_steps"] > 0 and stats["applied_steps"] > 0 and stats["mixed_phase"] > 0
+    assert stats["split"] > 0
 
 
-def test_random_fp32_gradients_device_control_and_exchanges():
+def test_random_fp32_gradients_device_control_and_exchanges(launch_pieces):
     rng = np.random.default_rng(4242)
+    prng = np.random.default_rng(32)
     for case in range(120):
         count = int(rng.choice([1, 5, 1023, 2049, 4096 + 31, 70_001, 200_003]))
+        piece = draw_piece(prng, count)
+        zs.zero_set_launch_piece(piece)
         dtype = "f16" if case % 2 else "bf16"
         pa, pg = int(rng.integers(0, 8)), int(rng.integers(0, 8))
         S = float(rng.choice([1.0, 256.0, 3.0, 65536.0]))
@@ -121,7 +148,7 @@ def test_random_fp32_gradients_device_control_and_exchanges():
             zs.zero_grad_accumulate(acc.view, gv.view, count, 1, 0, first=(j == 0))
             oracle.grad_accumulate(ref_acc, u16(g), dtype, first=(j == 0))
         torch.cuda.synchronize()
-        assert np.array_equal(f32(acc.view).view(np.uint32), ref_acc.view(np.uint32)), case
+        assert np.array_equal(f32(acc.view).view(np.uint32), ref_acc.view(np.uint32)), (case, piece)
         flag = torch.zeros(1, dtype=torch.int32, device=DEV)
         ssq = torch.zeros(1, device=DEV)
         parts = torch.empty(zs.SUMSQ_PARTIALS, dtype=torch.float64, device=DEV)
@@ -145,7 +172,7 @@ def test_random_fp32_gradients_device_control_and_exchanges():
             torch.cuda.synchronize()
             got = dict(master=f32(V["master"].view), m=f32(V["m"].view), v=f32(V["v"].view),
                        w16=u16(V["w16"].view))
-            assert_close(got, ref, dtype, f"g32 case {case}")
+            assert_close(got, ref, dtype, f"g32 case {case} piece {piece}")
         # the exchanges over a random rank count and formats
         psi = int(rng.integers(1, 150_000))
         n = int(rng.integers(1, 17))
