@@ -41,7 +41,13 @@
  *     slower element-wise kernel gives the same results.
  *   - All device work is enqueued on `stream` (a hipStream_t; 0 = the null
  *     stream) of the current HIP device, and the call returns without
- *     synchronising.  Calls are thread-safe and stateless: the only mutable
+ *     synchronising.  A call may enqueue several kernel launches: the step
+ *     of a shard of 2^28 elements or more, for one, goes out as consecutive
+ *     launches of 2^27 elements (a HIP graph captured from it holds one node
+ *     per launch).  Argument errors are found before anything is enqueued;
+ *     if a launch itself fails (ZERO_EHIP), launches before it in the same
+ *     call may already be enqueued, and the arrays they write are then in
+ *     an unspecified state.  Calls are thread-safe and stateless: the only mutable
  *     state the library keeps between calls is a per-device cache of device
  *     properties (compute units, LDS sizes), written once with the values
  *     the runtime reports.  (zero_shard_tuning.h declares test and tuning
@@ -188,8 +194,8 @@ int zero_overflow_check_noalloc(const void *g16, zero_dtype dt, uint64_t psi, ui
  *   Errors: ZERO_EDTYPE for a bad dt; ZERO_EINVAL for bad layout arguments,
  *   step == 0, loss_scale not positive and finite, beta1 or beta2 outside
  *   [0, 1), eps negative or not finite, lr or weight_decay not finite, a
- *   NULL or misaligned array pointer with count > 0; ZERO_EHIP if the launch
- *   fails.  On error nothing has been enqueued.
+ *   NULL or misaligned array pointer with count > 0 (nothing enqueued);
+ *   ZERO_EHIP if a launch fails (see the note on launches above).
  */
 int zero_adam_step(void *w16, const void *g16, float *master, float *m, float *v, zero_dtype dt,
                    uint64_t psi, uint32_t n, uint32_t rank, float lr, float beta1, float beta2,
