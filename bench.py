@@ -397,8 +397,9 @@ def measure_extras(dev, n_elem: int = 1 << 30, reps: int = 5) -> dict:
     check 4, accumulate with the FP32 check fused 10, 16-bit check with the sum
     of squares 2 (S a power of two, and S = 3),
     FP32-gradient step 30, reduce of 8 FP16 replicas into FP16 18 (read
-    8 x 2, write 2), gather of 8 FP16 shards 4 (read 2, write 2), and the
-    device-controlled check + decision + step 30 (2 + 28)."""
+    8 x 2, write 2), the same reduce with the check of its chunk fused in 18,
+    the 16-bit check of that chunk alone 2, gather of 8 FP16 shards 4 (read 2,
+    write 2), and the device-controlled check + decision + step 30 (2 + 28)."""
     import torch
 
     import synth
@@ -468,6 +469,12 @@ def measure_extras(dev, n_elem: int = 1 << 30, reps: int = 5) -> dict:
     shard = torch.empty(lay.count, dtype=torch.float16, device=dev)
     record("reduce_shard_8x_f16", timed(lambda: zs.zero_reduce_shard(shard, reps16, n, ranks, 0)),
            lay.count, 2 * ranks + 2)
+    # the reduce with the overflow check of its chunk fused in: the reduce's 18 B per
+    # chunk element, in place of 18 + 2 for the reduce followed by the 16-bit check
+    record("reduce_shard_check_8x_f16", timed(lambda: zs.zero_reduce_shard_check(
+        shard, reps16, n, ranks, 0, 65536.0, flag)), lay.count, 2 * ranks + 2)
+    record("overflow_check_f16_chunk", timed(lambda: zs.zero_overflow_check(
+        shard, lay.count, 1, 0, 65536.0, flag)), lay.count, 2)
     shards = [r[:zs.zero_shard_layout(n, ranks, k).count].clone() for k, r in enumerate(reps16)]
     del reps16
     record("gather_shards_8x_f16", timed(lambda: zs.zero_gather_shards(w16, shards, n, ranks)),

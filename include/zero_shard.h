@@ -47,10 +47,10 @@
  *     per launch).  Argument errors are found before anything is enqueued;
  *     if a launch itself fails (ZERO_EHIP), launches before it in the same
  *     call may already be enqueued, and the arrays they write are then in
- *     an unspecified state.  Calls are thread-safe and stateless: the only mutable
- *     state the library keeps between calls is a per-device cache of device
- *     properties (compute units, LDS sizes), written once with the values
- *     the runtime reports.  (zero_shard_tuning.h declares test and tuning
+ *     an unspecified state.  Calls are thread-safe and stateless: the only
+ *     mutable state the library keeps between calls is a per-device cache of
+ *     device properties (compute units, LDS sizes), written once with the
+ *     values the runtime reports.  (zero_shard_tuning.h declares test and tuning
  *     overrides of launch shapes; they are per thread and change no result.)
  */
 #ifndef ZERO_SHARD_H_
@@ -310,6 +310,27 @@ int zero_reduce_shard(void *out, zero_dtype out_dt, const void *const *replicas,
                       zero_dtype in_dt, uint64_t psi, uint32_t n, uint32_t rank, void *stream);
 
 /*
+ * zero_reduce_shard_check -- zero_reduce_shard with the unscale + overflow
+ * check of its result fused in ("Training models too big for one GPU: ZeRO &
+ * FSDP", "Data parallelism and the all-reduce": each rank's chunk is the sum
+ * over ranks; "Mixed-precision training": the gradients are divided by S and
+ * the step is skipped if any is inf or NaN).  The reduced chunk is the one
+ * zero_reduce_shard writes, bit for bit, and *d_found_inf becomes 1 iff some
+ * written out[i] / loss_scale is not finite, else 0: the flag that
+ * zero_overflow_check (16-bit out_dt) or zero_overflow_check_g32 (FP32) would
+ * give on out, without reading it again.  For a ZeRO-2/3 rank whose
+ * gradients arrive by a reduce-scatter.
+ *   loss_scale   S > 0, finite.
+ *   d_found_inf  device int32, written (cleared first, also for an empty
+ *                rank); it may not overlap out or a replica's chunk.
+ *   Errors: those of zero_reduce_shard, and ZERO_EINVAL for a bad loss_scale
+ *   or a NULL, misaligned or overlapping d_found_inf.
+ */
+int zero_reduce_shard_check(void *out, zero_dtype out_dt, const void *const *replicas,
+                            zero_dtype in_dt, uint64_t psi, uint32_t n, uint32_t rank,
+                            float loss_scale, int32_t *d_found_inf, void *stream);
+
+/*
  * zero_gather_shards -- full[k*S + i] = shard_k[i] for every rank k < n and
  * i < count(k): the flat buffer from its n shards.  Elements of full at
  * psi and beyond (the padding) are not written.
@@ -455,6 +476,16 @@ int zero_adam_step_g32_dev(void *w16, const float *g32, float *master, float *m,
 int zero_grad_accumulate_check_dev(float *acc, const void *g16, zero_dtype dt, uint64_t psi,
                                    uint32_t n, uint32_t rank, int32_t first,
                                    zero_device_ctl *d_ctl, void *stream);
+
+/*
+ * zero_reduce_shard_check_dev -- zero_reduce_shard_check with S read from
+ * d_ctl->scaler.loss_scale and the flag written to d_ctl->found_inf, for the
+ * device-resident sequence (zero_scaler_update_dev and zero_adam_step_dev
+ * follow).  d_ctl may not overlap out or a replica's chunk.
+ */
+int zero_reduce_shard_check_dev(void *out, zero_dtype out_dt, const void *const *replicas,
+                                zero_dtype in_dt, uint64_t psi, uint32_t n, uint32_t rank,
+                                zero_device_ctl *d_ctl, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Sharded checkpoints: each rank writes its own slice of the model states to

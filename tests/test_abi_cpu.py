@@ -483,6 +483,31 @@ def test_adam_step_rejects_overlapping_views(ptrs):
     assert adam(psi=400, n=4, rank=0, ptrs=ptrs) == -1
 
 
+def test_reduce_check_argument_errors():
+    # psi = 400 over 4 ranks: rank 0's chunk is 100 elements (200 bytes of FP16)
+    L = zs.lib
+    reps = (ctypes.c_void_p * 4)(FAKE * 4, FAKE * 8, FAKE * 4, FAKE * 8)   # may repeat
+    out, flag = FAKE * 12, FAKE * 16
+    # the reduce's own errors come first
+    assert L.zero_reduce_shard_check(out, 5, reps, 0, 400, 4, 0, 1.0, flag, None) == -2
+    assert L.zero_reduce_shard_check(None, 0, reps, 0, 400, 4, 0, 1.0, flag, None) == -1
+    assert L.zero_reduce_shard_check(out, 0, reps, 0, 400, 4, 4, 1.0, flag, None) == -1
+    # the loss scale
+    for S in (0.0, -1.0, float("inf"), float("nan")):
+        assert L.zero_reduce_shard_check(out, 0, reps, 0, 400, 4, 0, S, flag, None) == -1
+    # the flag: NULL, misaligned, inside the output, inside a replica's chunk
+    assert L.zero_reduce_shard_check(out, 0, reps, 0, 400, 4, 0, 1.0, None, None) == -1
+    assert L.zero_reduce_shard_check(out, 0, reps, 0, 400, 4, 0, 1.0, flag + 2, None) == -1
+    assert L.zero_reduce_shard_check(out, 0, reps, 0, 400, 4, 0, 1.0, out + 196, None) == -1
+    assert L.zero_reduce_shard_check(out, 0, reps, 0, 400, 4, 0, 1.0, FAKE * 8 + 100,
+                                     None) == -1
+    # the control block of the device-resident form: NULL, misaligned, over the output
+    assert L.zero_reduce_shard_check_dev(out, 0, reps, 0, 400, 4, 0, None, None) == -1
+    assert L.zero_reduce_shard_check_dev(out, 0, reps, 0, 400, 4, 0, flag + 4, None) == -1
+    assert L.zero_reduce_shard_check_dev(out, 0, reps, 0, 400, 4, 0, out, None) == -1
+    assert L.zero_reduce_shard_check_dev(out, 0, reps, 0, 400, 4, 0, FAKE * 4 + 64, None) == -1
+
+
 def test_overlap_checks_of_accumulate_reduce_and_gather():
     # accumulate: acc (FP32) over the gradients
     assert zs.lib.zero_grad_accumulate(FAKE, FAKE + 200, 0, 400, 4, 0, 0, None) == -1
@@ -520,6 +545,8 @@ def test_binding_rejects_host_tensors_before_any_device_call():
         lambda: zs.zero_adam_step_dev(h16, h16.clone(), h32, h32.clone(), h32.clone(), n, 1, 0,
                                       ctl=ctl, **hp),
         lambda: zs.zero_reduce_shard(h16[:32], [h16, h16.clone()], n, 2, 0),
+        lambda: zs.zero_reduce_shard_check(h16[:32], [h16, h16.clone()], n, 2, 0, 1.0, flag),
+        lambda: zs.zero_reduce_shard_check_dev(h16[:32], [h16, h16.clone()], n, 2, 0, ctl),
         lambda: zs.zero_gather_shards(h16, [h16[:32].clone(), h16[:32].clone()], n, 2),
     ]
     for i, call in enumerate(calls):

@@ -86,6 +86,8 @@ from ._binding import (  # noqa: F401
     zero_overflow_check_g32_dev,
     zero_peak_memory,
     zero_reduce_shard,
+    zero_reduce_shard_check,
+    zero_reduce_shard_check_dev,
     zero_reshard_plan,
     zero_scaler_update,
     zero_scaler_update_dev,
@@ -121,6 +123,8 @@ __all__ = [
     "zero_overflow_check_g32_dev",
     "zero_adam_step_g32_dev",
     "zero_reduce_shard",
+    "zero_reduce_shard_check",
+    "zero_reduce_shard_check_dev",
     "zero_gather_shards",
     "zero_comm_volume",
     "zero_peak_memory",

@@ -100,6 +100,10 @@ lib.zero_adam_step_g32.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _u64, _u32, _u
 lib.zero_adam_step_g32.restype = _i32
 lib.zero_reduce_shard.argtypes = [_vp, _i32, _vp, _i32, _u64, _u32, _u32, _vp]
 lib.zero_reduce_shard.restype = _i32
+lib.zero_reduce_shard_check.argtypes = [_vp, _i32, _vp, _i32, _u64, _u32, _u32, _f32, _vp, _vp]
+lib.zero_reduce_shard_check.restype = _i32
+lib.zero_reduce_shard_check_dev.argtypes = [_vp, _i32, _vp, _i32, _u64, _u32, _u32, _vp, _vp]
+lib.zero_reduce_shard_check_dev.restype = _i32
 lib.zero_gather_shards.argtypes = [_vp, _vp, _i32, _u64, _u32, _vp]
 lib.zero_gather_shards.restype = _i32
 
@@ -569,6 +573,46 @@ def zero_reduce_shard(out: torch.Tensor, replicas, psi: int, n: int, rank: int,
                                    _FORMATS[in_dt], psi, n, rank, _stream_handle(stream, dev))
     if rc != 0:
         raise ZeroError(rc, "zero_reduce_shard")
+
+
+def _reduce_views(out, replicas, psi, n, rank):
+    lay = zero_shard_layout(psi, n, rank)
+    dev = out.device
+    if len(replicas) != n:
+        raise ValueError(f"need {n} replicas, got {len(replicas)}")
+    in_dt = replicas[0].dtype
+    for k, r in enumerate(replicas):
+        _view(r, f"replica {k}", (in_dt,), psi, dev)
+    if in_dt not in _FORMATS:
+        raise TypeError(f"replica dtype {in_dt} not supported")
+    p_out = _view(out, "out", tuple(_FORMATS), lay.count, dev)
+    return dev, in_dt, p_out
+
+
+def zero_reduce_shard_check(out: torch.Tensor, replicas, psi: int, n: int, rank: int,
+                            loss_scale: float, found_inf: torch.Tensor, stream=None) -> None:
+    """zero_reduce_shard with the overflow check of the written chunk fused in: found_inf
+    becomes 1 iff some out[i] / loss_scale is not finite."""
+    dev, in_dt, p_out = _reduce_views(out, replicas, psi, n, rank)
+    p_f = _view(found_inf, "found_inf", (torch.int32,), 1, dev)
+    with torch.cuda.device(dev):
+        rc = lib.zero_reduce_shard_check(p_out, _FORMATS[out.dtype], _ptr_list(replicas),
+                                         _FORMATS[in_dt], psi, n, rank, loss_scale, p_f,
+                                         _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_reduce_shard_check")
+
+
+def zero_reduce_shard_check_dev(out: torch.Tensor, replicas, psi: int, n: int, rank: int,
+                                ctl: torch.Tensor, stream=None) -> None:
+    """zero_reduce_shard_check with S read from, and the flag written to, the control block."""
+    dev, in_dt, p_out = _reduce_views(out, replicas, psi, n, rank)
+    with torch.cuda.device(dev):
+        rc = lib.zero_reduce_shard_check_dev(p_out, _FORMATS[out.dtype], _ptr_list(replicas),
+                                             _FORMATS[in_dt], psi, n, rank, _ctl_ptr(ctl, dev),
+                                             _stream_handle(stream, dev))
+    if rc != 0:
+        raise ZeroError(rc, "zero_reduce_shard_check_dev")
 
 
 def zero_gather_shards(full: torch.Tensor, shards, psi: int, n: int, stream=None) -> None:

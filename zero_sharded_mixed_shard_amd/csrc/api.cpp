@@ -375,35 +375,107 @@ extern "C" int zero_adam_step_g32(void *w16, const float *g32, float *master, fl
     return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_adam_step_g32 launch");
 }
 
-extern "C" int zero_reduce_shard(void *out, zero_dtype out_dt, const void *const *replicas,
-                                 zero_dtype in_dt, uint64_t psi, uint32_t n, uint32_t rank,
-                                 void *stream) {
+namespace {
+
+// Checks shared by the reduce and the reduce with the fused check: formats,
+// layout, pointers, and that the output overlaps no replica's chunk unless it
+// is exactly one of them in the same format (in place: each element is
+// written after every replica's element was read).  Fills the replica views
+// advanced to the rank's first element, the count and the byte spans of the
+// views (for the flag's overlap test).
+int reduce_args(void *out, zero_dtype out_dt, const void *const *replicas, zero_dtype in_dt,
+                uint64_t psi, uint32_t n, uint32_t rank, zs::ReplicaSet *set, uint64_t *count,
+                uint64_t *out_bytes, uint64_t *in_bytes) {
     const auto fmt_ok = [](zero_dtype d) { return d == ZERO_F16 || d == ZERO_BF16 || d == ZERO_F32; };
     if (!fmt_ok(out_dt) || !fmt_ok(in_dt)) return ZERO_EDTYPE;
     zero_layout lay;
     if (zero_shard_layout(psi, n, rank, &lay) != ZERO_OK) return ZERO_EINVAL;
     if (n > zs::kMaxLocalRanks) return ZERO_EINVAL;
-    if (lay.count == 0) return ZERO_OK;
+    *count = lay.count;
     const uintptr_t in_b = in_dt == ZERO_F32 ? 4 : 2, out_b = out_dt == ZERO_F32 ? 4 : 2;
+    *out_bytes = out_b * lay.count;
+    *in_bytes = in_b * lay.count;
+    if (lay.count == 0) return ZERO_OK;
     if (out == nullptr || !aligned(out, out_b) || replicas == nullptr) return ZERO_EINVAL;
-    zs::ReplicaSet set;
     for (uint32_t k = 0; k < n; ++k) {
         if (replicas[k] == nullptr || !aligned(replicas[k], in_b)) return ZERO_EINVAL;
-        set.p[k] = static_cast<const char *>(replicas[k]) + lay.offset * in_b;
-        // the output may be exactly a replica's chunk in the same format (in place:
-        // each element is written after every replica's element was read) but may
-        // not overlap one otherwise; replicas may repeat one another
-        const bool in_place = out == set.p[k] && out_b == in_b;
-        if (!in_place && overlap(out, out_b * lay.count, set.p[k], in_b * lay.count))
-            return ZERO_EINVAL;
+        set->p[k] = static_cast<const char *>(replicas[k]) + lay.offset * in_b;
+        // replicas may repeat one another (read-only)
+        const bool in_place = out == set->p[k] && out_b == in_b;
+        if (!in_place && overlap(out, *out_bytes, set->p[k], *in_bytes)) return ZERO_EINVAL;
     }
+    return ZERO_OK;
+}
+
+// The flag of the fused check may share no byte with the output or a replica's chunk.
+bool flag_clear_of(const int32_t *flag, uint64_t flag_bytes, const void *out, uint64_t out_bytes,
+                   const zs::ReplicaSet &set, uint32_t n, uint64_t in_bytes, uint64_t count) {
+    if (count == 0) return true;
+    if (overlap(flag, flag_bytes, out, out_bytes)) return false;
+    for (uint32_t k = 0; k < n; ++k)
+        if (overlap(flag, flag_bytes, set.p[k], in_bytes)) return false;
+    return true;
+}
+
+int reduce_launch(void *out, zero_dtype out_dt, const zs::ReplicaSet &set, zero_dtype in_dt,
+                  uint32_t n, uint64_t count, const zs::ReduceCheck &chk, void *stream,
+                  const char *what) {
     zs::DeviceProps dev;
     const int prc = device_props(&dev);
     if (prc != ZERO_OK) return prc;
     const hipError_t e = zs::launch_reduce_shard(out, static_cast<int>(out_dt), set,
-                                                 static_cast<int>(in_dt), n, lay.count, dev,
+                                                 static_cast<int>(in_dt), n, count, chk, dev,
                                                  static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ZERO_OK : fail_hip(e, "zero_reduce_shard launch");
+    return e == hipSuccess ? ZERO_OK : fail_hip(e, what);
+}
+
+}  // namespace
+
+extern "C" int zero_reduce_shard(void *out, zero_dtype out_dt, const void *const *replicas,
+                                 zero_dtype in_dt, uint64_t psi, uint32_t n, uint32_t rank,
+                                 void *stream) {
+    zs::ReplicaSet set;
+    uint64_t count = 0, out_bytes = 0, in_bytes = 0;
+    const int rc = reduce_args(out, out_dt, replicas, in_dt, psi, n, rank, &set, &count,
+                               &out_bytes, &in_bytes);
+    if (rc != ZERO_OK || count == 0) return rc;
+    return reduce_launch(out, out_dt, set, in_dt, n, count, zs::ReduceCheck{1.0f, nullptr, nullptr},
+                         stream, "zero_reduce_shard launch");
+}
+
+extern "C" int zero_reduce_shard_check(void *out, zero_dtype out_dt, const void *const *replicas,
+                                       zero_dtype in_dt, uint64_t psi, uint32_t n, uint32_t rank,
+                                       float loss_scale, int32_t *d_found_inf, void *stream) {
+    zs::ReplicaSet set;
+    uint64_t count = 0, out_bytes = 0, in_bytes = 0;
+    const int rc = reduce_args(out, out_dt, replicas, in_dt, psi, n, rank, &set, &count,
+                               &out_bytes, &in_bytes);
+    if (rc != ZERO_OK) return rc;
+    if (!(loss_scale > 0.0f) || !finite(loss_scale)) return ZERO_EINVAL;
+    if (d_found_inf == nullptr || !aligned(d_found_inf, 4)) return ZERO_EINVAL;
+    if (!flag_clear_of(d_found_inf, 4, out, out_bytes, set, n, in_bytes, count))
+        return ZERO_EINVAL;
+    return reduce_launch(out, out_dt, set, in_dt, n, count,
+                         zs::ReduceCheck{loss_scale, nullptr, d_found_inf}, stream,
+                         "zero_reduce_shard_check launch");
+}
+
+extern "C" int zero_reduce_shard_check_dev(void *out, zero_dtype out_dt,
+                                           const void *const *replicas, zero_dtype in_dt,
+                                           uint64_t psi, uint32_t n, uint32_t rank,
+                                           zero_device_ctl *d_ctl, void *stream) {
+    zs::ReplicaSet set;
+    uint64_t count = 0, out_bytes = 0, in_bytes = 0;
+    const int rc = reduce_args(out, out_dt, replicas, in_dt, psi, n, rank, &set, &count,
+                               &out_bytes, &in_bytes);
+    if (rc != ZERO_OK) return rc;
+    if (d_ctl == nullptr || !aligned(d_ctl, alignof(zero_device_ctl))) return ZERO_EINVAL;
+    if (!flag_clear_of(reinterpret_cast<const int32_t *>(d_ctl), sizeof(zero_device_ctl), out,
+                       out_bytes, set, n, in_bytes, count))
+        return ZERO_EINVAL;
+    return reduce_launch(out, out_dt, set, in_dt, n, count,
+                         zs::ReduceCheck{1.0f, &d_ctl->scaler.loss_scale, &d_ctl->found_inf},
+                         stream, "zero_reduce_shard_check_dev launch");
 }
 
 extern "C" int zero_gather_shards(void *full, const void *const *shards, zero_dtype dt,

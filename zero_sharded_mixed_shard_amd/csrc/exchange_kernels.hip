@@ -103,6 +103,30 @@ __device__ __forceinline__ void store_vec(typename Fmt<F>::T *p, const float v[K
     }
 }
 
+// Magnitude bits of the value a format stores for the FP32 sum s: the value
+// after rounding to the output format, as FP32 bits with the sign cleared.
+// Non-negative FP32 bit patterns order like the values, so the largest
+// magnitude a lane wrote is an integer maximum.
+template <int OUT>
+__device__ __forceinline__ uint32_t stored_magnitude(float s) {
+    return __builtin_bit_cast(uint32_t, to_f32<OUT>(from_f32<OUT>(s))) & 0x7fffffffu;
+}
+
+// The flag of the check over the written values, from a lane's largest
+// magnitude: some out[i] / S is not finite iff the largest finite |out[i]|
+// divided by S overflows or some out[i] is inf or NaN (a correctly rounded
+// division by S > 0 is monotone in |out[i]|).  Every lane of the wave calls it.
+__device__ __forceinline__ void raise_check_flag(uint32_t mx, const ReduceCheck &chk) {
+    const float S = chk.loss_scale_dev != nullptr ? *chk.loss_scale_dev : chk.loss_scale;
+    const uint32_t e = 0x7f800000u;
+    const uint32_t q = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, mx) / S);
+    const bool bad = mx >= e || (q & e) == e || !(S > 0.0f) ||
+                     (__builtin_bit_cast(uint32_t, S) & e) == e;
+    if (__any(bad)) {
+        if ((threadIdx.x & 63u) == 0) *chk.flag = 1;
+    }
+}
+
 // out[i] = sum over k < n of in_k[i] for i in [0, count), where in_k already
 // points at rank r's first element of replica k.  With n_vec > 0: vector q
 // covers elements head + q*K .. +K-1 (K = kPerVec<IN>), one 256-vector tile
@@ -110,49 +134,63 @@ __device__ __forceinline__ void store_vec(typename Fmt<F>::T *p, const float v[K
 // time.  With n_vec == 0 the whole grid walks every element.
 // out is not restrict-qualified: it may be one of the replicas' chunks (in
 // place); every lane reads all replicas at its elements before it writes them.
-template <int IN, int OUT>
+// With CHECK the kernel also raises chk.flag (cleared by a kernel launched
+// before it) iff some written out[i] / S is not finite: the overflow check of
+// the result, with no second pass over it.
+template <int IN, int OUT, bool CHECK>
 __global__ __launch_bounds__(kThreads) void reduce_shard_kernel(
     typename Fmt<OUT>::T *out, ReplicaSet in, uint32_t n, uint64_t count,
-    uint32_t head, uint64_t n_vec) {
+    uint32_t head, uint64_t n_vec, ReduceCheck chk) {
     using TI = typename Fmt<IN>::T;
     constexpr int K = kPerVec<IN>;
+    uint32_t mx = 0;   // largest magnitude written (CHECK)
+    auto note = [&](float s) {
+        if constexpr (CHECK) {
+            const uint32_t a = stored_magnitude<OUT>(s);
+            mx = a > mx ? a : mx;
+        }
+    };
     auto one = [&](uint64_t i) {
         float s = 0.0f;
         for (uint32_t k = 0; k < n; ++k) s = s + to_f32<IN>(static_cast<const TI *>(in.p[k])[i]);
         out[i] = from_f32<OUT>(s);
+        note(s);
     };
     if (n_vec == 0) {
         const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
         for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < count;
              i += stride)
             one(i);
-        return;
-    }
-    const uint64_t n_tiles = (n_vec + kThreads - 1) / kThreads;
-    for (uint64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-        const uint64_t q = t * kThreads + threadIdx.x;
-        if (q < n_vec) {
-            const uint64_t e = head + q * K;
-            float s[K];
+    } else {
+        const uint64_t n_tiles = (n_vec + kThreads - 1) / kThreads;
+        for (uint64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+            const uint64_t q = t * kThreads + threadIdx.x;
+            if (q < n_vec) {
+                const uint64_t e = head + q * K;
+                float s[K];
 #pragma unroll
-            for (int j = 0; j < K; ++j) s[j] = 0.0f;
-            // one replica at a time, in rank order: keeping several replicas' loads
-            // in flight per lane (4 or 8, with or without an occupancy cap) measured
-            // no better over sizes on MI355X -- nine streams at once are what limit it
-            for (uint32_t k = 0; k < n; ++k) {
-                float x[K];
-                widen<IN>(load_raw<IN>(static_cast<const TI *>(in.p[k]) + e), x);
+                for (int j = 0; j < K; ++j) s[j] = 0.0f;
+                // one replica at a time, in rank order: keeping several replicas' loads
+                // in flight per lane (4 or 8, with or without an occupancy cap) measured
+                // no better over sizes on MI355X -- nine streams at once are what limit it
+                for (uint32_t k = 0; k < n; ++k) {
+                    float x[K];
+                    widen<IN>(load_raw<IN>(static_cast<const TI *>(in.p[k]) + e), x);
 #pragma unroll
-                for (int j = 0; j < K; ++j) s[j] = s[j] + x[j];
+                    for (int j = 0; j < K; ++j) s[j] = s[j] + x[j];
+                }
+                store_vec<OUT, K>(out + e, s);
+#pragma unroll
+                for (int j = 0; j < K; ++j) note(s[j]);
             }
-            store_vec<OUT, K>(out + e, s);
+        }
+        if (blockIdx.x == 0) {
+            if (threadIdx.x < head) one(threadIdx.x);
+            const uint64_t tail = head + n_vec * K + threadIdx.x;
+            if (tail < count) one(tail);
         }
     }
-    if (blockIdx.x == 0) {
-        if (threadIdx.x < head) one(threadIdx.x);
-        const uint64_t tail = head + n_vec * K + threadIdx.x;
-        if (tail < count) one(tail);
-    }
+    if constexpr (CHECK) raise_check_flag(mx, chk);
 }
 
 // full[k*S + i] = shard_k[i] for i < count_k; blockIdx.y = k.  A shard whose
@@ -217,7 +255,7 @@ constexpr int kGatherPerCU = 8;
 
 template <int IN, int OUT>
 hipError_t reduce_dispatch(void *out, const ReplicaSet &in, uint32_t n, uint64_t count,
-                           const DeviceProps &dev, hipStream_t stream) {
+                           const ReduceCheck &chk, const DeviceProps &dev, hipStream_t stream) {
     constexpr uint32_t in_b = kBytes<IN>, out_b = kBytes<OUT>;
     constexpr uint32_t K = kPerVec<IN>;
     constexpr uint32_t out_align = K * out_b < kVecBytes ? K * out_b : kVecBytes;
@@ -229,19 +267,30 @@ hipError_t reduce_dispatch(void *out, const ReplicaSet &in, uint32_t n, uint64_t
         if ((addr(in.p[k]) + static_cast<uint64_t>(head) * in_b) % kVecBytes != 0) vec = false;
     const uint64_t n_vec = vec ? (count - head) / K : 0;
     if (n_vec == 0) head = 0;  // every element one at a time
-    reduce_shard_kernel<IN, OUT><<<blocks_for(n_vec > 0 ? n_vec : count), kThreads,
-                                   cap_lds_bytes(per_cu_or(kReducePerCU, dev), dev), stream>>>(
-        static_cast<typename Fmt<OUT>::T *>(out), in, n, count, head, n_vec);
+    const uint32_t blocks = blocks_for(n_vec > 0 ? n_vec : count);
+    const size_t lds = cap_lds_bytes(per_cu_or(kReducePerCU, dev), dev);
+    auto *o = static_cast<typename Fmt<OUT>::T *>(out);
+    if (chk.flag != nullptr)
+        reduce_shard_kernel<IN, OUT, true><<<blocks, kThreads, lds, stream>>>(o, in, n, count,
+                                                                             head, n_vec, chk);
+    else
+        reduce_shard_kernel<IN, OUT, false><<<blocks, kThreads, lds, stream>>>(o, in, n, count,
+                                                                              head, n_vec, chk);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_reduce_shard(void *out, int out_fmt, const ReplicaSet &in, int in_fmt,
-                               uint32_t n, uint64_t count, const DeviceProps &dev,
-                               hipStream_t stream) {
+                               uint32_t n, uint64_t count, const ReduceCheck &chk,
+                               const DeviceProps &dev, hipStream_t stream) {
+    if (chk.flag != nullptr) {
+        const hipError_t e = launch_clear_flag(chk.flag, stream);
+        if (e != hipSuccess || count == 0) return e;
+    }
 #define ZS_REDUCE(I, O) \
-    if (in_fmt == I && out_fmt == O) return reduce_dispatch<I, O>(out, in, n, count, dev, stream);
+    if (in_fmt == I && out_fmt == O) \
+        return reduce_dispatch<I, O>(out, in, n, count, chk, dev, stream);
     ZS_REDUCE(0, 0) ZS_REDUCE(0, 1) ZS_REDUCE(0, 2)
     ZS_REDUCE(1, 0) ZS_REDUCE(1, 1) ZS_REDUCE(1, 2)
     ZS_REDUCE(2, 0) ZS_REDUCE(2, 1) ZS_REDUCE(2, 2)

@@ -181,11 +181,24 @@ struct GatherSet {
     uint32_t vec[kMaxLocalRanks];         // filled by the launcher
 };
 
+// The overflow check fused into the reduce: with flag set, *flag is cleared
+// first (also when count == 0) and raised iff some written out[i] / S is not
+// finite.  flag == nullptr: the plain reduce.
+struct ReduceCheck {
+    float loss_scale;             // S, unless loss_scale_dev is set
+    const float *loss_scale_dev;  // S read on the device, or null
+    int32_t *flag;                // the flag, or null
+};
+
 // out[i] = FP32 sum over k < n of in.p[k][i], rounded to out_fmt (0 FP16,
-// 1 BF16, 2 FP32), i < count; count > 0.
+// 1 BF16, 2 FP32), i < count; count > 0 unless chk.flag is set.
 hipError_t launch_reduce_shard(void *out, int out_fmt, const ReplicaSet &in, int in_fmt,
-                               uint32_t n, uint64_t count, const DeviceProps &dev,
-                               hipStream_t stream);
+                               uint32_t n, uint64_t count, const ReduceCheck &chk,
+                               const DeviceProps &dev, hipStream_t stream);
+
+// Enqueue a one-lane kernel that sets *flag = 0 (a kernel rather than a memset,
+// so that a captured graph replays it correctly).
+hipError_t launch_clear_flag(int32_t *flag, hipStream_t stream);
 
 // full[k*shard + i] = set.p[k][i] for i < set.count[k], k < n.
 hipError_t launch_gather_shards(void *full, int elem_bytes, GatherSet &set, uint32_t n,

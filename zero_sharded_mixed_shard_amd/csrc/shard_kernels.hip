@@ -1047,6 +1047,11 @@ hipError_t launch_grad_accumulate(int dtype, float *acc, const uint16_t *g16, ui
                  : accumulate_dispatch<1, false, false>(acc, g16, count, none, dev, stream);
 }
 
+hipError_t launch_clear_flag(int32_t *flag, hipStream_t stream) {
+    check_init<<<1, 64, 0, stream>>>(flag, nullptr);
+    return hipGetLastError();
+}
+
 hipError_t launch_grad_accumulate_check(int dtype, float *acc, const uint16_t *g16,
                                         uint64_t count, bool first, float loss_scale,
                                         const float *loss_scale_dev, int32_t *flag,
