@@ -7,9 +7,10 @@
 * reduce-scatter then all-gather equals the all-reduce (the oracle's
   element-wise sum of the full replicas);
 * a whole data-parallel step on one GPU: the n replicas' gradients are
-  reduce-scattered, each rank checks and steps its shard, the 16-bit shards
-  are all-gathered, and the result equals the unsharded update of the summed
-  gradients, bit for bit.
+  reduce-scattered, each rank checks (separately, or fused into the
+  reduce-scatter) and steps its shard, the 16-bit shards are all-gathered,
+  and the result equals the unsharded update of the summed gradients, bit
+  for bit.
 """
 import numpy as np
 import pytest
@@ -98,11 +99,13 @@ def test_gather_and_identity_with_all_reduce(fmt):
     log(f"gather {fmt}: bitwise; RS + AG == AR")
 
 
-def test_data_parallel_step_on_one_gpu():
+@pytest.mark.parametrize("fused", [False, True])
+def test_data_parallel_step_on_one_gpu(fused):
     # ZeRO-2 step with n = 8 simulated ranks on one GPU: 16-bit gradients of
     # 8 replicas -> reduce-scatter (FP16 out, the sum carries 8x the loss
     # scale) -> per-rank check + step on its shard -> all-gather of the 16-bit
-    # weights.  Equals the unsharded step on the all-reduced gradients.
+    # weights.  Equals the unsharded step on the all-reduced gradients.  fused:
+    # the check rides on the reduce-scatter (zero_reduce_shard_check).
     psi, n = 1_000_003, 8
     S = 1024.0 * n        # loss scale times n: the reduce leaves the SUM (R-11)
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
@@ -124,8 +127,11 @@ def test_data_parallel_step_on_one_gpu():
         reps = make_replicas(psi, n, "f16", 5000 + 10 * t, std=1e-3 * 1024)
         for k in range(n):
             sh = shards[k]
-            zs.zero_reduce_shard(sh["g"], reps, psi, n, k)
-            zs.zero_overflow_check(sh["g"], psi, n, k, S, flag)
+            if fused:
+                zs.zero_reduce_shard_check(sh["g"], reps, psi, n, k, S, flag)
+            else:
+                zs.zero_reduce_shard(sh["g"], reps, psi, n, k)
+                zs.zero_overflow_check(sh["g"], psi, n, k, S, flag)
             zs.zero_adam_step(sh["w"], sh["g"], sh["master"], sh["m"], sh["v"], psi, n, k,
                               step=t, loss_scale=S, found_inf=flag, **hp)
         zs.zero_gather_shards(full_w, [sh["w"] for sh in shards], psi, n)
@@ -139,7 +145,7 @@ def test_data_parallel_step_on_one_gpu():
     got = dict(master=np.concatenate([f32(sh["master"]) for sh in shards]),
                m=np.concatenate([f32(sh["m"]) for sh in shards]),
                v=np.concatenate([f32(sh["v"]) for sh in shards]), w16=u16(full_w))
-    log("  RS -> step -> AG", assert_close(got, ref, "f16", "dp step"))
+    log(f"  RS -> step -> AG (check fused: {fused})", assert_close(got, ref, "f16", "dp step"))
 
 
 def sum_f32(arrays):
