@@ -7,8 +7,10 @@ check of 16-bit gradients; FP32 output: the check of FP32 gradients), for
 every pair of formats, ragged sizes, misaligned and mismatched views, planted
 inf and NaN at head, vector and tail positions, sums that overflow the output
 format, quotients that overflow FP32, an empty rank (the flag is still
-cleared), an in-place reduce, the tile loops of a lowered grid cap, and the
-device-resident form that reads S from the control block.
+cleared), an in-place reduce, the tile loops of a lowered grid cap, the
+device-resident form that reads S from the control block, and a ZeRO-2 rank's
+whole device-resident step (this reduce, the decision, the step) captured in a
+HIP graph and replayed.
 """
 import numpy as np
 import pytest
@@ -158,3 +160,56 @@ def test_reduce_check_device_control():
     c = zs.device_ctl_read(ctl)
     assert c.found_inf == 1 and c.apply == 0 and c.scaler.loss_scale == 512.0
     log("reduce+check under device control: flags equal, the decision skips on the NaN")
+
+
+def test_reduce_check_step_captured_in_a_graph():
+    # a ZeRO-2 rank's whole device-resident step -- the reduce-scatter with the
+    # check fused, the decision, the step -- captured once and replayed over new
+    # replica gradients (one with a planted inf), each replay against the same
+    # sequence run eagerly on a second copy of the state, bit for bit
+    psi, n, rank = 400_003, 4, 1
+    lay = zs.zero_shard_layout(psi, n, rank)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    bias = zs.zero_bias_corrections(0.9, 0.999, 1, 16).to(DEV)
+    reps = make_replicas(psi, n, "f16", 61, std=1e-3 * 4096)
+    master0 = torch.randn(lay.count, generator=torch.Generator().manual_seed(62)) * 0.02
+
+    def state():
+        return dict(master=master0.to(DEV), m=torch.zeros(lay.count, device=DEV),
+                    v=torch.zeros(lay.count, device=DEV),
+                    g=torch.empty(lay.count, dtype=torch.float16, device=DEV),
+                    w=torch.zeros(lay.count, dtype=torch.float16, device=DEV),
+                    ctl=zs.device_ctl_new(4096.0 * n, DEV))
+
+    def enqueue(st):
+        zs.zero_reduce_shard_check_dev(st["g"], reps, psi, n, rank, st["ctl"])
+        zs.zero_scaler_update_dev(st["ctl"], bias, 1)
+        zs.zero_adam_step_dev(st["w"], st["g"], st["master"], st["m"], st["v"], lay.count, 1, 0,
+                              ctl=st["ctl"], **hp)
+
+    E, G = state(), state()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        enqueue(G)
+    torch.cuda.synchronize()
+    fresh = make_replicas(psi, n, "f16", 63, std=1e-3 * 4096)
+    for i in range(5):
+        for k in range(n):
+            reps[k].copy_(fresh[k])
+            reps[k].mul_(1.0 + 0.125 * i)
+        if i == 2:
+            reps[0][lay.offset + 7] = float("inf")
+        graph.replay()
+        enqueue(E)
+        torch.cuda.synchronize()
+        for key in ("master", "m", "v", "g", "w"):
+            a, b = E[key], G[key]
+            iv = torch.int16 if a.dtype == torch.float16 else torch.int32
+            assert torch.equal(a.view(iv), b.view(iv)), (i, key)
+        ce, cg = zs.device_ctl_read(E["ctl"]), zs.device_ctl_read(G["ctl"])
+        assert bytes(ce) == bytes(cg), i
+        assert cg.found_inf == (1 if i == 2 else 0) and cg.apply == (0 if i == 2 else 1), i
+    assert zs.device_ctl_read(G["ctl"]).scaler.step == 4
+    del graph
+    log("reduce+check -> decision -> step captured in a graph: every replay equals the eager run")
