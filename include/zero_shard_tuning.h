@@ -43,13 +43,13 @@ int zero_set_occupancy(uint32_t blocks_per_cu);
 
 /*
  * zero_set_launch_piece -- most elements per launch of the step (both
- * gradient formats, host or device control) and of the accumulates that this
- * thread enqueues afterwards.  A longer shard goes out as consecutive launches
+ * gradient formats, host or device control), of the accumulates and of the
+ * flag-only overflow check that this thread enqueues afterwards.  A longer shard goes out as consecutive launches
  * over whole tiles, back to back on the same stream; elementwise work, so
  * results are bitwise the same under every setting.  0 (the default) restores
  * each kernel's own rule (the step and the accumulate with the fused check
  * of a later micro-batch: launches of 2^27 elements once a shard holds two of
- * them; the other accumulates: one launch).  A value below one tile
+ * them; the other accumulates and the check: one launch).  A value below one tile
  * means one tile; UINT64_MAX means one launch whatever the size.  Returns
  * ZERO_OK.
  */

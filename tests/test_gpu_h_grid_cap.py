@@ -124,6 +124,42 @@ def test_step_g32_and_accumulate_in_pieces(piece):
     g32_and_accumulate_case(f"piece={piece}", piece % 97)
 
 
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "f32"])
+def test_flag_check_in_pieces(fmt):
+    # the flag-only check cut into launches of one, three or seven tiles of
+    # 1024 vectors: a non-finite value at the head, at either side of a piece
+    # boundary, inside the last partial tile and in the elements after the
+    # last vector is seen, and a clean buffer leaves the flag 0
+    td = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[fmt]
+    per = 4 if fmt == "f32" else 8
+    tile = 1024 * per
+    count = 9 * tile + 3 * per + 5
+    g = synth.fill_normal_(torch.empty(count, dtype=td), 1e-3, 81)
+    gv = GuardedView(count, td, 3, DEV)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    check = zs.zero_overflow_check_g32 if fmt == "f32" else zs.zero_overflow_check
+    try:
+        for piece in PIECES:
+            zs.zero_set_launch_piece(piece * per // 2)   # 1, 3 and 7 tiles of this format
+            gv.view.copy_(g.to(DEV))
+            check(gv.view, count, 1, 0, 1024.0, flag)
+            assert int(flag.item()) == 0, (fmt, piece)
+            for pos in (0, 2, tile - 1, tile, 3 * tile - 1, 3 * tile + 1, 7 * tile, 9 * tile + 7,
+                        count - 1):
+                bad = g.clone()
+                bad[pos] = float("inf") if pos % 2 else float("nan")
+                gv.view.copy_(bad.to(DEV))
+                check(gv.view, count, 1, 0, 1024.0, flag)
+                want = (oracle.overflow_check_g32(f32(bad), 1024.0)[0] if fmt == "f32"
+                        else oracle.overflow_check(u16(bad), fmt, 1024.0)[0])
+                assert int(flag.item()) == want == 1, (fmt, piece, pos)
+    finally:
+        torch.cuda.synchronize()
+        zs.zero_set_launch_piece(0)
+    assert gv.guards_intact()
+    log(f"flag check {fmt} in pieces of 1, 3 and 7 tiles: every planted value seen")
+
+
 def test_pieces_with_a_lowered_grid_cap():
     # both overrides at once: launches of seven tiles, each walked by three
     # blocks in turn (the tile loop inside every piece)

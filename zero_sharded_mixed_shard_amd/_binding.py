@@ -163,10 +163,11 @@ def zero_set_occupancy(blocks_per_cu: int) -> None:
 
 
 def zero_set_launch_piece(elements: int) -> None:
-    """Most elements per launch of this thread's step and accumulate launches; a longer shard
-    goes out as consecutive launches on one stream.  0 restores each kernel's rule (the step
-    and the fused-check accumulate of a later micro-batch: launches of 2^27 once a shard holds
-    two; the other accumulates: one launch); 2**64 - 1 means one launch."""
+    """Most elements per launch of this thread's step, accumulate and flag-only check launches;
+    a longer shard goes out as consecutive launches on one stream.  0 restores each kernel's
+    rule (the step and the fused-check accumulate of a later micro-batch: launches of 2^27 once
+    a shard holds two; the other accumulates and the check: one launch); 2**64 - 1 means one
+    launch."""
     if not 0 <= elements < 1 << 64:
         raise ValueError("elements must fit in 64 bits")
     lib.zero_set_launch_piece(elements)

@@ -905,6 +905,13 @@ inline uint32_t grid_for(uint64_t need) {
 // 6.50, 6.51 -> 6.44, 6.44), so those stay one launch.
 constexpr uint64_t kStepPiece = 1ull << 27;
 
+// Elements per launch of the flag-only check: one launch.  The same plan of
+// back-to-back launches (one clear of the flag first) read 1e10 FP16
+// gradients at 7.40-7.42 TB/s in launches of 2^30, 7.16-7.17 of 2^28 and
+// 6.93-6.94 of 2^27, against 7.50 in one launch (three processes): a check
+// launch is short, so its boundaries cost more than a read stream gains.
+constexpr uint64_t kCheckPiece = 0;
+
 template <int DT, typename GT, int MODE>
 hipError_t adam_launch(uint16_t *w16, const GT *g, float *master, float *m, float *v,
                        uint64_t count, const AdamScalars &s, const int32_t *flag,
@@ -1005,9 +1012,23 @@ hipError_t check_dispatch(const GT *g, uint64_t count, float loss_scale,
                           double *partials, const DeviceProps &dev, hipStream_t stream) {
     const CheckGrid c = check_grid<GT, DT>(g, count, sumsq != nullptr, dev);
     if (sumsq == nullptr) {
-        overflow_flag_kernel<GT, DT, kCheckU><<<c.blocks, kThreads, c.lds, stream>>>(
-            g, count, c.head, c.n_vec, loss_scale, loss_scale_dev, flag);
-        return hipGetLastError();
+        // one block per tile of kCheckU * 256 vectors; a long shard may go out as
+        // consecutive launches of whole tiles (the last one with the partial
+        // tile and the elements after the last vector), all raising one flag
+        constexpr uint64_t kTileVec = static_cast<uint64_t>(kThreads) * kCheckU;
+        constexpr uint64_t kPer = GradBits<GT, DT>::kPerVec;
+        const uint64_t n_tiles = c.n_vec / kTileVec;
+        return by_pieces(
+            count, c.head, n_tiles, kTileVec * kPer,
+            piece_tiles(kCheckPiece, kTileVec * kPer, n_tiles, dev),
+            [&](uint64_t off, uint64_t cnt, uint32_t h, uint64_t) {
+                const uint64_t nv = (cnt - h) / kPer;
+                const uint64_t need = nv > 0 ? (nv + kTileVec - 1) / kTileVec
+                                             : (cnt - h + kThreads - 1) / kThreads;
+                overflow_flag_kernel<GT, DT, kCheckU><<<grid_for(need), kThreads, c.lds, stream>>>(
+                    g + off, cnt, h, nv, loss_scale, loss_scale_dev, flag);
+                return hipGetLastError();
+            });
     }
     overflow_sumsq_kernel<GT, DT, kCheckU><<<c.blocks, kThreads, 0, stream>>>(
         g, count, c.head, c.n_vec, loss_scale, loss_scale_dev, flag, partials);
